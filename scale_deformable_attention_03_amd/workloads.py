@@ -1,0 +1,218 @@
+"""Seeded synthetic inputs shaped like the Deformable DETR workloads.
+
+This module draws inputs only; it holds none of the core's arithmetic (no
+bilinear sampling, no weighted sum).  The same bytes feed the HIP library and
+the CPU oracle.
+
+Shapes come from the pages:
+  * Ascend DrivingSDK API page for multi_scale_deformable_attn, usage example:
+    bs 1, one 100x100 level, 4 heads, 8 points, 16 queries, 32 dims,
+    value = U[0,1)*0.01, locations = 0.005, weights = U[0,1) + 1e-5, and a
+    backward with an all-ones output gradient;
+  * Deformable DETR walkthrough (zhangshiyu.com/post/59697), section 2.2.4:
+    d_model 256 = 8 heads x 32 dims, 4 levels, 4 points; encoder queries are
+    the flattened pixels themselves with pixel-centre reference points
+    ((j + 0.5)/W, (i + 0.5)/H) (get_reference_points, valid ratios 1);
+    attention weights are a softmax over the L*P logits of one head;
+    section 2.3: 300 decoder queries; section 2.1.1: backbone strides
+    8/16/32/64.
+
+Recipe (identical for every consumer):
+  * numpy ``default_rng(seed)`` (PCG64); draws happen in the fixed order
+    value, reference points, offsets / locations, logits / weights,
+    grad_output;
+  * every float is drawn in float64 and cast once to the workload dtype
+    (through torch's round-to-nearest-even conversion);
+  * the softmax of the weight logits is part of input preparation (the core
+    takes weights as given and never normalises them).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Workload:
+    """One problem instance on the host (torch CPU tensors, workload dtype)."""
+
+    name: str
+    dtype: str                       # "f32" | "f16" | "bf16"
+    spatial_shapes: np.ndarray       # int64 [L, 2] = (H, W)
+    level_start_index: np.ndarray    # int64 [L]
+    value: torch.Tensor              # [bs, K, M, D]
+    sampling_locations: torch.Tensor  # [bs, Q, M, L, P, 2]
+    attention_weights: torch.Tensor  # [bs, Q, M, L, P]
+    grad_output: torch.Tensor        # [bs, Q, M*D]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def dims(self):
+        bs, K, M, D = self.value.shape
+        _, Q, _, L, P, _ = self.sampling_locations.shape
+        return dict(bs=bs, num_keys=K, num_heads=M, embed_dims=D, num_levels=L,
+                    num_points=P, num_queries=Q)
+
+    def f32(self, name: str) -> np.ndarray:
+        """The named float tensor widened exactly to float32 (oracle input)."""
+        return getattr(self, name).to(torch.float32).numpy()
+
+
+def level_starts(shapes) -> np.ndarray:
+    """Exclusive prefix sum of H*W over levels (flattened level offsets)."""
+    shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
+    hw = shapes[:, 0] * shapes[:, 1]
+    return np.concatenate([[0], np.cumsum(hw)[:-1]]).astype(np.int64)
+
+
+def _cast(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(DTYPES[dtype]).contiguous()
+
+
+def _softmax_last(x: np.ndarray) -> np.ndarray:
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def pixel_centre_refs(shapes) -> np.ndarray:
+    """[K, 2] normalised (x, y) pixel centres of every flattened key, level by
+    level, row-major within a level (valid ratios 1)."""
+    refs = []
+    for H, W in np.asarray(shapes, dtype=np.int64).reshape(-1, 2):
+        ys, xs = np.meshgrid((np.arange(H) + 0.5) / H, (np.arange(W) + 0.5) / W, indexing="ij")
+        refs.append(np.stack([xs.reshape(-1), ys.reshape(-1)], axis=-1))
+    return np.concatenate(refs, axis=0)
+
+
+def make(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries: int,
+         dtype: str, seed: int, value_dist: str = "normal", loc_dist: str = "uniform",
+         loc_args: tuple = (0.0, 1.0), weight_dist: str = "softmax", grad_dist: str = "normal",
+         meta: dict | None = None) -> Workload:
+    """General seeded generator.
+
+    value_dist:  "normal" N(0,1) | "u001" U[0,1)*0.01
+    loc_dist:    "uniform" U[lo,hi]^2 i.i.d. per sample (loc_args = (lo, hi))
+                 "encoder" pixel-centre ref of query q (queries = keys) +
+                           N(0, sigma) offsets, clamped (loc_args = (sigma, lo, hi))
+                 "decoder" per-query ref U[0,1]^2 shared over heads/levels/points
+                           + N(0, sigma) offsets (loc_args = (sigma,))
+                 "const"   every coordinate equals loc_args[0]
+    weight_dist: "softmax" softmax over L*P of N(0,1) logits | "u+1e-5" U[0,1)+1e-5
+    grad_dist:   "normal" N(0,1) | "ones"
+    """
+    shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
+    L = shapes.shape[0]
+    K = int((shapes[:, 0] * shapes[:, 1]).sum())
+    M, D, P, Q = heads, dims, points, queries
+    rng = np.random.default_rng(seed)
+
+    if value_dist == "normal":
+        value = rng.standard_normal((bs, K, M, D))
+    elif value_dist == "u001":
+        value = rng.random((bs, K, M, D)) * 0.01
+    else:
+        raise ValueError(value_dist)
+
+    lshape = (bs, Q, M, L, P, 2)
+    if loc_dist == "uniform":
+        lo, hi = loc_args
+        loc = rng.uniform(lo, hi, size=lshape)
+    elif loc_dist == "encoder":
+        sigma, lo, hi = loc_args
+        if Q != K:
+            raise ValueError("encoder locations need queries == keys")
+        ref = pixel_centre_refs(shapes)                      # [K, 2]
+        loc = ref[None, :, None, None, None, :] + rng.normal(0.0, sigma, size=lshape)
+        loc = np.clip(loc, lo, hi)
+    elif loc_dist == "decoder":
+        (sigma,) = loc_args
+        ref = rng.random((bs, Q, 2))
+        loc = ref[:, :, None, None, None, :] + rng.normal(0.0, sigma, size=lshape)
+    elif loc_dist == "const":
+        loc = np.full(lshape, float(loc_args[0]))
+    else:
+        raise ValueError(loc_dist)
+
+    if weight_dist == "softmax":
+        logits = rng.standard_normal((bs, Q, M, L * P))
+        w = _softmax_last(logits).reshape(bs, Q, M, L, P)
+    elif weight_dist == "u+1e-5":
+        w = rng.random((bs, Q, M, L, P)) + 1e-5
+    else:
+        raise ValueError(weight_dist)
+
+    if grad_dist == "normal":
+        g = rng.standard_normal((bs, Q, M * D))
+    elif grad_dist == "ones":
+        g = np.ones((bs, Q, M * D))
+    else:
+        raise ValueError(grad_dist)
+
+    return Workload(name=name, dtype=dtype, spatial_shapes=shapes,
+                    level_start_index=level_starts(shapes),
+                    value=_cast(value, dtype), sampling_locations=_cast(loc, dtype),
+                    attention_weights=_cast(w, dtype), grad_output=_cast(g, dtype),
+                    meta=dict(meta or {}, seed=seed))
+
+
+# --- the five named workloads -------------------------------------------------
+
+DETR_LEVELS = [(100, 134), (50, 67), (25, 34), (13, 17)]
+LARGE_LEVELS = [(128, 128), (64, 64), (32, 32), (16, 16)]
+STRESS_LEVELS = [(200, 200), (100, 100), (50, 50), (25, 25)]
+
+
+def tiny_single_level(kink: bool = False) -> Workload:
+    """bs 1, one 100x100 level, 4 heads x 32 dims, 8 points, 16 queries, fp32;
+    value U[0,0.01), locations U[0,1]^2 (or the constant 0.005 of the usage
+    example when ``kink``), weights U[0,1)+1e-5, grad_output ones."""
+    return make("tiny_single_level" + ("_kink" if kink else ""), 1, [(100, 100)], 4, 32, 8, 16,
+                "f32", 1001, value_dist="u001",
+                loc_dist="const" if kink else "uniform",
+                loc_args=(0.005,) if kink else (0.0, 1.0),
+                weight_dist="u+1e-5", grad_dist="ones")
+
+
+def detr_encoder(bs: int = 2, dtype: str = "f32", sigma: float = 0.02, seed: int = 1002) -> Workload:
+    """Deformable-DETR encoder self-attention: 4 levels (100,134) (50,67)
+    (25,34) (13,17), K = Q = 17821, 8 heads x 32 dims, 4 points."""
+    K = sum(h * w for h, w in DETR_LEVELS)
+    return make("detr_encoder", bs, DETR_LEVELS, 8, 32, 4, K, dtype, seed,
+                loc_dist="encoder", loc_args=(sigma, -0.05, 1.05))
+
+
+def detr_decoder(dtype: str = "f32") -> Workload:
+    """Deformable-DETR decoder cross-attention: the encoder's 4-level value,
+    bs 2, 300 queries, 4 points; refs U[0,1]^2 + N(0, 0.05) offsets."""
+    return make("detr_decoder", 2, DETR_LEVELS, 8, 32, 4, 300, dtype, 1003,
+                loc_dist="decoder", loc_args=(0.05,))
+
+
+def large_batch_encoder(bs: int = 8, dtype: str = "bf16") -> Workload:
+    """bs 8 encoder on the 1024x1024 pyramid (128,128) (64,64) (32,32) (16,16),
+    K = Q = 21760, 8 heads x 32 dims, 4 points, bf16."""
+    K = sum(h * w for h, w in LARGE_LEVELS)
+    return make("large_batch_encoder", bs, LARGE_LEVELS, 8, 32, 4, K, dtype, 1004,
+                loc_dist="encoder", loc_args=(0.02, -0.05, 1.05))
+
+
+def max_constraint(dtype: str = "f16") -> Workload:
+    """bs 4, 8 heads x 64 dims, 4 levels x 16 points (L*P = 64), levels
+    (200,200) (100,100) (50,50) (25,25), K = 53125, 900 queries, fp16;
+    locations U[-0.1, 1.1]^2."""
+    return make("max_constraint", 4, STRESS_LEVELS, 8, 64, 16, 900, dtype, 1005,
+                loc_dist="uniform", loc_args=(-0.1, 1.1))
+
+
+NAMED = {
+    "tiny_single_level": tiny_single_level,
+    "detr_encoder": detr_encoder,
+    "detr_decoder": detr_decoder,
+    "large_batch_encoder": large_batch_encoder,
+    "max_constraint": max_constraint,
+}
