@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Throughput of the MSDeformAttn core, forward + backward, on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+msda_forward followed by msda_backward (zero-fill, gradient kernel and, for
+16-bit dtypes, the float32 -> dtype conversion), both through the C ABI on
+torch's current stream.  Inputs are resident in HBM before timing starts.
+To keep the 256 MB Infinity Cache from serving a whole step's working set,
+steps rotate over several identical copies of every buffer.
+
+Default workload: Deformable-DETR encoder self-attention, fp32, bs 2, levels
+(100,134) (50,67) (25,34) (13,17), 17821 queries = keys, 8 heads x 32 dims,
+4 points, seeded synthetic inputs (scale_deformable_attention_03_amd.workloads).
+
+Prints one JSON line: queries/s (bs * num_queries per step / seconds per
+step), plus the roofline of the dominant kernel (algorithmic bytes per launch
+over its HIP-event-timed average duration against 8 TB/s) and the CPU oracle
+timed on the host cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak
+MALL_BYTES = 256 << 20       # Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_03_amd", "csrc", f)
+                  for f in ("msda_api.hip", "msda_kernels.hpp", "msda_device.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def touched_rows(wl) -> int:
+    """Number of (batch, key, head) value rows that at least one in-map
+    bilinear corner reads (the compulsory part of the value traffic)."""
+    import torch
+    loc = wl.sampling_locations.to(torch.float32).numpy()
+    bs, Q, M, L, P, _ = loc.shape
+    K = wl.value.shape[1]
+    seen = np.zeros((bs, K, M), dtype=bool)
+    bi = np.broadcast_to(np.arange(bs)[:, None, None, None], (bs, Q, M, P))
+    mi = np.broadcast_to(np.arange(M)[None, None, :, None], (bs, Q, M, P))
+    for lvl, (H, W) in enumerate(wl.spatial_shapes):
+        s0 = int(wl.level_start_index[lvl])
+        x = (loc[:, :, :, lvl, :, 0] * np.float32(W)).astype(np.float32) - np.float32(0.5)
+        y = (loc[:, :, :, lvl, :, 1] * np.float32(H)).astype(np.float32) - np.float32(0.5)
+        ok = (x > -1) & (x < W) & (y > -1) & (y < H)
+        x0 = np.floor(np.where(ok, x, 0)).astype(np.int64)
+        y0 = np.floor(np.where(ok, y, 0)).astype(np.int64)
+        for dy in (0, 1):
+            for dx in (0, 1):
+                xc, yc = x0 + dx, y0 + dy
+                v = ok & (xc >= 0) & (xc < W) & (yc >= 0) & (yc < H)
+                seen[bi[v], (s0 + yc * W + xc)[v], mi[v]] = True
+    return int(seen.sum())
+
+
+def algorithmic_bytes(wl, rows: int) -> dict:
+    e = wl.value.element_size()
+    bs, K, M, D = wl.value.shape
+    Q = wl.sampling_locations.shape[1]
+    L, P = wl.sampling_locations.shape[3:5]
+    value_rows = rows * D * e
+    loc = bs * Q * M * L * P * 2 * e
+    w = bs * Q * M * L * P * e
+    out = bs * Q * M * D * e
+    full_value = bs * K * M * D * e
+    fwd = value_rows + loc + w + out
+    bwd = value_rows + loc + w + out + full_value + loc + w   # + grad_out; writes gv, gloc, gw
+    return dict(fwd=fwd, bwd=bwd, total=fwd + bwd)
+
+
+def load_traffic(digest: str, kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they were taken on other kernel sources or another workload."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel, {})
+    if rec.get("kernel_digest") != digest or ent.get("workload") != workload:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    import oracle
+    args = (wl.f32("value"), wl.spatial_shapes, wl.level_start_index,
+            wl.f32("sampling_locations"), wl.f32("attention_weights"))
+    g = wl.f32("grad_output")
+    cores = oracle.threads(0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args)
+        oracle.backward(*args, g)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    bs, Q = wl.sampling_locations.shape[:2]
+    return {"value": reps * bs * Q / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full fwd+bwd passes of the benchmark workload ({bs}x{Q} queries), "
+                      f"{dt:.1f} s, float64 scalar C with OpenMP"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="detr_encoder",
+                    choices=["detr_encoder", "large_batch_encoder", "max_constraint", "detr_decoder",
+                             "tiny_single_level"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MSDeformAttn core runs on a single MI355X here "
+              "(batch or head sharding of this core needs no communication). "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+    from scale_deformable_attention_03_amd import _lib, ops
+    from scale_deformable_attention_03_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    wl = W.NAMED[args.workload]()
+    bs, K, M, D = wl.value.shape
+    Q, L, P = wl.sampling_locations.shape[1], wl.sampling_locations.shape[3], wl.sampling_locations.shape[4]
+    rows = touched_rows(wl)
+    ab = algorithmic_bytes(wl, rows)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+
+    # Rotating buffer sets: the sets together exceed twice the Infinity Cache.
+    step_bytes = sum(t.numel() * t.element_size() for t in
+                     (wl.value, wl.sampling_locations, wl.attention_weights, wl.grad_output)) * 2
+    nsets = max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1)
+    nsets = min(nsets, 8)
+    sets = []
+    need_ws = _lib.workspace_bytes(prob)
+    for _ in range(nsets):
+        s = dict(value=wl.value.to(dev), loc=wl.sampling_locations.to(dev), w=wl.attention_weights.to(dev),
+                 g=wl.grad_output.to(dev))
+        s["out"] = torch.empty(bs, Q, M * D, dtype=wl.value.dtype, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["gl"] = torch.empty_like(s["loc"])
+        s["gw"] = torch.empty_like(s["w"])
+        s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
+        s["acc"] = torch.zeros(bs, K, M, D, dtype=torch.float32, device=dev)
+        s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def fwd(s):
+        p = s["ptr"]
+        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
+
+    def bwd(s):
+        p = s["ptr"]
+        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                      p["ws"] if need_ws else 0, need_ws, sp)
+
+    def grad_kernel(s):
+        p = s["ptr"]
+        _lib.backward_accumulate(prob, p["value"], p["loc"], p["w"], p["g"], p["acc"], p["gl"], p["gw"], sp)
+
+    log(f"[bench] {args.workload}: bs {bs} K {K} Q {Q} M {M} D {D} L {L} P {P} {wl.dtype}; "
+        f"{nsets} buffer sets; warmup {args.warmup} steps {args.steps}")
+    for i in range(args.warmup):
+        fwd(sets[i % nsets])
+        bwd(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % nsets]
+        ev[i][0].record(stream)
+        fwd(s)
+        ev[i][1].record(stream)
+        bwd(s)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
+        f"bwd {bwd_ms * 1e3:.1f} us")
+
+    # The gradient kernel alone (msda_backward_accumulate), live, same rotation.
+    nk = max(20, args.steps // 2)
+    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nk)]
+    for i in range(nk):
+        s = sets[i % nsets]
+        evk[i][0].record(stream)
+        grad_kernel(s)
+        evk[i][1].record(stream)
+    torch.cuda.synchronize()
+    grad_ms = float(np.mean([a.elapsed_time(b) for a, b in evk]))
+    log(f"[bench] gradient kernel alone: {grad_ms * 1e3:.1f} us")
+
+    digest = kernel_digest()
+    if grad_ms >= fwd_ms:
+        kname, kms, kbytes = "msda_backward_kernel", grad_ms, ab["bwd"]
+    else:
+        kname, kms, kbytes = "msda_forward_kernel", fwd_ms, ab["fwd"]
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = load_traffic(digest, kname, args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kname,
+                "kernel_us": round(kms * 1e3, 2), "algorithmic_bytes_per_launch": kbytes}
+
+    queries = bs * Q
+    value = queries / (ms_per_step * 1e-3)
+    eff_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": "MSDeformAttn fwd+bwd queries/s and achieved HBM GB/s (% roofline), DETR encoder",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bs, "num_queries": Q, "num_keys": K,
+                   "num_heads": M, "embed_dims": D, "num_levels": L, "num_points": P,
+                   "spatial_shapes": [list(map(int, s)) for s in wl.spatial_shapes],
+                   "buffer_sets": nsets, "parallelism": "single GPU"},
+        "effective_gbps": round(eff_gbps, 1),
+        "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "fwd_us": round(fwd_ms * 1e3, 2),
+        "bwd_us": round(bwd_ms * 1e3, 2),
+        "algorithmic_bytes": ab,
+        "touched_value_rows": rows,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+        "kernel_digest": digest,
+        "roofline": roofline,
+    }
+    if args.no_cpu_baseline:
+        result["cpu_baseline"] = None
+    else:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

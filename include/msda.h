@@ -1,0 +1,208 @@
+/*
+ * msda.h -- C ABI of the MI355X (gfx950) multi-scale deformable attention core.
+ *
+ * The operation (forward):
+ *   For every batch b, query q and head m, sample level l of the flattened
+ *   multi-scale map bilinearly at each of its P normalised locations, weight
+ *   each sample by its attention weight and sum the L*P weighted samples:
+ *
+ *     out[b, q, m*D + d] = sum_{l<L} sum_{p<P} w[b,q,m,l,p] *
+ *                          bilinear(value_l[b, :, :, m, d], loc[b,q,m,l,p])
+ *
+ *   Definition: "Deformable DETR walkthrough" (zhangshiyu.com/post/59697),
+ *   section 2.2.4, reference function ms_deform_attn_core_pytorch: per level,
+ *   grid_sample(mode=bilinear, padding_mode=zeros, align_corners=False) at
+ *   grid = 2*loc - 1, times the weights, summed over levels and points.
+ *   Interface, tensor layouts and envelope: Ascend DrivingSDK API page for
+ *   multi_scale_deformable_attn (prototype, parameter list, return value,
+ *   constraints).  The backward returns gradients for value, locations and
+ *   weights only ("DQ-DETR ops directory" CSDN page, section 2(3)).
+ *
+ * Conventions shared by every entry point:
+ *   - Pixel coordinates: x = loc_x * W - 0.5, y = loc_y * H - 0.5, each
+ *     rounded to float32 separately (no fused multiply-add).  A sample takes
+ *     part only when -1 < x < W and -1 < y < H (NaN and +-Inf fail); a corner
+ *     outside the map reads as zero (per-corner zero padding).
+ *   - Layouts (all row-major, contiguous, one dtype for every float tensor):
+ *       value                   [batch, num_keys, num_heads, embed_dims]
+ *       sampling_locations      [batch, num_queries, num_heads, num_levels, num_points, 2]  (x, y)
+ *       attention_weights       [batch, num_queries, num_heads, num_levels, num_points]
+ *       output / grad_output    [batch, num_queries, num_heads * embed_dims]
+ *       grad_value              like value
+ *       grad_sampling_locations like sampling_locations
+ *       grad_attention_weights  like attention_weights
+ *     Row `start_l + h*W_l + w` of value is pixel (h, w) of level l.
+ *   - spatial_shapes and level_start_index are HOST arrays (int64), read
+ *     during the call only; they reach the kernels as launch arguments.  The
+ *     float tensors and the workspace are DEVICE pointers on the current
+ *     device.
+ *   - Arithmetic: inputs are widened to float32, all sums are float32, every
+ *     output is rounded once (round-to-nearest-even) to the dtype.  fp16 and
+ *     bf16 backward accumulate grad_value in a float32 workspace.
+ *   - Ownership: the caller allocates and owns every buffer.  The library
+ *     allocates nothing, keeps no state between calls, never synchronises the
+ *     host, and enqueues all work on `stream` (so calls may be captured in a
+ *     HIP graph).
+ *   - Errors: argument problems are reported synchronously, before anything
+ *     is enqueued.  A failed launch returns MSDA_ERROR_HIP.  Faults inside a
+ *     kernel surface at the caller's next synchronisation, as for any HIP
+ *     work.
+ */
+#ifndef MSDA_H_
+#define MSDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSDA_ABI_VERSION 1
+
+/* Float type of every float tensor of one call (fp32 and fp16 per the
+ * Ascend API page's dtype list; bf16 in addition). */
+typedef enum {
+    MSDA_F32 = 0,
+    MSDA_F16 = 1,
+    MSDA_BF16 = 2
+} msda_dtype_t;
+
+typedef enum {
+    MSDA_SUCCESS = 0,
+    MSDA_ERROR_INVALID_VALUE = 1, /* inconsistent sizes, NULL pointers, workspace too small */
+    MSDA_ERROR_NOT_SUPPORTED = 2, /* outside the envelope below */
+    MSDA_ERROR_MISALIGNED = 3,    /* a device pointer is not 16-byte aligned */
+    MSDA_ERROR_HIP = 4            /* a HIP launch failed */
+} msda_status_t;
+
+/*
+ * Problem descriptor.
+ *   batch, num_queries          >= 0 (0 makes an empty problem: nothing to
+ *                                  compute; the backward still zeroes
+ *                                  grad_value)
+ *   num_heads                   1..8      (Ascend constraints: heads <= 8)
+ *   embed_dims                  8..256, a multiple of 8 (Ascend parameter list
+ *                                  and constraints)
+ *   num_levels, num_points      >= 1, num_levels * num_points <= 64 (Ascend
+ *                                  constraints)
+ *   num_keys                    = sum_l H_l * W_l (asserted by MSDeformAttn.forward
+ *                                  in the walkthrough)
+ *   spatial_shapes              host int64 [num_levels][2] = (H_l, W_l), each >= 1
+ *   level_start_index           host int64 [num_levels], the exclusive prefix sum
+ *                                  of H_l * W_l
+ *   Index range: num_keys*num_heads*embed_dims and
+ *   num_queries*num_heads*num_levels*num_points*2 must stay below 2^31 (per-batch
+ *   offsets are 32-bit); larger problems return MSDA_ERROR_NOT_SUPPORTED.
+ */
+typedef struct {
+    int32_t batch;
+    int32_t num_keys;
+    int32_t num_heads;
+    int32_t embed_dims;
+    int32_t num_levels;
+    int32_t num_points;
+    int32_t num_queries;
+    msda_dtype_t dtype;
+    const int64_t *spatial_shapes;
+    const int64_t *level_start_index;
+} msda_problem_t;
+
+/*
+ * msda_validate: check a descriptor on the host (no HIP call, no device
+ * access).  Returns MSDA_SUCCESS, MSDA_ERROR_INVALID_VALUE or
+ * MSDA_ERROR_NOT_SUPPORTED.  Every other entry point runs the same checks
+ * first.
+ */
+msda_status_t msda_validate(const msda_problem_t *problem);
+
+/*
+ * msda_forward: output = MSDeformAttn core(value, locations, weights).
+ *   value, sampling_locations, attention_weights: device, read only.
+ *   output: device, overwritten in full.
+ *   Every pointer 16-byte aligned; a pointer may be NULL only if its tensor
+ *   has no elements.  One kernel launch on `stream`.  The result is
+ *   bitwise repeatable run to run.
+ */
+msda_status_t msda_forward(const msda_problem_t *problem,
+                           const void *value,
+                           const void *sampling_locations,
+                           const void *attention_weights,
+                           void *output,
+                           hipStream_t stream);
+
+/*
+ * msda_backward_workspace_bytes: device workspace msda_backward needs for
+ * this problem: 0 for fp32; batch*num_keys*num_heads*embed_dims*4 bytes (a
+ * float32 grad_value accumulator) for fp16 and bf16.  Returns 0 for an
+ * invalid descriptor as well; msda_backward then reports the error.
+ */
+size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
+
+/*
+ * msda_backward: gradients of sum(grad_output * output) with respect to
+ * value, sampling_locations and attention_weights.
+ *   grad_value[corner row]   += w * (bilinear weight) * grad_output, summed
+ *                               over every sample; rows never sampled are 0
+ *   grad_attention_weights    = <grad_output, bilinear sample>
+ *   grad_sampling_locations   = (W * w * <grad_output, d sample/dx>,
+ *                                H * w * <grad_output, d sample/dy>)
+ *   Derivatives are taken with respect to the normalised locations (hence
+ *   the factors W and H); at an integer pixel coordinate the cell that floor
+ *   selects is used (the right derivative).  Samples outside the map get zero
+ *   gradients.
+ *   All three gradients are OVERWRITTEN (not accumulated).  grad_value is
+ *   accumulated with float32 atomics, so its low bits may vary from run to
+ *   run; the other two gradients are bitwise repeatable.
+ *   workspace: device, at least msda_backward_workspace_bytes(problem) bytes
+ *   (may be NULL when that is 0), 16-byte aligned, owned by the caller; its
+ *   contents are scratch on entry and on exit.
+ *   Enqueues: a fill kernel (zeroes grad_value or the workspace), the
+ *   gradient kernel, and for fp16/bf16 a conversion kernel, on `stream`.
+ */
+msda_status_t msda_backward(const msda_problem_t *problem,
+                            const void *value,
+                            const void *sampling_locations,
+                            const void *attention_weights,
+                            const void *grad_output,
+                            void *grad_value,
+                            void *grad_sampling_locations,
+                            void *grad_attention_weights,
+                            void *workspace,
+                            size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * msda_backward_accumulate: the gradient kernel of msda_backward alone.
+ *   grad_value_acc (device, float32, laid out like value whatever the
+ *   problem's dtype) is ACCUMULATED into: grad_value_acc[corner row] +=
+ *   w * (bilinear weight) * grad_output; the caller zeroes or pre-fills it.
+ *   grad_sampling_locations and grad_attention_weights (problem dtype) are
+ *   overwritten, as in msda_backward.  One kernel launch on `stream`, no
+ *   workspace.  For callers that sum the value gradient of several calls
+ *   into one float32 buffer, or that clear it themselves earlier in a
+ *   stream.  Same checks and error codes as msda_backward.
+ */
+msda_status_t msda_backward_accumulate(const msda_problem_t *problem,
+                                       const void *value,
+                                       const void *sampling_locations,
+                                       const void *attention_weights,
+                                       const void *grad_output,
+                                       float *grad_value_acc,
+                                       void *grad_sampling_locations,
+                                       void *grad_attention_weights,
+                                       hipStream_t stream);
+
+/* msda_status_string: a static, human-readable name for a status code. */
+const char *msda_status_string(msda_status_t status);
+
+/* msda_abi_version: MSDA_ABI_VERSION of the built library. */
+int32_t msda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H_ */

@@ -1,0 +1,104 @@
+"""ctypes binding of libmsda.so (the C ABI declared in include/msda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind these calls.  There is no fallback: if the library is missing
+the import of this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
+
+MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
+STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
+          3: "MSDA_ERROR_MISALIGNED", 4: "MSDA_ERROR_HIP"}
+EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
+           "msda_backward_accumulate", "msda_status_string", "msda_abi_version")
+
+
+class MsdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class Problem(ctypes.Structure):
+    """msda_problem_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_keys", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("embed_dims", ctypes.c_int32),
+                ("num_levels", ctypes.c_int32), ("num_points", ctypes.c_int32),
+                ("num_queries", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("spatial_shapes", ctypes.POINTER(ctypes.c_int64)),
+                ("level_start_index", ctypes.POINTER(ctypes.c_int64))]
+
+
+def make_problem(batch, num_keys, num_heads, embed_dims, num_levels, num_points, num_queries,
+                 dtype: int, spatial_shapes, level_start_index):
+    """Build a Problem; returns (problem, keepalive) -- keep the second alive
+    for as long as the first is used (it owns the host shape arrays)."""
+    shapes = np.ascontiguousarray(np.asarray(spatial_shapes, dtype=np.int64).reshape(-1))
+    starts = np.ascontiguousarray(np.asarray(level_start_index, dtype=np.int64).reshape(-1))
+    p = Problem(int(batch), int(num_keys), int(num_heads), int(embed_dims), int(num_levels),
+                int(num_points), int(num_queries), int(dtype),
+                shapes.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    return p, (shapes, starts)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m scale_deformable_attention_03_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp = ctypes.c_void_p
+    lib.msda_validate.argtypes = [P]
+    lib.msda_validate.restype = ctypes.c_int
+    lib.msda_forward.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.msda_forward.restype = ctypes.c_int
+    lib.msda_backward_workspace_bytes.argtypes = [P]
+    lib.msda_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.msda_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msda_backward.restype = ctypes.c_int
+    lib.msda_backward_accumulate.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msda_backward_accumulate.restype = ctypes.c_int
+    lib.msda_status_string.argtypes = [ctypes.c_int]
+    lib.msda_status_string.restype = ctypes.c_char_p
+    lib.msda_abi_version.argtypes = []
+    lib.msda_abi_version.restype = ctypes.c_int32
+    return lib
+
+
+lib = _load()
+
+
+def validate(problem: Problem) -> int:
+    return lib.msda_validate(ctypes.byref(problem))
+
+
+def workspace_bytes(problem: Problem) -> int:
+    return int(lib.msda_backward_workspace_bytes(ctypes.byref(problem)))
+
+
+def forward(problem: Problem, value: int, loc: int, w: int, out: int, stream: int) -> None:
+    st = lib.msda_forward(ctypes.byref(problem), value, loc, w, out, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_forward")
+
+
+def backward(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,
+             gw: int, workspace: int, workspace_bytes_: int, stream: int) -> None:
+    st = lib.msda_backward(ctypes.byref(problem), value, loc, w, gout, gvalue, gloc, gw,
+                           workspace, workspace_bytes_, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward")
+
+
+def backward_accumulate(problem: Problem, value: int, loc: int, w: int, gout: int, gacc: int,
+                        gloc: int, gw: int, stream: int) -> None:
+    st = lib.msda_backward_accumulate(ctypes.byref(problem), value, loc, w, gout, gacc, gloc, gw, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_accumulate")

@@ -1,0 +1,53 @@
+"""Build libmsda.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc.
+
+    python -m scale_deformable_attention_03_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmsda.so")
+SOURCES = [os.path.join(CSRC, "msda_api.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_kernels.hpp")] + \
+          [os.path.join(INCLUDE, "msda.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-result", "-Wno-pass-failed",
+    # float32 atomics compile to the hardware global_atomic_add_f32
+    "-munsafe-fp-atomics",
+    # no packed-fp32 instructions (v_pk_*_f32) in generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into ``libmsda.so`` (always recompiles)."""
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", LIB + ".tmp", *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def stale() -> bool:
+    """True when the library is missing or older than a source or header."""
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(f) > t for f in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,226 @@
+// Device-side building blocks shared by the MSDeformAttn kernels (gfx950).
+//
+// Data layout (see include/msda.h): value [bs, K, M, D]; a (batch, query,
+// head) triple is a "group" G = (b*Q + q)*M + m.  Its locations are the
+// L*P*2 contiguous elements at G*L*P*2, its weights the L*P elements at
+// G*L*P, its output (and grad_output) the D elements at G*D.  A group is
+// processed by LPR consecutive lanes; each active lane owns VEC consecutive
+// channels (VECB bytes), so a bilinear corner is one coalesced row read of
+// D*e bytes spread over the group's lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msda {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { static constexpr int bytes = 4; };
+template <> struct Elem<kF16> { static constexpr int bytes = 2; };
+template <> struct Elem<kBF16> { static constexpr int bytes = 2; };
+
+constexpr int kMaxLevels = 64;   // L*P <= 64 bounds L
+
+// Level geometry as launch arguments: uniform across the grid, so the
+// compiler keeps the entries it reads in scalar registers.
+struct LevelTable {
+    int32_t H[kMaxLevels];
+    int32_t W[kMaxLevels];
+    int32_t start[kMaxLevels];
+};
+
+struct Problem {
+    int32_t bs, K, M, D, L, P, Q;
+    int32_t lpr_active;      // lanes of a group that own channels
+    int64_t ngroups;         // bs * Q * M
+    LevelTable lv;
+};
+
+// ---- scalar conversions --------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+    _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16));
+    return static_cast<float>(h);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    _Float16 h = static_cast<_Float16>(f);   // v_cvt_f16_f32: round to nearest even
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void* base, int64_t i) {
+    if constexpr (DT == kF32) {
+        return static_cast<const float*>(base)[i];
+    } else if constexpr (DT == kF16) {
+        return f16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+    } else {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_scalar(void* base, int64_t i, float v) {
+    if constexpr (DT == kF32) {
+        static_cast<float*>(base)[i] = v;
+    } else if constexpr (DT == kF16) {
+        static_cast<uint16_t*>(base)[i] = static_cast<uint16_t>(f32_to_f16_bits(v));
+    } else {
+        static_cast<uint16_t*>(base)[i] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+    }
+}
+
+// ---- vector row slices -------------------------------------------------------
+
+// VECB raw bytes of a row, held in 32-bit words.
+template <int VECB> struct Raw { uint32_t w[VECB / 4]; };
+
+template <int VECB>
+__device__ __forceinline__ Raw<VECB> load_raw(const void* p) {
+    Raw<VECB> r;
+    if constexpr (VECB == 16) {
+        uint4 v = *static_cast<const uint4*>(p);
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (VECB == 8) {
+        uint2 v = *static_cast<const uint2*>(p);
+        r.w[0] = v.x; r.w[1] = v.y;
+    } else {
+        r.w[0] = *static_cast<const uint32_t*>(p);
+    }
+    return r;
+}
+
+template <int VECB>
+__device__ __forceinline__ void store_raw(void* p, const Raw<VECB>& r) {
+    if constexpr (VECB == 16) {
+        *static_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    } else if constexpr (VECB == 8) {
+        *static_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+    } else {
+        *static_cast<uint32_t*>(p) = r.w[0];
+    }
+}
+
+// Widen VECB bytes of dtype DT into VEC floats (element 0 in the low bits).
+template <int DT, int VECB>
+__device__ __forceinline__ void widen(const Raw<VECB>& r, float* out) {
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i) out[i] = __uint_as_float(r.w[i]);
+    } else if constexpr (DT == kF16) {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i) {
+            out[2 * i] = f16_bits_to_f32(r.w[i] & 0xffffu);
+            out[2 * i + 1] = f16_bits_to_f32(r.w[i] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i) {
+            out[2 * i] = __uint_as_float(r.w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+        }
+    }
+}
+
+// Round VEC floats to dtype DT (nearest even) and pack into VECB bytes.
+template <int DT, int VECB>
+__device__ __forceinline__ Raw<VECB> narrow(const float* in) {
+    Raw<VECB> r;
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i) r.w[i] = __float_as_uint(in[i]);
+    } else if constexpr (DT == kF16) {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i)
+            r.w[i] = f32_to_f16_bits(in[2 * i]) | (f32_to_f16_bits(in[2 * i + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VECB / 4; ++i)
+            r.w[i] = f32_to_bf16_bits(in[2 * i]) | (f32_to_bf16_bits(in[2 * i + 1]) << 16);
+    }
+    return r;
+}
+
+// ---- sampling geometry ---------------------------------------------------------
+
+// Pixel coordinates of a normalised location under align_corners=False:
+// x = loc_x*W - 0.5, y = loc_y*H - 0.5, each product and difference rounded
+// to float32 on its own (contraction off: a fused multiply-add would move
+// exact pixel centres such as 0.005*100 - 0.5 off the integer grid).
+// Returns whether the sample touches the map: -1 < x < W and -1 < y < H
+// (NaN fails).
+__device__ __forceinline__ bool pixel_coords(float loc_x, float loc_y, float Wf, float Hf,
+                                             float& x, float& y) {
+#pragma clang fp contract(off)
+    x = loc_x * Wf;
+    x = x - 0.5f;
+    y = loc_y * Hf;
+    y = y - 0.5f;
+    return (x > -1.0f) & (x < Wf) & (y > -1.0f) & (y < Hf);
+}
+
+// Bilinear cell of a valid sample: the four corners' flat offsets (in
+// elements, relative to the (batch, head) base), their in-map flags and
+// bilinear weights (without the attention weight).
+struct Cell {
+    int32_t off00;           // row (start + y0*W + x0) times the row pitch M*D
+    int32_t dx, dy;          // offset steps to the x+1 and y+1 corners
+    bool v00, v01, v10, v11;
+    float lx, ly, hx, hy;
+};
+
+__device__ __forceinline__ Cell make_cell(float x, float y, int32_t W, int32_t H, int32_t start,
+                                          int32_t pitch) {
+    Cell c;
+    float fx = floorf(x), fy = floorf(y);
+    int32_t x0 = static_cast<int32_t>(fx), y0 = static_cast<int32_t>(fy);
+    c.lx = x - fx;
+    c.ly = y - fy;
+    c.hx = 1.0f - c.lx;
+    c.hy = 1.0f - c.ly;
+    bool inx0 = x0 >= 0, inx1 = x0 + 1 < W, iny0 = y0 >= 0, iny1 = y0 + 1 < H;
+    c.v00 = iny0 & inx0;
+    c.v01 = iny0 & inx1;
+    c.v10 = iny1 & inx0;
+    c.v11 = iny1 & inx1;
+    c.off00 = (start + y0 * W + x0) * pitch;
+    c.dx = pitch;
+    c.dy = W * pitch;
+    return c;
+}
+
+// ---- launch geometry -----------------------------------------------------------
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Remap so that each XCD walks one contiguous range of tiles: neighbouring
+// query tiles (raster neighbours in an encoder) then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t block, int64_t nblocks) {
+    constexpr int64_t kXcd = 8;
+    int64_t x = block % kXcd, i = block / kXcd;
+    int64_t per = nblocks / kXcd, rem = nblocks % kXcd;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// Sum over the LPR lanes of a group (LPR a power of two, groups aligned).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace msda

@@ -1,0 +1,148 @@
+"""PyTorch-facing entry points of the MSDeformAttn core.
+
+Signature and layouts follow the Ascend DrivingSDK API page for
+multi_scale_deformable_attn (prototype and parameter list):
+
+    ms_deform_attn(value, spatial_shapes, level_start_index,
+                   sampling_locations, attention_weights) -> output
+
+    value               [bs, num_keys, num_heads, embed_dims]
+    spatial_shapes      [num_levels, 2] (H, W), int32/int64, any device
+    level_start_index   [num_levels],  int32/int64, any device
+    sampling_locations  [bs, num_queries, num_heads, num_levels, num_points, 2]
+    attention_weights   [bs, num_queries, num_heads, num_levels, num_points]
+    output              [bs, num_queries, num_heads * embed_dims]
+
+The autograd backward returns gradients for value, sampling_locations and
+attention_weights and None for the two integer tensors, as
+MSDeformAttnFunction.backward does on the "DQ-DETR ops directory" CSDN page
+(section 2(3)).
+
+This module only marshals arguments: PyTorch supplies device memory and the
+current stream, the HIP library computes.  The shape tensors are read on the
+host (a device copy is fetched once per call, which synchronises).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib
+
+DTYPE_CODE = {torch.float32: _lib.MSDA_F32, torch.float16: _lib.MSDA_F16,
+              torch.bfloat16: _lib.MSDA_BF16}
+
+
+def _host_int64(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu")
+        return np.ascontiguousarray(x.numpy().astype(np.int64, copy=False))
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+def _check(t: torch.Tensor, name: str, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype} (one dtype for all float tensors)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def problem_for(value: torch.Tensor, spatial_shapes, level_start_index,
+                sampling_locations: torch.Tensor):
+    """(Problem, keepalive) for tensors laid out as in the module docstring."""
+    if value.dim() != 4 or sampling_locations.dim() != 6 or sampling_locations.shape[-1] != 2:
+        raise ValueError("value must be [bs, K, M, D] and sampling_locations [bs, Q, M, L, P, 2]")
+    if value.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {value.dtype}")
+    bs, K, M, D = value.shape
+    bs2, Q, M2, L, P, _ = sampling_locations.shape
+    if bs2 != bs or M2 != M:
+        raise ValueError("batch / heads of value and sampling_locations differ")
+    shapes = _host_int64(spatial_shapes).reshape(-1, 2)
+    starts = _host_int64(level_start_index).reshape(-1)
+    if shapes.shape[0] != L or starts.shape[0] != L:
+        raise ValueError("spatial_shapes / level_start_index do not match num_levels")
+    return _lib.make_problem(bs, K, M, D, L, P, Q, DTYPE_CODE[value.dtype], shapes, starts)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """One msda_forward call on the current stream; returns output."""
+    prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
+    dev, dt = value.device, value.dtype
+    bs, K, M, D = value.shape
+    _, Q, _, L, P, _ = sampling_locations.shape
+    _check(value, "value", dt, dev)
+    _check(sampling_locations, "sampling_locations", dt, dev)
+    _check(attention_weights, "attention_weights", dt, dev, (bs, Q, M, L, P))
+    if out is None:
+        out = torch.empty((bs, Q, M * D), dtype=dt, device=dev)
+    _check(out, "output", dt, dev, (bs, Q, M * D))
+    _lib.forward(prob, value.data_ptr(), sampling_locations.data_ptr(),
+                 attention_weights.data_ptr(), out.data_ptr(), _stream(dev))
+    return out
+
+
+def backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+             grad_output, grads=None, workspace: torch.Tensor | None = None):
+    """One msda_backward call on the current stream; returns
+    (grad_value, grad_sampling_locations, grad_attention_weights)."""
+    prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
+    dev, dt = value.device, value.dtype
+    bs, K, M, D = value.shape
+    _, Q, _, L, P, _ = sampling_locations.shape
+    _check(value, "value", dt, dev)
+    _check(sampling_locations, "sampling_locations", dt, dev)
+    _check(attention_weights, "attention_weights", dt, dev, (bs, Q, M, L, P))
+    _check(grad_output, "grad_output", dt, dev, (bs, Q, M * D))
+    if grads is None:
+        grads = (torch.empty_like(value), torch.empty_like(sampling_locations),
+                 torch.empty_like(attention_weights))
+    gv, gl, gw = grads
+    _check(gv, "grad_value", dt, dev, value.shape)
+    _check(gl, "grad_sampling_locations", dt, dev, sampling_locations.shape)
+    _check(gw, "grad_attention_weights", dt, dev, attention_weights.shape)
+    need = _lib.workspace_bytes(prob)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if (need > 0) else 0
+    _lib.backward(prob, value.data_ptr(), sampling_locations.data_ptr(),
+                  attention_weights.data_ptr(), grad_output.data_ptr(), gv.data_ptr(),
+                  gl.data_ptr(), gw.data_ptr(), ws_ptr, need, _stream(dev))
+    return gv, gl, gw
+
+
+class MSDeformAttnFunction(torch.autograd.Function):
+    """Autograd wrapper: forward = msda_forward, backward = msda_backward."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+        shapes = _host_int64(spatial_shapes)
+        starts = _host_int64(level_start_index)
+        out = forward(value, shapes, starts, sampling_locations, attention_weights)
+        ctx.save_for_backward(value, sampling_locations, attention_weights)
+        ctx.host_shapes = (shapes, starts)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, loc, w = ctx.saved_tensors
+        shapes, starts = ctx.host_shapes
+        gv, gl, gw = backward(value, shapes, starts, loc, w, grad_output.contiguous())
+        return gv, None, None, gl, gw
+
+
+def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+    """Differentiable MSDeformAttn core (see the module docstring)."""
+    return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index,
+                                      sampling_locations, attention_weights)

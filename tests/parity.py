@@ -1,0 +1,98 @@
+"""Shared helpers of the parity tests: run a workload through the HIP library
+(via the C ABI) and through the CPU oracle, and compare element by element.
+
+Tolerances (the bar an element must meet: |gpu - ref| <= rtol*|ref| + atol):
+  fp32 forward            rtol 1e-5, atol 1e-6
+  fp32 backward           rtol 1e-4, atol 1e-4 * RMS(ref tensor)
+                          (float32 atomics reorder the grad_value sums)
+  fp16 / bf16, all        rtol 1e-2, atol 1e-2 * RMS(ref tensor)
+                          (against the float64 oracle fed the same 16-bit inputs)
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {
+    ("f32", "fwd"): (1e-5, None, 1e-6),
+    ("f32", "bwd"): (1e-4, 1e-4, None),
+    ("f16", "fwd"): (1e-2, 1e-2, None),
+    ("f16", "bwd"): (1e-2, 1e-2, None),
+    ("bf16", "fwd"): (1e-2, 1e-2, None),
+    ("bf16", "bwd"): (1e-2, 1e-2, None),
+}
+
+
+def assert_close(name, gpu, ref, rtol, atol_rms=None, atol=None):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    if ref.size == 0:
+        return
+    if atol is None:
+        atol = atol_rms * float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(gpu - ref)
+    bound = rtol * np.abs(ref) + atol
+    bad = ~(err <= bound)            # NaN in gpu counts as bad
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(np.where(bad, err - bound, -np.inf))), ref.shape)
+        norm = float(np.linalg.norm((gpu - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+        raise AssertionError(
+            f"{name}: {int(bad.sum())}/{ref.size} elements out of tolerance "
+            f"(rtol {rtol:g}, atol {atol:.3g}); worst at {i}: gpu {gpu[i]!r} ref {ref[i]!r}; "
+            f"normwise rel err {norm:.3g}")
+
+
+def to_device(wl, device="cuda"):
+    return dict(value=wl.value.to(device), loc=wl.sampling_locations.to(device),
+                w=wl.attention_weights.to(device), g=wl.grad_output.to(device))
+
+
+def gpu_forward(wl, t=None):
+    from scale_deformable_attention_03_amd import ops
+    t = t or to_device(wl)
+    out = ops.forward(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"], t["w"])
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_backward(wl, t=None):
+    from scale_deformable_attention_03_amd import ops
+    t = t or to_device(wl)
+    gv, gl, gw = ops.backward(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"], t["w"], t["g"])
+    torch.cuda.synchronize()
+    return gv, gl, gw
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle_forward(wl, nthreads=0):
+    return oracle.forward(wl.f32("value"), wl.spatial_shapes, wl.level_start_index,
+                          wl.f32("sampling_locations"), wl.f32("attention_weights"), nthreads)
+
+
+def oracle_backward(wl, nthreads=0):
+    return oracle.backward(wl.f32("value"), wl.spatial_shapes, wl.level_start_index,
+                           wl.f32("sampling_locations"), wl.f32("attention_weights"),
+                           wl.f32("grad_output"), nthreads)
+
+
+def check_forward(wl, out=None):
+    out = gpu_forward(wl) if out is None else out
+    rtol, arms, atol = TOL[(wl.dtype, "fwd")]
+    assert_close(f"{wl.name}/{wl.dtype}/output", f64(out), oracle_forward(wl), rtol, arms, atol)
+    return out
+
+
+def check_backward(wl, grads=None):
+    gv, gl, gw = gpu_backward(wl) if grads is None else grads
+    rgv, rgl, rgw = oracle_backward(wl)
+    rtol, arms, atol = TOL[(wl.dtype, "bwd")]
+    assert_close(f"{wl.name}/{wl.dtype}/grad_attention_weights", f64(gw), rgw, rtol, arms, atol)
+    assert_close(f"{wl.name}/{wl.dtype}/grad_sampling_locations", f64(gl), rgl, rtol, arms, atol)
+    assert_close(f"{wl.name}/{wl.dtype}/grad_value", f64(gv), rgv, rtol, arms, atol)
+    return gv, gl, gw
