@@ -49,10 +49,27 @@ def make_problem(batch, num_keys, num_heads, embed_dims, num_levels, num_points,
     return p, (shapes, starts)
 
 
+def _hip_runtimes() -> set:
+    """Paths of every HIP runtime (libamdhip64) mapped into this process."""
+    with open("/proc/self/maps") as f:
+        return {line.split()[-1] for line in f if "libamdhip64" in line}
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m scale_deformable_attention_03_amd.build`")
+    # PyTorch ships its own HIP runtime.  Load it first, so that libmsda.so's
+    # dependency on libamdhip64.so.7 resolves to that same, already loaded
+    # runtime (matched by soname).  Loaded the other way round, the process
+    # would hold two HIP runtimes, and handles of one (streams, allocations)
+    # would be passed to the other.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("more than one HIP runtime is loaded in this process "
+                          f"({sorted(runtimes)}); import torch before anything that loads "
+                          "/opt/rocm's libamdhip64")
     P = ctypes.POINTER(Problem)
     vp = ctypes.c_void_p
     lib.msda_validate.argtypes = [P]

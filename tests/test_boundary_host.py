@@ -146,3 +146,8 @@ def test_empty_tensors_may_be_null():
     # nothing is enqueued by the forward.
     p, keep = prob(Q=0)
     assert _fwd(p, 0x10000, None, None, None) == OK
+
+
+def test_single_hip_runtime_in_process():
+    """libmsda.so must share PyTorch's HIP runtime (one libamdhip64 mapped)."""
+    assert len(_lib._hip_runtimes()) == 1, _lib._hip_runtimes()
