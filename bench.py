@@ -20,6 +20,7 @@ timed on the host cores as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -36,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak
 MALL_BYTES = 256 << 20       # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_03_amd", "csrc", f)
-                  for f in ("msda_api.hip", "msda_kernels.hpp", "msda_device.hpp")]
+                  for f in ("msda_api.hip", "msda_forward.hpp", "msda_backward.hpp", "msda_device.hpp")]
 
 
 def log(*a):
@@ -87,7 +88,12 @@ def algorithmic_bytes(wl, rows: int) -> dict:
     full_value = bs * K * M * D * e
     fwd = value_rows + loc + w + out
     bwd = value_rows + loc + w + out + full_value + loc + w   # + grad_out; writes gv, gloc, gw
-    return dict(fwd=fwd, bwd=bwd, total=fwd + bwd)
+    # the backward's two big kernels: the gather (value rows, loc, w,
+    # grad_out in; grad_loc, grad_w out) and the accumulation (loc, w,
+    # grad_out in; grad_value out)
+    grad = value_rows + loc + w + out + loc + w
+    accum = loc + w + out + full_value
+    return dict(fwd=fwd, bwd=bwd, total=fwd + bwd, grad=grad, accum=accum)
 
 
 def load_traffic(digest: str, kernel: str, workload: str):
@@ -175,7 +181,6 @@ def main() -> int:
         s["gl"] = torch.empty_like(s["loc"])
         s["gw"] = torch.empty_like(s["w"])
         s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
-        s["acc"] = torch.zeros(bs, K, M, D, dtype=torch.float32, device=dev)
         s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
         sets.append(s)
     stream = torch.cuda.current_stream(dev)
@@ -189,10 +194,6 @@ def main() -> int:
         p = s["ptr"]
         _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
                       p["ws"] if need_ws else 0, need_ws, sp)
-
-    def grad_kernel(s):
-        p = s["ptr"]
-        _lib.backward_accumulate(prob, p["value"], p["loc"], p["w"], p["g"], p["acc"], p["gl"], p["gw"], sp)
 
     log(f"[bench] {args.workload}: bs {bs} K {K} Q {Q} M {M} D {D} L {L} P {P} {wl.dtype}; "
         f"{nsets} buffer sets; warmup {args.warmup} steps {args.steps}")
@@ -218,23 +219,43 @@ def main() -> int:
     log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
         f"bwd {bwd_ms * 1e3:.1f} us")
 
-    # The gradient kernel alone (msda_backward_accumulate), live, same rotation.
-    nk = max(20, args.steps // 2)
-    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nk)]
+    # Per-stage times of msda_backward (HIP events recorded by the library
+    # between its kernels, msda_backward_profile), live, same rotation.
+    hip = ctypes.CDLL("libamdhip64.so.7")     # PyTorch's runtime, already loaded
+    nstage = len(_lib.BACKWARD_STAGES)
+    nk = max(20, args.steps // 4)
+    evs = []
+    for _ in range(nk):
+        arr = (ctypes.c_void_p * (nstage + 1))()
+        for j in range(nstage + 1):
+            if hip.hipEventCreate(ctypes.byref(arr, j * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        evs.append(arr)
     for i in range(nk):
         s = sets[i % nsets]
-        evk[i][0].record(stream)
-        grad_kernel(s)
-        evk[i][1].record(stream)
+        p = s["ptr"]
+        fwd(s)
+        _lib.backward_profile(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                              p["ws"] if need_ws else 0, need_ws, evs[i], sp)
     torch.cuda.synchronize()
-    grad_ms = float(np.mean([a.elapsed_time(b) for a, b in evk]))
-    log(f"[bench] gradient kernel alone: {grad_ms * 1e3:.1f} us")
+    stage_ms = np.zeros(nstage)
+    f = ctypes.c_float()
+    for arr in evs:
+        for j in range(nstage):
+            if hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arr[j]), ctypes.c_void_p(arr[j + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            stage_ms[j] += f.value / nk
+        for j in range(nstage + 1):
+            hip.hipEventDestroy(ctypes.c_void_p(arr[j]))
+    stages_us = {name: round(float(v) * 1e3, 2) for name, v in zip(_lib.BACKWARD_STAGES, stage_ms)}
+    log(f"[bench] backward stages (us): {stages_us}")
 
     digest = kernel_digest()
-    if grad_ms >= fwd_ms:
-        kname, kms, kbytes = "msda_backward_kernel", grad_ms, ab["bwd"]
-    else:
-        kname, kms, kbytes = "msda_forward_kernel", fwd_ms, ab["fwd"]
+    kernels = {"msda_forward_kernel": (fwd_ms, ab["fwd"]),
+               "msda_backward_kernel": (stage_ms[3], ab["grad"]),
+               "msda_accumulate_kernel": (stage_ms[4], ab["accum"])}
+    kname = max(kernels, key=lambda k: kernels[k][0])
+    kms, kbytes = kernels[kname]
     achieved = kbytes / (kms * 1e-3) / 1e9
     traffic = load_traffic(digest, kname, args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -265,6 +286,7 @@ def main() -> int:
         "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
+        "bwd_stages_us": stages_us,
         "algorithmic_bytes": ab,
         "touched_value_rows": rows,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

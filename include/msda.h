@@ -134,10 +134,13 @@ msda_status_t msda_forward(const msda_problem_t *problem,
                            hipStream_t stream);
 
 /*
- * msda_backward_workspace_bytes: device workspace msda_backward needs for
- * this problem: 0 for fp32; batch*num_keys*num_heads*embed_dims*4 bytes (a
- * float32 grad_value accumulator) for fp16 and bf16.  Returns 0 for an
- * invalid descriptor as well; msda_backward then reports the error.
+ * msda_backward_workspace_bytes: device workspace msda_backward and
+ * msda_backward_accumulate need for this problem.  It holds the binned
+ * transpose of the sampling pattern (per-segment counts and cursors, the
+ * unit list and up to four 4-byte records per sample) and, for fp16 and
+ * bf16, a float32 grad_value accumulator (batch*num_keys*num_heads*
+ * embed_dims*4 bytes).  Returns 0 for an empty problem and for an invalid
+ * descriptor; the backward then reports the error.
  */
 size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
 
@@ -158,9 +161,15 @@ size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
  *   run; the other two gradients are bitwise repeatable.
  *   workspace: device, at least msda_backward_workspace_bytes(problem) bytes
  *   (may be NULL when that is 0), 16-byte aligned, owned by the caller; its
- *   contents are scratch on entry and on exit.
- *   Enqueues: a fill kernel (zeroes grad_value or the workspace), the
- *   gradient kernel, and for fp16/bf16 a conversion kernel, on `stream`.
+ *   contents are scratch on entry and on exit.  Calls that overlap in time
+ *   must not share a workspace.
+ *   Enqueues on `stream`: a record count, a scan, the gradient kernel (a
+ *   gather like the forward, which also writes the records), the
+ *   accumulation kernel (one workgroup per key segment writes grad_value
+ *   rows once) and, for fp16/bf16, a conversion kernel.  Problems whose
+ *   sampling pattern does not fit the record format (more than 2^21 samples
+ *   per (batch, head) or more than 2048 key segments) fall back to a zero
+ *   fill and float atomics.
  */
 msda_status_t msda_backward(const msda_problem_t *problem,
                             const void *value,
@@ -175,15 +184,17 @@ msda_status_t msda_backward(const msda_problem_t *problem,
                             hipStream_t stream);
 
 /*
- * msda_backward_accumulate: the gradient kernel of msda_backward alone.
+ * msda_backward_accumulate: msda_backward, adding grad_value into a float32
+ * buffer instead of overwriting it.
  *   grad_value_acc (device, float32, laid out like value whatever the
  *   problem's dtype) is ACCUMULATED into: grad_value_acc[corner row] +=
  *   w * (bilinear weight) * grad_output; the caller zeroes or pre-fills it.
  *   grad_sampling_locations and grad_attention_weights (problem dtype) are
- *   overwritten, as in msda_backward.  One kernel launch on `stream`, no
- *   workspace.  For callers that sum the value gradient of several calls
- *   into one float32 buffer, or that clear it themselves earlier in a
- *   stream.  Same checks and error codes as msda_backward.
+ *   overwritten, as in msda_backward.  Same kernels as msda_backward except
+ *   that the accumulation kernel adds its rows with float atomics (and no
+ *   conversion kernel runs).  For callers that sum the value gradient of
+ *   several calls into one float32 buffer.  Same workspace, checks and error
+ *   codes as msda_backward.
  */
 msda_status_t msda_backward_accumulate(const msda_problem_t *problem,
                                        const void *value,
@@ -193,7 +204,37 @@ msda_status_t msda_backward_accumulate(const msda_problem_t *problem,
                                        float *grad_value_acc,
                                        void *grad_sampling_locations,
                                        void *grad_attention_weights,
+                                       void *workspace,
+                                       size_t workspace_bytes,
                                        hipStream_t stream);
+
+/*
+ * msda_backward_profile: msda_backward, recording HIP events between its
+ * kernels so that a caller can time each stage on the stream.
+ *   stage_events: host array of MSDA_BACKWARD_STAGES + 1 events created by
+ *   the caller (hipEventCreate); event k is recorded just before stage k,
+ *   the last one after the final stage:
+ *     0 zero the segment counts      1 count records per segment
+ *     2 scan counts into ranges      3 gradient kernel (gather, records)
+ *     4 accumulate grad_value        5 fp16/bf16 conversion
+ *   A stage with no kernel for the problem (the conversion for fp32; the
+ *   count, scan and accumulation on the float-atomic fallback, whose zero
+ *   fill then runs as stage 0) leaves its two events back to back.
+ *   Otherwise identical to msda_backward; stage_events must not be NULL.
+ */
+#define MSDA_BACKWARD_STAGES 6
+msda_status_t msda_backward_profile(const msda_problem_t *problem,
+                                    const void *value,
+                                    const void *sampling_locations,
+                                    const void *attention_weights,
+                                    const void *grad_output,
+                                    void *grad_value,
+                                    void *grad_sampling_locations,
+                                    void *grad_attention_weights,
+                                    void *workspace,
+                                    size_t workspace_bytes,
+                                    hipEvent_t *stage_events,
+                                    hipStream_t stream);
 
 /* msda_status_string: a static, human-readable name for a status code. */
 const char *msda_status_string(msda_status_t status);

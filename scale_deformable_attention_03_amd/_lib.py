@@ -17,7 +17,9 @@ MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
 STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
           3: "MSDA_ERROR_MISALIGNED", 4: "MSDA_ERROR_HIP"}
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
-           "msda_backward_accumulate", "msda_status_string", "msda_abi_version")
+           "msda_backward_accumulate", "msda_backward_profile", "msda_status_string",
+           "msda_abi_version")
+BACKWARD_STAGES = ("zero_counts", "count", "scan", "gradient", "accumulate", "narrow")
 
 
 class MsdaError(RuntimeError):
@@ -80,8 +82,10 @@ def _load():
     lib.msda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.msda_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward.restype = ctypes.c_int
-    lib.msda_backward_accumulate.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msda_backward_accumulate.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward_accumulate.restype = ctypes.c_int
+    lib.msda_backward_profile.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.msda_backward_profile.restype = ctypes.c_int
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
@@ -115,7 +119,18 @@ def backward(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: 
 
 
 def backward_accumulate(problem: Problem, value: int, loc: int, w: int, gout: int, gacc: int,
-                        gloc: int, gw: int, stream: int) -> None:
-    st = lib.msda_backward_accumulate(ctypes.byref(problem), value, loc, w, gout, gacc, gloc, gw, stream)
+                        gloc: int, gw: int, workspace: int, workspace_bytes_: int, stream: int) -> None:
+    st = lib.msda_backward_accumulate(ctypes.byref(problem), value, loc, w, gout, gacc, gloc, gw,
+                                      workspace, workspace_bytes_, stream)
     if st != 0:
         raise MsdaError(st, "msda_backward_accumulate")
+
+
+def backward_profile(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,
+                     gw: int, workspace: int, workspace_bytes_: int, events, stream: int) -> None:
+    """msda_backward with HIP events recorded between its stages (events: a
+    ctypes array of len(BACKWARD_STAGES) + 1 hipEvent_t handles)."""
+    st = lib.msda_backward_profile(ctypes.byref(problem), value, loc, w, gout, gvalue, gloc, gw,
+                                   workspace, workspace_bytes_, events, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_profile")

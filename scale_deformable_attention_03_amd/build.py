@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsda.so")
 SOURCES = [os.path.join(CSRC, "msda_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_kernels.hpp")] + \
+HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp")] + \
           [os.path.join(INCLUDE, "msda.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

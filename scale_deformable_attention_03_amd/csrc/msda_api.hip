@@ -1,15 +1,19 @@
 // C ABI of the MSDeformAttn core (declarations and contract: include/msda.h).
 //
-// Host side only: validate the descriptor, pack the level table into launch
-// arguments, choose the kernel instantiation, enqueue.  No allocation, no
-// host synchronisation, no state between calls.
+// Host side only: validate the descriptor, plan the launch (level table,
+// key segments of the binned backward, workspace layout), choose the kernel
+// instantiations, enqueue.  No allocation, no host synchronisation, no state
+// between calls.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "msda.h"
-#include "msda_kernels.hpp"
+#include "msda_backward.hpp"
+#include "msda_forward.hpp"
 
 namespace {
 
@@ -70,6 +74,27 @@ msda_status_t check_problem(const msda_problem_t* p) {
     return MSDA_SUCCESS;
 }
 
+int64_t value_elems(const msda_problem_t* p) {
+    return int64_t(p->batch) * p->num_keys * p->num_heads * p->embed_dims;
+}
+int64_t sample_elems(const msda_problem_t* p) {
+    return int64_t(p->batch) * p->num_queries * p->num_heads * p->num_levels * p->num_points;
+}
+int64_t out_elems(const msda_problem_t* p) {
+    return int64_t(p->batch) * p->num_queries * p->num_heads * p->embed_dims;
+}
+
+int floor_log2(int64_t v) {
+    int s = 0;
+    while ((int64_t(2) << s) <= v) ++s;
+    return s;
+}
+
+// Problem descriptor for the kernels, including the key segments of the
+// binned backward: level l gets segments of 2^shift keys, sized so that a
+// segment receives about kUnitRecords / 2 records when the samples spread
+// evenly over the level (two records per sample and level, Q*P samples per
+// level and plane).  A tile of 2^shift keys * D floats stays within 32 KB.
 msda::Problem pack(const msda_problem_t* p) {
     msda::Problem pb;
     memset(&pb, 0, sizeof(pb));
@@ -82,22 +107,71 @@ msda::Problem pack(const msda_problem_t* p) {
     pb.Q = p->num_queries;
     pb.lpr_active = lane_split(p->embed_dims, p->dtype).active;
     pb.ngroups = int64_t(p->batch) * p->num_queries * p->num_heads;
+    pb.nplanes = p->batch * p->num_heads;
+    const int max_shift = floor_log2(std::min<int64_t>(msda::kMaxSegKeys, 8192 / p->embed_dims));
+    int64_t nseg = 0;
     for (int l = 0; l < p->num_levels; ++l) {
-        pb.lv.H[l] = static_cast<int32_t>(p->spatial_shapes[2 * l]);
-        pb.lv.W[l] = static_cast<int32_t>(p->spatial_shapes[2 * l + 1]);
+        const int64_t H = p->spatial_shapes[2 * l], W = p->spatial_shapes[2 * l + 1];
+        pb.lv.H[l] = static_cast<int32_t>(H);
+        pb.lv.W[l] = static_cast<int32_t>(W);
         pb.lv.start[l] = static_cast<int32_t>(p->level_start_index[l]);
+        const double per_key = 2.0 * double(p->num_queries) * p->num_points / double(H * W);
+        const double keys = per_key > 0 ? (msda::kUnitRecords / 2) / per_key : double(msda::kMaxSegKeys);
+        int shift = keys >= 1.0 ? floor_log2(static_cast<int64_t>(keys)) : 0;
+        if (shift > max_shift) shift = max_shift;
+        pb.seg_shift[l] = shift;
+        pb.seg_base[l] = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
+        nseg += (H * W + (int64_t(1) << shift) - 1) >> shift;
     }
+    pb.seg_base[p->num_levels] = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
+    pb.nseg = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
     return pb;
 }
 
-int64_t value_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_keys * p->num_heads * p->embed_dims;
+// The binned backward needs: sample indices per plane within the record
+// field, at most kMaxSegments segments per plane, record positions and unit
+// counts within int32.
+int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
+
+bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
+    const int64_t per_plane = int64_t(p->num_queries) * p->num_levels * p->num_points;
+    return per_plane < (int64_t(1) << msda::kRecSampleBits) && pb.nseg <= msda::kMaxSegments &&
+           max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * pb.nseg < kIndexLimit / 2;
 }
-int64_t sample_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_queries * p->num_heads * p->num_levels * p->num_points;
-}
-int64_t out_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_queries * p->num_heads * p->embed_dims;
+
+// ---- workspace layout --------------------------------------------------------
+
+struct Layout {
+    bool binned;
+    size_t counts, cursor, nunits, units, records, acc, total;
+    int64_t max_units;
+};
+
+size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
+    Layout w;
+    memset(&w, 0, sizeof(w));
+    w.binned = binned_ok(p, pb);
+    size_t off = 0;
+    if (w.binned) {
+        const int64_t nbins = int64_t(pb.nplanes) * pb.nseg;
+        w.max_units = nbins + (max_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
+        w.counts = off;
+        off += round_up(nbins * 4);
+        w.cursor = off;
+        off += round_up(nbins * 4);
+        w.nunits = off;
+        off += 256;
+        w.units = off;
+        off += round_up(w.max_units * 16);
+        w.records = off;
+        off += round_up(max_records(p) * 4);
+    }
+    w.acc = off;
+    if (p->dtype != MSDA_F32) off += round_up(value_elems(p) * 4);
+    w.total = off;
+    return w;
 }
 
 // A device pointer must be non-NULL when its tensor has elements, and
@@ -117,10 +191,13 @@ msda_status_t check_ptr(const void* ptr, int64_t elems) {
 // Launch through hipLaunchKernel, whose return code belongs to this launch
 // alone (no sticky error of an earlier, unrelated call is read or cleared).
 template <typename... Args>
-msda_status_t launch(const void* kernel, unsigned blocks, size_t lds_bytes, hipStream_t stream,
+msda_status_t launch(const void* kernel, int64_t blocks, int threads, size_t lds_bytes, hipStream_t stream,
                      Args... args) {
+    if (blocks <= 0) return MSDA_SUCCESS;
+    if (blocks > 0x7fffffff) return MSDA_ERROR_NOT_SUPPORTED;
     void* argv[] = {static_cast<void*>(&args)...};
-    return hipLaunchKernel(kernel, dim3(blocks), dim3(kBlock), argv, lds_bytes, stream) == hipSuccess
+    return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), argv, lds_bytes,
+                           stream) == hipSuccess
                ? MSDA_SUCCESS
                : MSDA_ERROR_HIP;
 }
@@ -128,38 +205,17 @@ msda_status_t launch(const void* kernel, unsigned blocks, size_t lds_bytes, hipS
 template <typename K>
 const void* kfn(K* k) { return reinterpret_cast<const void*>(k); }
 
-// ---- kernel selection ------------------------------------------------------
-
-struct Launch {
-    unsigned blocks;
-    size_t lds_bytes;
-};
-
-Launch geometry(const msda::Problem& pb, int lpr) {
-    const int64_t gpb = kBlock / lpr;
-    Launch g;
-    g.blocks = static_cast<unsigned>((pb.ngroups + gpb - 1) / gpb);
-    g.lds_bytes = sizeof(float) * msda::lds_words(static_cast<int>(gpb), pb.L * pb.P);
-    return g;
+int64_t fill_blocks(int64_t n) {
+    const int64_t want = (n + kBlock - 1) / kBlock;
+    return want < 8192 ? (want > 0 ? want : 1) : 8192;
 }
 
-template <int DT, int VECB, int LPR>
-msda_status_t fwd_launch(const msda::Problem& pb, const void* v, const void* loc, const void* w,
-                         void* out, hipStream_t st) {
-    const Launch g = geometry(pb, LPR);
-    const void* k = (pb.L == 4 && pb.P == 4) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4>)
-                                             : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0>);
-    return launch(k, g.blocks, g.lds_bytes, st, v, loc, w, out, pb);
+msda_status_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
+    const int64_t n16 = static_cast<int64_t>(bytes / 16);
+    return launch(kfn(&msda::msda_zero_kernel), fill_blocks(n16), kBlock, 0, st, static_cast<uint4*>(p), n16);
 }
 
-template <int DT, int VECB, int LPR>
-msda_status_t bwd_launch(const msda::Problem& pb, const void* v, const void* loc, const void* w,
-                         const void* gout, float* gacc, void* gloc, void* gw, hipStream_t st) {
-    const Launch g = geometry(pb, LPR);
-    const void* k = (pb.L == 4 && pb.P == 4) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4>)
-                                             : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0>);
-    return launch(k, g.blocks, g.lds_bytes, st, v, loc, w, gout, gacc, gloc, gw, pb);
-}
+// ---- kernel selection ----------------------------------------------------------
 
 // Calls F<DT, VECB, LPR>::run(args...) for the problem's lane split.
 template <int DT, template <int, int, int> class F, typename... A>
@@ -178,25 +234,185 @@ msda_status_t by_split(const LaneSplit& s, A&&... a) {
     }
 }
 
+template <template <int, int, int> class F, typename... A>
+msda_status_t by_dtype_split(msda_dtype_t dt, const LaneSplit& s, A&&... a) {
+    switch (dt) {
+        case MSDA_F32: return by_split<kF32, F>(s, a...);
+        case MSDA_F16: return by_split<kF16, F>(s, a...);
+        default: return by_split<kBF16, F>(s, a...);
+    }
+}
+
+bool is_l4p4(const msda::Problem& pb) { return pb.L == 4 && pb.P == 4; }
+
 template <int DT, int VECB, int LPR>
 struct Fwd {
     static msda_status_t run(const msda::Problem& pb, const void* v, const void* loc, const void* w,
                              void* out, hipStream_t st) {
-        return fwd_launch<DT, VECB, LPR>(pb, v, loc, w, out, st);
+        const int gpb = kBlock / LPR;
+        const int64_t blocks = (pb.ngroups + gpb - 1) / gpb;
+        const size_t lds = sizeof(float) * msda::lds_words(gpb, pb.L * pb.P);
+        const void* k = is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4>)
+                                    : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0>);
+        return launch(k, blocks, kBlock, lds, st, v, loc, w, out, pb);
+    }
+};
+
+// Groups per gradient workgroup: the full 256 lanes unless the staged
+// records (4 per sample) would exceed kMaxWgRecords.
+int grad_gpb(const msda::Problem& pb, int lpr) {
+    int gpb = kBlock / lpr;
+    const int cap = msda::kMaxWgRecords / (4 * pb.L * pb.P);
+    if (gpb > cap) gpb = cap < 1 ? 1 : cap;
+    return gpb;
+}
+
+template <int DT, int VECB, int LPR>
+struct Grad {
+    static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
+                             const void* w, const void* gout, float* gacc, uint32_t* records,
+                             int32_t* cursor, void* gloc, void* gw, hipStream_t st) {
+        const int gpb = binned ? grad_gpb(pb, LPR) : kBlock / LPR;
+        const int LP = pb.L * pb.P;
+        const int64_t blocks = int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
+        size_t lds = sizeof(float) * msda::lds_words(gpb, LP);
+        if (binned) lds += sizeof(int32_t) * (2 * size_t(pb.nseg) + gpb) + 2 * sizeof(uint32_t) * gpb * LP * 4;
+        const void* k;
+        if (binned)
+            k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)
+                            : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, true>);
+        else
+            k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, false>)
+                            : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, false>);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, records, cursor, gloc, gw, pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
-struct Bwd {
-    static msda_status_t run(const msda::Problem& pb, const void* v, const void* loc, const void* w,
-                             const void* gout, float* gacc, void* gloc, void* gw, hipStream_t st) {
-        return bwd_launch<DT, VECB, LPR>(pb, v, loc, w, gout, gacc, gloc, gw, st);
+struct Accum {
+    static msda_status_t run(const msda::Problem& pb, int64_t max_units, const void* loc, const void* w,
+                             const void* gout, const uint32_t* records, const int32_t* nunits,
+                             const int4* units, float* gacc, hipStream_t st) {
+        int max_shift = 0;
+        for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
+        const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
+                           (sizeof(uint32_t) + sizeof(uint16_t)) * msda::kUnitRecords +
+                           2 * sizeof(int32_t) * msda::kMaxSegKeys;
+        const void* k = is_l4p4(pb) ? kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR, 4, 4>)
+                                    : kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR, 0, 0>);
+        return launch(k, max_units, kBlock, lds, st, loc, w, gout, records, nunits, units, gacc, pb);
     }
 };
 
-unsigned fill_blocks(int64_t n) {
-    const int64_t want = (n + kBlock - 1) / kBlock;
-    return static_cast<unsigned>(want < 8192 ? (want > 0 ? want : 1) : 8192);
+template <int DT>
+msda_status_t count_launch(const msda::Problem& pb, const void* loc, int32_t* counts, hipStream_t st) {
+    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
+    const int64_t blocks = int64_t(pb.nplanes) * ((nsamp + msda::kCountChunk - 1) / msda::kCountChunk);
+    const void* k = is_l4p4(pb) ? kfn(&msda::msda_bin_count_kernel<DT, 4, 4>)
+                                : kfn(&msda::msda_bin_count_kernel<DT, 0, 0>);
+    return launch(k, blocks, kBlock, sizeof(int32_t) * pb.nseg, st, loc, counts, pb);
+}
+
+msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
+                                  const void* sampling_locations, const void* attention_weights,
+                                  const void* grad_output, const void* grad_value,
+                                  const void* grad_sampling_locations,
+                                  const void* grad_attention_weights) {
+    const int64_t nv = value_elems(problem), ns = sample_elems(problem), no = out_elems(problem);
+    MSDA_TRY(check_ptr(value, nv));
+    MSDA_TRY(check_ptr(sampling_locations, ns));
+    MSDA_TRY(check_ptr(attention_weights, ns));
+    MSDA_TRY(check_ptr(grad_output, no));
+    MSDA_TRY(check_ptr(grad_value, nv));
+    MSDA_TRY(check_ptr(grad_sampling_locations, ns));
+    MSDA_TRY(check_ptr(grad_attention_weights, ns));
+    return MSDA_SUCCESS;
+}
+
+// Records events[k] (when events is not NULL) on the stream just before
+// backward stage k; stage kStageEnd marks the end of the last stage.
+enum Stage { kStageZero = 0, kStageCount, kStageScan, kStageGrad, kStageAccum, kStageNarrow, kStageEnd };
+
+msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
+    if (events == nullptr) return MSDA_SUCCESS;
+    return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
+}
+
+// The backward into the float32 buffer gacc.  accumulate = 0: gacc is
+// overwritten in full; accumulate = 1: gacc is added to.
+msda_status_t backward_into(const msda_problem_t* problem, const void* value, const void* loc,
+                            const void* w, const void* gout, float* gacc, void* gloc, void* gw,
+                            char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
+    const msda::Problem pb = pack(problem);
+    const Layout lay = layout(problem, pb);
+    const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
+    if (!lay.binned) {
+        // Float atomics straight into gacc.
+        MSDA_TRY(mark(ev, kStageZero, st));
+        if (!accumulate) MSDA_TRY(zero_bytes(gacc, size_t(value_elems(problem)) * 4, st));
+        MSDA_TRY(mark(ev, kStageCount, st));
+        MSDA_TRY(mark(ev, kStageScan, st));
+        MSDA_TRY(mark(ev, kStageGrad, st));
+        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
+                                      static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                                      gloc, gw, st));
+        return mark(ev, kStageAccum, st);
+    }
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+    int32_t* cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
+    int32_t* nunits = reinterpret_cast<int32_t*>(ws + lay.nunits);
+    int4* units = reinterpret_cast<int4*>(ws + lay.units);
+    uint32_t* records = reinterpret_cast<uint32_t*>(ws + lay.records);
+
+    MSDA_TRY(mark(ev, kStageZero, st));
+    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
+    MSDA_TRY(mark(ev, kStageCount, st));
+    switch (problem->dtype) {
+        case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, loc, counts, st)); break;
+        case MSDA_F16: MSDA_TRY(count_launch<kF16>(pb, loc, counts, st)); break;
+        default: MSDA_TRY(count_launch<kBF16>(pb, loc, counts, st)); break;
+    }
+    MSDA_TRY(mark(ev, kStageScan, st));
+    MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), 1, msda::kScanThreads, 0, st,
+                    static_cast<const int32_t*>(counts), cursor, nunits, units, gacc, accumulate, pb));
+    MSDA_TRY(mark(ev, kStageGrad, st));
+    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, records, cursor,
+                                  gloc, gw, st));
+    MSDA_TRY(mark(ev, kStageAccum, st));
+    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, loc, w, gout,
+                                 static_cast<const uint32_t*>(records), static_cast<const int32_t*>(nunits),
+                                 static_cast<const int4*>(units), gacc, st);
+}
+
+msda_status_t backward_call(const msda_problem_t* problem, const void* value, const void* sampling_locations,
+                            const void* attention_weights, const void* grad_output, void* grad_value,
+                            void* grad_sampling_locations, void* grad_attention_weights, void* workspace,
+                            size_t workspace_bytes, hipEvent_t* ev, hipStream_t stream) {
+    MSDA_TRY(check_problem(problem));
+    MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output,
+                                 grad_value, grad_sampling_locations, grad_attention_weights));
+    const int64_t nv = value_elems(problem);
+    const size_t need = nv == 0 ? 0 : layout(problem, pack(problem)).total;
+    if (need > 0) {
+        if (workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
+        MSDA_TRY(check_ptr(workspace, 1));
+    }
+    if (nv == 0) return MSDA_SUCCESS;
+    char* ws = static_cast<char*>(workspace);
+    const Layout lay = layout(problem, pack(problem));
+    float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
+                                             : reinterpret_cast<float*>(ws + lay.acc);
+    MSDA_TRY(backward_into(problem, value, sampling_locations, attention_weights, grad_output, gacc,
+                           grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
+    MSDA_TRY(mark(ev, kStageNarrow, stream));
+    if (problem->dtype != MSDA_F32) {
+        const int64_t n8 = nv / 8;
+        const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
+                                                   : kfn(&msda::msda_narrow_kernel<kBF16>);
+        MSDA_TRY(launch(k, fill_blocks(n8), kBlock, 0, stream, reinterpret_cast<const float4*>(gacc),
+                        static_cast<uint4*>(grad_value), n8));
+    }
+    return mark(ev, kStageEnd, stream);
 }
 
 }  // namespace
@@ -229,113 +445,55 @@ msda_status_t msda_forward(const msda_problem_t* problem, const void* value,
     if (out_elems(problem) == 0) return MSDA_SUCCESS;
     const msda::Problem pb = pack(problem);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    switch (problem->dtype) {
-        case MSDA_F32:
-            return by_split<kF32, Fwd>(s, pb, value, sampling_locations, attention_weights, output, stream);
-        case MSDA_F16:
-            return by_split<kF16, Fwd>(s, pb, value, sampling_locations, attention_weights, output, stream);
-        default:
-            return by_split<kBF16, Fwd>(s, pb, value, sampling_locations, attention_weights, output, stream);
-    }
+    return by_dtype_split<Fwd>(problem->dtype, s, pb, value, sampling_locations, attention_weights, output,
+                                  stream);
 }
 
 size_t msda_backward_workspace_bytes(const msda_problem_t* problem) {
     if (check_problem(problem) != MSDA_SUCCESS) return 0;
-    if (problem->dtype == MSDA_F32) return 0;
-    return static_cast<size_t>(value_elems(problem)) * sizeof(float);
+    if (value_elems(problem) == 0) return 0;
+    return layout(problem, pack(problem)).total;
 }
-
-}  // extern "C"
-
-namespace {
-
-// The gradient kernel: accumulate into the float32 buffer gacc.
-msda_status_t backward_kernel(const msda_problem_t* problem, const void* value,
-                              const void* sampling_locations, const void* attention_weights,
-                              const void* grad_output, float* gacc, void* grad_sampling_locations,
-                              void* grad_attention_weights, hipStream_t stream) {
-    if (out_elems(problem) == 0) return MSDA_SUCCESS;
-    const msda::Problem pb = pack(problem);
-    const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    switch (problem->dtype) {
-        case MSDA_F32:
-            return by_split<kF32, Bwd>(s, pb, value, sampling_locations, attention_weights, grad_output,
-                                       gacc, grad_sampling_locations, grad_attention_weights, stream);
-        case MSDA_F16:
-            return by_split<kF16, Bwd>(s, pb, value, sampling_locations, attention_weights, grad_output,
-                                       gacc, grad_sampling_locations, grad_attention_weights, stream);
-        default:
-            return by_split<kBF16, Bwd>(s, pb, value, sampling_locations, attention_weights, grad_output,
-                                        gacc, grad_sampling_locations, grad_attention_weights, stream);
-    }
-}
-
-msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
-                                  const void* sampling_locations, const void* attention_weights,
-                                  const void* grad_output, const void* grad_value,
-                                  const void* grad_sampling_locations,
-                                  const void* grad_attention_weights) {
-    const int64_t nv = value_elems(problem), ns = sample_elems(problem), no = out_elems(problem);
-    MSDA_TRY(check_ptr(value, nv));
-    MSDA_TRY(check_ptr(sampling_locations, ns));
-    MSDA_TRY(check_ptr(attention_weights, ns));
-    MSDA_TRY(check_ptr(grad_output, no));
-    MSDA_TRY(check_ptr(grad_value, nv));
-    MSDA_TRY(check_ptr(grad_sampling_locations, ns));
-    MSDA_TRY(check_ptr(grad_attention_weights, ns));
-    return MSDA_SUCCESS;
-}
-
-}  // namespace
-
-extern "C" {
 
 msda_status_t msda_backward(const msda_problem_t* problem, const void* value,
                             const void* sampling_locations, const void* attention_weights,
                             const void* grad_output, void* grad_value,
                             void* grad_sampling_locations, void* grad_attention_weights,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    MSDA_TRY(check_problem(problem));
-    MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output,
-                                 grad_value, grad_sampling_locations, grad_attention_weights));
-    const int64_t nv = value_elems(problem);
-    const size_t need = msda_backward_workspace_bytes(problem);
-    if (need > 0) {
-        if (workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
-        MSDA_TRY(check_ptr(workspace, nv));
-    }
-    if (nv == 0) return MSDA_SUCCESS;
+    return backward_call(problem, value, sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes, nullptr,
+                         stream);
+}
 
-    // grad_value rows that no sample touches must come back as zero.
-    float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
-                                             : static_cast<float*>(workspace);
-    const int64_t n16 = nv * 4 / 16;   // nv is a multiple of 8
-    MSDA_TRY(launch(kfn(&msda::msda_zero_kernel), fill_blocks(n16), 0, stream,
-                    reinterpret_cast<uint4*>(gacc), n16));
-
-    MSDA_TRY(backward_kernel(problem, value, sampling_locations, attention_weights, grad_output, gacc,
-                             grad_sampling_locations, grad_attention_weights, stream));
-
-    if (problem->dtype != MSDA_F32) {
-        const int64_t n8 = nv / 8;
-        const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
-                                                   : kfn(&msda::msda_narrow_kernel<kBF16>);
-        MSDA_TRY(launch(k, fill_blocks(n8), 0, stream, reinterpret_cast<const float4*>(gacc),
-                        static_cast<uint4*>(grad_value), n8));
-    }
-    return MSDA_SUCCESS;
+msda_status_t msda_backward_profile(const msda_problem_t* problem, const void* value,
+                                    const void* sampling_locations, const void* attention_weights,
+                                    const void* grad_output, void* grad_value,
+                                    void* grad_sampling_locations, void* grad_attention_weights,
+                                    void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
+                                    hipStream_t stream) {
+    if (stage_events == nullptr) return MSDA_ERROR_INVALID_VALUE;
+    return backward_call(problem, value, sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
+                         stage_events, stream);
 }
 
 msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void* value,
                                        const void* sampling_locations, const void* attention_weights,
                                        const void* grad_output, float* grad_value_acc,
                                        void* grad_sampling_locations, void* grad_attention_weights,
-                                       hipStream_t stream) {
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
     MSDA_TRY(check_problem(problem));
     MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output,
                                  grad_value_acc, grad_sampling_locations, grad_attention_weights));
-    return backward_kernel(problem, value, sampling_locations, attention_weights, grad_output,
-                           grad_value_acc, grad_sampling_locations, grad_attention_weights, stream);
+    const size_t need = msda_backward_workspace_bytes(problem);
+    if (need > 0) {
+        if (workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
+        MSDA_TRY(check_ptr(workspace, 1));
+    }
+    if (value_elems(problem) == 0) return MSDA_SUCCESS;
+    return backward_into(problem, value, sampling_locations, attention_weights, grad_output, grad_value_acc,
+                         grad_sampling_locations, grad_attention_weights, static_cast<char*>(workspace), 1,
+                         nullptr, stream);
 }
 
 }  // extern "C"

@@ -36,6 +36,13 @@ struct Problem {
     int32_t lpr_active;      // lanes of a group that own channels
     int64_t ngroups;         // bs * Q * M
     LevelTable lv;
+    // Key segments of the binned backward (see msda_backward.hpp): level l
+    // is cut into segments of 2^seg_shift[l] keys, numbered from
+    // seg_base[l] within a (batch, head) plane; seg_base[L] = nseg.
+    int32_t nseg;
+    int32_t nplanes;         // bs * M
+    int32_t seg_shift[kMaxLevels];
+    int32_t seg_base[kMaxLevels + 1];
 };
 
 // ---- scalar conversions --------------------------------------------------
@@ -177,6 +184,7 @@ __device__ __forceinline__ bool pixel_coords(float loc_x, float loc_y, float Wf,
 // elements, relative to the (batch, head) base), their in-map flags and
 // bilinear weights (without the attention weight).
 struct Cell {
+    int32_t x0, y0;          // floor of the pixel coordinates
     int32_t off00;           // row (start + y0*W + x0) times the row pitch M*D
     int32_t dx, dy;          // offset steps to the x+1 and y+1 corners
     bool v00, v01, v10, v11;
@@ -187,23 +195,50 @@ __device__ __forceinline__ Cell make_cell(float x, float y, int32_t W, int32_t H
                                           int32_t pitch) {
     Cell c;
     float fx = floorf(x), fy = floorf(y);
-    int32_t x0 = static_cast<int32_t>(fx), y0 = static_cast<int32_t>(fy);
+    c.x0 = static_cast<int32_t>(fx);
+    c.y0 = static_cast<int32_t>(fy);
     c.lx = x - fx;
     c.ly = y - fy;
     c.hx = 1.0f - c.lx;
     c.hy = 1.0f - c.ly;
-    bool inx0 = x0 >= 0, inx1 = x0 + 1 < W, iny0 = y0 >= 0, iny1 = y0 + 1 < H;
+    bool inx0 = c.x0 >= 0, inx1 = c.x0 + 1 < W, iny0 = c.y0 >= 0, iny1 = c.y0 + 1 < H;
     c.v00 = iny0 & inx0;
     c.v01 = iny0 & inx1;
     c.v10 = iny1 & inx0;
     c.v11 = iny1 & inx1;
-    c.off00 = (start + y0 * W + x0) * pitch;
+    c.off00 = (start + c.y0 * W + c.x0) * pitch;
     c.dx = pitch;
     c.dy = W * pitch;
     return c;
 }
 
 // ---- launch geometry -----------------------------------------------------------
+
+constexpr int kBlock = 256;   // lanes of a full workgroup
+
+// LDS footprint (float words) of the staged locations and weights of gpb
+// groups: per group, 2*LP location words (+2 padding so neighbouring groups
+// start on different banks) and LP weight words (+1).
+__host__ __device__ constexpr int lds_words(int gpb, int lp) {
+    return gpb * (2 * lp + 2) + gpb * (lp + 1);
+}
+
+// Stage, as float32, the locations and weights of `gcount` groups into LDS
+// (layout of lds_words).  Group g is flattened group g0 + g * gstride.
+template <int DT>
+__device__ __forceinline__ void stage_groups(const void* __restrict__ loc, const void* __restrict__ attw,
+                                             float* sloc, float* sw, int64_t g0, int64_t gstride,
+                                             int gcount, int LP) {
+    const int two_lp = 2 * LP;
+    for (int i = threadIdx.x; i < gcount * two_lp; i += blockDim.x) {
+        const int g = i / two_lp, j = i - g * two_lp;
+        sloc[g * (two_lp + 2) + j] = load_scalar<DT>(loc, (g0 + g * gstride) * two_lp + j);
+    }
+    for (int i = threadIdx.x; i < gcount * LP; i += blockDim.x) {
+        const int g = i / LP, j = i - g * LP;
+        sw[g * (LP + 1) + j] = load_scalar<DT>(attw, (g0 + g * gstride) * LP + j);
+    }
+}
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that each XCD walks one contiguous range of tiles: neighbouring

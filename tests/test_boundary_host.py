@@ -100,13 +100,20 @@ def test_null_descriptor_and_null_shape_arrays():
 
 
 def test_workspace_bytes():
+    # fp32: the binned transpose only (up to 4 records of 4 bytes per sample,
+    # plus counts, cursors and the unit list); fp16/bf16 add a float32
+    # grad_value accumulator.
     p, keep = prob(dtype=0)
-    assert _lib.workspace_bytes(p) == 0
+    f32 = _lib.workspace_bytes(p)
+    samples = 2 * 300 * 8 * 4 * 4
+    assert 16 * samples <= f32 < 16 * samples + (8 << 20)
     for dt in (1, 2):
         p, keep = prob(dtype=dt)
-        assert _lib.workspace_bytes(p) == 2 * 17821 * 8 * 32 * 4
+        assert _lib.workspace_bytes(p) == f32 + 2 * 17821 * 8 * 32 * 4
     p, keep = prob(dtype=1, D=12)
     assert _lib.workspace_bytes(p) == 0   # invalid descriptor
+    p, keep = prob(bs=0)
+    assert _lib.workspace_bytes(p) == 0   # empty problem
 
 
 def _fwd(p, v, loc, w, out):
@@ -129,6 +136,7 @@ def test_backward_pointer_and_workspace_checks_return_before_launch():
     good = 0x10000
     p, keep = prob(dtype=2)
     need = _lib.workspace_bytes(p)
+    assert need > 0
     args = [good] * 7
     assert lib.msda_backward(ctypes.byref(p), *args, None, need, None) == INVALID      # no workspace
     assert lib.msda_backward(ctypes.byref(p), *args, good, need - 16, None) == INVALID  # too small

@@ -236,3 +236,37 @@ def test_sampled_outputs_one_by_one_at_full_size():
         b, q, m = int(rng.integers(2)), int(rng.integers(17821)), int(rng.integers(8))
         ref = oracle.forward_one(value, wl.spatial_shapes, wl.level_start_index, loc, w, b, q, m)
         assert_close(f"out[{b},{q},{m}]", out[b, q, m * D:(m + 1) * D], ref, 1e-5, atol=1e-6)
+
+
+def test_atomic_fallback_path():
+    """A level with more key segments than the binned backward supports
+    (one 1 x 600000 map) takes the float-atomic path; it must agree too."""
+    wl = W.make("fallback", 1, [(1, 600000)], 1, 8, 1, 64, "f32", seed=21)
+    t = to_device(wl)
+    check_forward(wl, gpu_forward(wl, t))
+    check_backward(wl, gpu_backward(wl, t))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_accumulate_adds(dtype):
+    """msda_backward_accumulate adds grad_value into a float32 buffer: two
+    calls on a pre-filled buffer give prefill + 2 * grad_value."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    wl = W.make("accumulate", 2, [(20, 30), (10, 15)], 4, 32, 4, 90, dtype, seed=8)
+    t = to_device(wl)
+    prob, keep = ops.problem_for(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"])
+    need = _lib.workspace_bytes(prob)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    acc = torch.full(t["value"].shape, 0.25, dtype=torch.float32, device="cuda")
+    gl = torch.empty_like(t["loc"])
+    gw = torch.empty_like(t["w"])
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        _lib.backward_accumulate(prob, t["value"].data_ptr(), t["loc"].data_ptr(), t["w"].data_ptr(),
+                                 t["g"].data_ptr(), acc.data_ptr(), gl.data_ptr(), gw.data_ptr(),
+                                 ws.data_ptr(), need, stream)
+    torch.cuda.synchronize()
+    rgv, rgl, rgw = oracle_backward(wl)
+    rtol, arms, atol = TOL[("f32", "bwd")] if dtype == "f32" else TOL[(dtype, "bwd")]
+    assert_close("accumulate/grad_value", f64(acc), 0.25 + 2 * rgv, rtol, arms, atol)
+    assert_close("accumulate/grad_w", f64(gw), rgw, *TOL[(dtype, "bwd")])
