@@ -68,7 +68,9 @@ msda_status_t check_problem(const msda_problem_t* p) {
     }
     if (keys != p->num_keys) return MSDA_ERROR_INVALID_VALUE;
     const int64_t pitch = int64_t(p->num_heads) * p->embed_dims;
-    if (int64_t(p->num_keys) * pitch >= kIndexLimit) return MSDA_ERROR_NOT_SUPPORTED;
+    // Per batch, value and output bytes are addressed with 32-bit offsets.
+    if (int64_t(p->num_keys) * pitch * elem_bytes(p->dtype) >= kIndexLimit) return MSDA_ERROR_NOT_SUPPORTED;
+    if (int64_t(p->num_queries) * pitch * elem_bytes(p->dtype) >= kIndexLimit) return MSDA_ERROR_NOT_SUPPORTED;
     if (int64_t(p->num_queries) * p->num_heads * p->num_levels * p->num_points * 2 >= kIndexLimit)
         return MSDA_ERROR_NOT_SUPPORTED;
     return MSDA_SUCCESS;
@@ -245,38 +247,41 @@ msda_status_t by_dtype_split(msda_dtype_t dt, const LaneSplit& s, A&&... a) {
 
 bool is_l4p4(const msda::Problem& pb) { return pb.L == 4 && pb.P == 4; }
 
+// Queries per workgroup: the full 256 lanes unless the per-sample LDS
+// records would exceed `max_samples` samples per workgroup.
+int tile_queries(const msda::Problem& pb, int lpr, int max_samples) {
+    int gpb = kBlock / lpr;
+    const int cap = max_samples / (pb.L * pb.P);
+    if (gpb > cap) gpb = cap < 1 ? 1 : cap;
+    return gpb;
+}
+
+int64_t plane_blocks(const msda::Problem& pb, int gpb) {
+    return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
+}
+
 template <int DT, int VECB, int LPR>
 struct Fwd {
     static msda_status_t run(const msda::Problem& pb, const void* v, const void* loc, const void* w,
                              void* out, hipStream_t st) {
-        const int gpb = kBlock / LPR;
-        const int64_t blocks = (pb.ngroups + gpb - 1) / gpb;
-        const size_t lds = sizeof(float) * msda::lds_words(gpb, pb.L * pb.P);
+        const int gpb = tile_queries(pb, LPR, 1024);
+        const size_t lds = sizeof(uint32_t) * gpb * (8 * pb.L * pb.P + 4);
         const void* k = is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4>)
                                     : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0>);
-        return launch(k, blocks, kBlock, lds, st, v, loc, w, out, pb);
+        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, out, pb, gpb);
     }
 };
-
-// Groups per gradient workgroup: the full 256 lanes unless the staged
-// records (4 per sample) would exceed kMaxWgRecords.
-int grad_gpb(const msda::Problem& pb, int lpr) {
-    int gpb = kBlock / lpr;
-    const int cap = msda::kMaxWgRecords / (4 * pb.L * pb.P);
-    if (gpb > cap) gpb = cap < 1 ? 1 : cap;
-    return gpb;
-}
 
 template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
                              const void* w, const void* gout, float* gacc, uint32_t* records,
                              int32_t* cursor, void* gloc, void* gw, hipStream_t st) {
-        const int gpb = binned ? grad_gpb(pb, LPR) : kBlock / LPR;
+        const int gpb = tile_queries(pb, LPR, msda::kMaxWgRecords / 4);
         const int LP = pb.L * pb.P;
-        const int64_t blocks = int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
-        size_t lds = sizeof(float) * msda::lds_words(gpb, LP);
-        if (binned) lds += sizeof(int32_t) * (2 * size_t(pb.nseg) + gpb) + 2 * sizeof(uint32_t) * gpb * LP * 4;
+        const int64_t blocks = plane_blocks(pb, gpb);
+        size_t lds = sizeof(uint32_t) * gpb * (12 * LP + 4);
+        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg) + 2 * sizeof(uint32_t) * gpb * LP * 4;
         const void* k;
         if (binned)
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)

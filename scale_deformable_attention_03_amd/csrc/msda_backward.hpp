@@ -42,6 +42,7 @@
 #pragma once
 
 #include "msda_device.hpp"
+#include "msda_forward.hpp"
 
 namespace msda {
 
@@ -267,11 +268,15 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 // ---------------------------------------------------------------------------
 // 3. gradient (gather): grad_w, grad_loc, and grad_value records or atomics
 // ---------------------------------------------------------------------------
-// Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes; workgroup
-// (plane, chunk) owns queries chunk*gpb .. +gpb of that (batch, head).
-// LDS: staged locations / weights (lds_words(gpb, LP) floats); when BINNED
-// also nseg histogram + nseg bases (int32), per-group record counts and
-// gpb*LP*4 record slots (two uint32 each).
+// Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes, plane-local
+// as in the forward.  A prologue (one lane per sample) computes the corner
+// offsets, the bilinear fractions and the gradient scales into LDS (12
+// words per sample) and, when BINNED, emits the sample's records; the main
+// loop gathers the four corner rows per sample and reduces
+//   grad_w   = <g, sample>,   grad_loc = (W*w*<g, d/dx>, H*w*<g, d/dy>)
+// over the group's lanes.
+// LDS: gpb * (12 * L * P + 4) words; when BINNED also nseg histogram and
+// nseg bases (int32) and 4 record slots per sample (2 words each).
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
@@ -281,46 +286,63 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                      void* __restrict__ grad_w, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
+    constexpr bool kFixedLP = L_CT != 0 && P_CT != 0;
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
     const int LP = L * P;
+    const int gstride = 12 * LP + 4;
 
-    extern __shared__ float smem[];
-    float* sloc = smem;
-    float* sw = smem + gpb * (2 * LP + 2);
-    int32_t* lhist = reinterpret_cast<int32_t*>(smem + lds_words(gpb, LP));
+    extern __shared__ uint32_t sm[];
+    uint32_t* srec = sm;
+    int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);
     int32_t* lbase = lhist + pb.nseg;
-    int32_t* gcnt = lbase + pb.nseg;
-    uint32_t* lrec = reinterpret_cast<uint32_t*>(gcnt + gpb);
+    uint32_t* lrec = reinterpret_cast<uint32_t*>(lbase + pb.nseg);
     uint32_t* lsr = lrec + gpb * LP * 4;
 
-    const int nqc = (pb.Q + gpb - 1) / gpb;
-    const int tile = static_cast<int>(xcd_tile(blockIdx.x, gridDim.x));
-    const int pl = tile / nqc, qc = tile - pl * nqc;
-    const int b = pl / pb.M, m = pl - b * pb.M;
-    const int q0 = qc * gpb;
-    const int gcount = min(gpb, pb.Q - q0);
-    const int64_t G0 = (static_cast<int64_t>(b) * pb.Q + q0) * pb.M + m;
-
+    const PlaneTile t = plane_tile(pb, gpb);
+    const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
     if constexpr (BINNED) {
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) lhist[i] = 0;
+        __syncthreads();
     }
-    stage_groups<DT>(loc, attw, sloc, sw, G0, pb.M, gcount, LP);
+
+    // prologue: one lane per sample
+    for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+        const int g = i / LP, lp = i - g * LP, l = lp / P;
+        const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+        const int H = pb.lv.H[l], W = pb.lv.W[l];
+        const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), H, W,
+                                         pb.lv.start[l], pitch);
+        const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        uint32_t* r = srec + g * gstride + lp * 12;
+        *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
+        *reinterpret_cast<float4*>(r + 4) = make_float4(c.hx, c.lx, c.hy, c.ly);
+        *reinterpret_cast<float4*>(r + 8) = make_float4(static_cast<float>(W) * aw, static_cast<float>(H) * aw,
+                                                        aw * c.hy, aw * c.ly);
+        if constexpr (BINNED) {
+            int k = 0;
+            if (c.ok) {
+                const uint32_t s = static_cast<uint32_t>((t.q0 + g) * LP + lp);
+                for_each_record(s, c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l], [&](uint32_t rec, int seg) {
+                    const int rank = atomicAdd(&lhist[seg], 1);
+                    lrec[4 * i + k] = rec;
+                    lsr[4 * i + k] = (static_cast<uint32_t>(seg) << 16) | static_cast<uint32_t>(rank);
+                    ++k;
+                });
+            }
+            for (; k < 4; ++k) lsr[4 * i + k] = 0xffffffffu;
+        }
+    }
     __syncthreads();
 
     const int lg = threadIdx.x / LPR, li = threadIdx.x % LPR;
-    if (lg < gcount) {
+    if (lg < t.gcount) {
         const bool active = li < pb.lpr_active;
-        const int64_t G = G0 + static_cast<int64_t>(lg) * pb.M;
-        const int pitch = pb.M * pb.D;
-        const int64_t vofs = static_cast<int64_t>(b) * pb.K * pitch + static_cast<int64_t>(m) * pb.D + li * VEC;
-        const char* vb = static_cast<const char*>(value) + vofs * E;
-        float* gb = gacc + vofs;
-        const float* my_loc = sloc + lg * (2 * LP + 2);
-        const float* my_w = sw + lg * (LP + 1);
-        uint32_t* my_rec = lrec + lg * LP * 4;
-        uint32_t* my_sr = lsr + lg * LP * 4;
-        int nrec = 0;
+        const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
+        const __amdgpu_buffer_rsrc_t vr = value_plane<E>(value, pb, t.b, t.m);
+        const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
+        const uint32_t* rec = srec + lg * gstride;
+        float* gb = gacc + (static_cast<int64_t>(t.b) * pb.K * pb.M + t.m) * pb.D + li * VEC;
 
         float g[VEC];
         if (active) {
@@ -329,90 +351,81 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 #pragma unroll
             for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
         }
+        constexpr int kOwn = kFixedLP ? (L_CT * P_CT + LPR - 1) / LPR : 1;
+        float own_w[kOwn], own_x[kOwn], own_y[kOwn];
 
 #pragma unroll
-        for (int l = 0; l < L; ++l) {
-            const int H = pb.lv.H[l], W = pb.lv.W[l], start = pb.lv.start[l];
-            const float Hf = static_cast<float>(H), Wf = static_cast<float>(W);
+        for (int lp = 0; lp < LP; ++lp) {
+            const uint4 o = *reinterpret_cast<const uint4*>(rec + lp * 12);
+            const float4 f = *reinterpret_cast<const float4*>(rec + lp * 12 + 4);   // hx lx hy ly
+            const float4 sc = *reinterpret_cast<const float4*>(rec + lp * 12 + 8);  // W*w H*w w*hy w*ly
+            float gw = 0.0f, gx = 0.0f, gy = 0.0f;
+            if (active) {
+                float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+                widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v00);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v01);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v10);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v11);
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int lp = l * P + p;
-                float x, y;
-                const bool ok = pixel_coords(my_loc[2 * lp], my_loc[2 * lp + 1], Wf, Hf, x, y);
-                const float aw = my_w[lp];
-                float gw = 0.0f, gx = 0.0f, gy = 0.0f;
-                if (ok) {
-                    const Cell c = make_cell(x, y, W, H, start, pitch);
-                    if (active) {
-                        float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) v00[i] = v01[i] = v10[i] = v11[i] = 0.0f;
-                        if (c.v00) widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00) * E), v00);
-                        if (c.v01) widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dx) * E), v01);
-                        if (c.v10) widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dy) * E), v10);
-                        if (c.v11) widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dy + c.dx) * E), v11);
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) {
-                            const float top = c.hx * v00[i] + c.lx * v01[i];
-                            const float bot = c.hx * v10[i] + c.lx * v11[i];
-                            gw += g[i] * (c.hy * top + c.ly * bot);
-                            gx += g[i] * (c.hy * (v01[i] - v00[i]) + c.ly * (v11[i] - v10[i]));
-                            gy += g[i] * (bot - top);
-                        }
-                        if constexpr (!BINNED) {
-                            const float wy0 = aw * c.hy, wy1 = aw * c.ly;
-#pragma unroll
-                            for (int i = 0; i < VEC; ++i) {
-                                if (c.v00) atomic_add_f32(gb + c.off00 + i, wy0 * c.hx * g[i]);
-                                if (c.v01) atomic_add_f32(gb + c.off00 + c.dx + i, wy0 * c.lx * g[i]);
-                                if (c.v10) atomic_add_f32(gb + c.off00 + c.dy + i, wy1 * c.hx * g[i]);
-                                if (c.v11) atomic_add_f32(gb + c.off00 + c.dy + c.dx + i, wy1 * c.lx * g[i]);
-                            }
-                        }
-                    }
-                    if constexpr (BINNED) {
-                        if (li == 0) {
-                            const uint32_t s = static_cast<uint32_t>((q0 + lg) * LP + lp);
-                            for_each_record(s, c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l],
-                                            [&](uint32_t rec, int seg) {
-                                                const int rank = atomicAdd(&lhist[seg], 1);
-                                                my_rec[nrec] = rec;
-                                                my_sr[nrec] = (static_cast<uint32_t>(seg) << 16) |
-                                                              static_cast<uint32_t>(rank);
-                                                ++nrec;
-                                            });
-                        }
-                    }
+                for (int i = 0; i < VEC; ++i) {
+                    const float top = f.x * v00[i] + f.y * v01[i];
+                    const float bot = f.x * v10[i] + f.y * v11[i];
+                    gw += g[i] * (f.z * top + f.w * bot);
+                    gx += g[i] * (f.z * (v01[i] - v00[i]) + f.w * (v11[i] - v10[i]));
+                    gy += g[i] * (bot - top);
                 }
-                gw = group_sum<LPR>(gw);
-                gx = group_sum<LPR>(gx);
-                gy = group_sum<LPR>(gy);
-                if (li == 0) {
-                    const int64_t s = G * LP + lp;
-                    store_scalar<DT>(grad_w, s, gw);
-                    store_scalar<DT>(grad_loc, 2 * s, ok ? Wf * aw * gx : 0.0f);
-                    store_scalar<DT>(grad_loc, 2 * s + 1, ok ? Hf * aw * gy : 0.0f);
+                if constexpr (!BINNED) {
+                    if (o.x != kOffMap)
+                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.x / E + i, sc.z * f.x * g[i]);
+                    if (o.y != kOffMap)
+                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.y / E + i, sc.z * f.y * g[i]);
+                    if (o.z != kOffMap)
+                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.z / E + i, sc.w * f.x * g[i]);
+                    if (o.w != kOffMap)
+                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.w / E + i, sc.w * f.y * g[i]);
                 }
             }
+            // a sample off the map (all four corners at kOffMap) gets exactly
+            // zero gradients, whatever grad_output holds
+            const bool off = ((o.x & o.y & o.z & o.w) & kOffMap) != 0u;
+            gw = off ? 0.0f : group_sum<LPR>(gw);
+            gx = off ? 0.0f : group_sum<LPR>(gx) * sc.x;
+            gy = off ? 0.0f : group_sum<LPR>(gy) * sc.y;
+            if constexpr (kFixedLP) {
+                // lane lp % LPR keeps this sample's results and writes them below
+                if (li == lp % LPR) {
+                    own_w[lp / LPR] = gw;
+                    own_x[lp / LPR] = gx;
+                    own_y[lp / LPR] = gy;
+                }
+            } else if (li == 0) {
+                const int64_t s = G * LP + lp;
+                store_scalar<DT>(grad_w, s, gw);
+                store_scalar<DT>(grad_loc, 2 * s, gx);
+                store_scalar<DT>(grad_loc, 2 * s + 1, gy);
+            }
         }
-        if constexpr (BINNED) {
-            if (li == 0) gcnt[lg] = nrec;
+        if constexpr (kFixedLP) {
+#pragma unroll
+            for (int k = 0; k < kOwn; ++k) {
+                const int lp = li + k * LPR;
+                if (lp < L_CT * P_CT) {
+                    const int64_t s = G * (L_CT * P_CT) + lp;
+                    store_scalar<DT>(grad_w, s, own_w[k]);
+                    store_scalar<DT>(grad_loc, 2 * s, own_x[k]);
+                    store_scalar<DT>(grad_loc, 2 * s + 1, own_y[k]);
+                }
+            }
         }
     }
     if constexpr (BINNED) {
-        if (threadIdx.x / LPR >= gcount && threadIdx.x % LPR == 0 && threadIdx.x / LPR < gpb)
-            gcnt[threadIdx.x / LPR] = 0;
         __syncthreads();
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x)
-            if (lhist[i] != 0) lbase[i] = atomicAdd(&cursor[static_cast<int64_t>(pl) * pb.nseg + i], lhist[i]);
+            if (lhist[i] != 0) lbase[i] = atomicAdd(&cursor[static_cast<int64_t>(t.pl) * pb.nseg + i], lhist[i]);
         __syncthreads();
-        const int slots = 4 * LP;
-        for (int i = threadIdx.x; i < gpb * slots; i += blockDim.x) {
-            const int grp = i / slots, j = i - grp * slots;
-            if (j < gcnt[grp]) {
-                const uint32_t sr = lsr[i];
-                records[lbase[sr >> 16] + static_cast<int>(sr & 0xffffu)] = lrec[i];
-            }
+        for (int i = threadIdx.x; i < t.gcount * LP * 4; i += blockDim.x) {
+            const uint32_t sr = lsr[i];
+            if (sr != 0xffffffffu) records[lbase[sr >> 16] + static_cast<int>(sr & 0xffffu)] = lrec[i];
         }
     }
 }
@@ -484,9 +497,15 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
         order[atomicAdd(&cur[recs[i] >> 24], 1)] = static_cast<uint16_t>(i);
     __syncthreads();
 
-    // Workers walk key-sorted slices; rows kf..kf+1 and kl..kl+1 of a slice
+    // Workers (LPR lanes each) walk key-sorted slices, accumulating a row in
+    // registers while the key holds.  Rows kf..kf+1 and kl..kl+1 of a slice
     // may also receive contributions from neighbouring workers and are merged
-    // with LDS adds, every other row is this worker's alone.
+    // with LDS adds; every other row is this worker's alone.  Records are
+    // taken kBatch at a time: lanes decode one record each (coordinates,
+    // corner weights, grad_output offset), the worker's lanes then load the
+    // kBatch grad_output rows together and fold them in key order.
+    constexpr int kBatch = 8;
+    constexpr int kPer = kBatch > LPR ? kBatch / LPR : 1;     // records a lane decodes
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
@@ -494,6 +513,12 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
     if (r0 < r1) {
         const int kf = static_cast<int>(recs[order[r0]] >> 24), kl = static_cast<int>(recs[order[r1 - 1]] >> 24);
         const float Hf = static_cast<float>(H), Wf = static_cast<float>(W);
+        const int64_t gplane = static_cast<int64_t>(b) * pb.Q * pb.M + m;      // group (b, 0, m)
+        const __amdgpu_buffer_rsrc_t gr = make_rsrc(
+            static_cast<const char*>(gout) + gplane * D * E,
+            static_cast<uint32_t>((static_cast<int64_t>(pb.Q) * pb.M - m) * D * E));
+        const uint32_t qstride = static_cast<uint32_t>(pb.M * D * E);
+        const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
         auto flush = [&](int row, const float* acc) {
             if (!active || row >= nk) return;
             float* dst = tile + row * D + li * VEC;
@@ -509,46 +534,75 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
 #pragma unroll
         for (int i = 0; i < VEC; ++i) accA[i] = accB[i] = 0.0f;
         int key = -1;
-        for (int r = r0; r < r1; ++r) {
-            const uint32_t rec = recs[order[r]];
-            const int rkey = static_cast<int>(rec >> 24);
-            if (rkey != key) {
-                if (key >= 0) {
-                    flush(key, accA);
-                    if (rkey == key + 1) {
+        for (int base = r0; base < r1; base += kBatch) {
+            int dkey[kPer];
+            float dca[kPer], dcb[kPer];
+            uint32_t dgo[kPer];
 #pragma unroll
-                        for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
-                    } else {
-                        flush(key + 1, accB);
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
-                    }
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
+            for (int k = 0; k < kPer; ++k) {
+                const int j = li + k * LPR;
+                dkey[k] = -1;
+                dca[k] = dcb[k] = 0.0f;
+                dgo[k] = 0u;
+                if (j < kBatch && base + j < r1) {
+                    const uint32_t rec = recs[order[base + j]];
+                    const int s = static_cast<int>(rec & kRecSampleMask);
+                    const int q = s / LP, lp = s - q * LP;
+                    const int64_t si = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
+                    float x, y;
+                    pixel_coords(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), Wf, Hf, x, y);
+                    const float fx = floorf(x), fy = floorf(y);
+                    const float lx = x - fx, ly = y - fy;
+                    const float aw = load_scalar<DT>(attw, si);
+                    const float wy = aw * (((rec >> 21) & 1u) ? ly : 1.0f - ly);
+                    const float cl = wy * (1.0f - lx), cr = wy * lx;
+                    const uint32_t mode = (rec >> 22) & 3u;
+                    dkey[k] = static_cast<int>(rec >> 24);
+                    dca[k] = mode == kRightOnly ? cr : cl;
+                    dcb[k] = mode == kBoth ? cr : 0.0f;
+                    dgo[k] = static_cast<uint32_t>(q) * qstride;
                 }
-                key = rkey;
             }
-            const int s = static_cast<int>(rec & kRecSampleMask);
-            const int q = s / LP, lp = s - q * LP;
-            const int64_t G = (static_cast<int64_t>(b) * pb.Q + q) * pb.M + m;
-            const int64_t si = G * LP + lp;
-            float x, y;
-            pixel_coords(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), Wf, Hf, x, y);
-            const float fx = floorf(x), fy = floorf(y);
-            const float lx = x - fx, ly = y - fy;
-            const float aw = load_scalar<DT>(attw, si);
-            const float wy = aw * (((rec >> 21) & 1u) ? ly : 1.0f - ly);
-            const float cl = wy * (1.0f - lx), cr = wy * lx;
-            const uint32_t mode = (rec >> 22) & 3u;
-            const float ca = mode == kRightOnly ? cr : cl;
-            const float cb = mode == kBoth ? cr : 0.0f;
-            if (active) {
-                float g[VEC];
-                widen<DT, VECB>(load_raw<VECB>(static_cast<const char*>(gout) + (G * D + li * VEC) * E), g);
+            int bkey[kBatch];
+            float bca[kBatch], bcb[kBatch], gv[kBatch][VEC];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int src = j % LPR, k = j / LPR < kPer ? j / LPR : 0;
+                bkey[j] = __shfl(dkey[k], src, LPR);
+                bca[j] = __shfl(dca[k], src, LPR);
+                bcb[j] = __shfl(dcb[k], src, LPR);
+                const uint32_t go = static_cast<uint32_t>(__shfl(static_cast<int>(dgo[k]), src, LPR));
+                if (active && bkey[j] >= 0) {
+                    widen<DT, VECB>(buffer_load<VECB>(gr, go + lane_b), gv[j]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) gv[j][i] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int rkey = bkey[j];
+                if (rkey < 0) break;
+                if (rkey != key) {
+                    if (key >= 0) {
+                        flush(key, accA);
+                        if (rkey == key + 1) {
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
+                        } else {
+                            flush(key + 1, accB);
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
+                        }
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
+                    }
+                    key = rkey;
+                }
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    accA[i] += ca * g[i];
-                    accB[i] += cb * g[i];
+                    accA[i] += bca[j] * gv[j][i];
+                    accB[i] += bcb[j] * gv[j][i];
                 }
             }
         }

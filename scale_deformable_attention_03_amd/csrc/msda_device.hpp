@@ -162,6 +162,33 @@ __device__ __forceinline__ Raw<VECB> narrow(const float* in) {
     return r;
 }
 
+// ---- buffer loads ------------------------------------------------------------
+
+// Raw buffer descriptor over `bytes` bytes from `base` (gfx9 word 3).  A load
+// whose offset lies at or beyond `bytes` returns zeros, which is how corners
+// off the map are read: their offset is set to kOffMap.
+constexpr uint32_t kOffMap = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+template <int VECB>
+__device__ __forceinline__ Raw<VECB> buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Raw<VECB> out;
+    if constexpr (VECB == 16) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+        out.w[0] = v[0]; out.w[1] = v[1]; out.w[2] = v[2]; out.w[3] = v[3];
+    } else if constexpr (VECB == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0);
+        out.w[0] = v[0]; out.w[1] = v[1];
+    } else {
+        out.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    }
+    return out;
+}
+
 // ---- sampling geometry ---------------------------------------------------------
 
 // Pixel coordinates of a normalised location under align_corners=False:
@@ -215,30 +242,6 @@ __device__ __forceinline__ Cell make_cell(float x, float y, int32_t W, int32_t H
 // ---- launch geometry -----------------------------------------------------------
 
 constexpr int kBlock = 256;   // lanes of a full workgroup
-
-// LDS footprint (float words) of the staged locations and weights of gpb
-// groups: per group, 2*LP location words (+2 padding so neighbouring groups
-// start on different banks) and LP weight words (+1).
-__host__ __device__ constexpr int lds_words(int gpb, int lp) {
-    return gpb * (2 * lp + 2) + gpb * (lp + 1);
-}
-
-// Stage, as float32, the locations and weights of `gcount` groups into LDS
-// (layout of lds_words).  Group g is flattened group g0 + g * gstride.
-template <int DT>
-__device__ __forceinline__ void stage_groups(const void* __restrict__ loc, const void* __restrict__ attw,
-                                             float* sloc, float* sw, int64_t g0, int64_t gstride,
-                                             int gcount, int LP) {
-    const int two_lp = 2 * LP;
-    for (int i = threadIdx.x; i < gcount * two_lp; i += blockDim.x) {
-        const int g = i / two_lp, j = i - g * two_lp;
-        sloc[g * (two_lp + 2) + j] = load_scalar<DT>(loc, (g0 + g * gstride) * two_lp + j);
-    }
-    for (int i = threadIdx.x; i < gcount * LP; i += blockDim.x) {
-        const int g = i / LP, j = i - g * LP;
-        sw[g * (LP + 1) + j] = load_scalar<DT>(attw, (g0 + g * gstride) * LP + j);
-    }
-}
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that each XCD walks one contiguous range of tiles: neighbouring

@@ -5,97 +5,145 @@
 // grid_sample (zeros padding, align_corners=False) at the L*P locations of a
 // (batch, query, head), weighted by the attention weights and summed.
 //
-// Mapping.  A workgroup of 256 lanes owns GPB = 256/LPR consecutive groups
-// (b, q, m).  It first stages the groups' locations and weights (contiguous
-// in memory) into LDS as float32, then each group's LPR lanes walk the L*P
-// samples: level geometry comes from launch arguments (scalar registers),
-// the four corner rows are coalesced VECB-byte-per-lane reads, and the
-// weighted corners are accumulated in float32 registers.  The path is a
-// gather; there is no dense contraction, so no MFMA.
+// Mapping.  A workgroup owns gpb consecutive queries of one (batch, head)
+// plane; consecutive workgroups walk a plane's queries, and the XCD-aware
+// block order gives each XCD contiguous runs of them, so a plane's value
+// rows (K * D elements) stay in that XCD's L2.
+//   prologue   one lane per sample: pixel coordinates, the cell's four corner
+//              byte offsets within the plane (kOffMap for a corner off the
+//              map) and the four corner weights times the attention weight,
+//              into LDS (8 words per sample);
+//   main loop  LPR lanes per query, VECB bytes of the D channels per lane:
+//              per sample, two broadcast LDS reads, four raw-buffer loads
+//              (off-map corners read as zeros) and 4*VEC FMAs into float32
+//              registers; no branches.
+// The path is a gather; there is no dense contraction, so no MFMA.
 #pragma once
 
 #include "msda_device.hpp"
 
 namespace msda {
 
-// ---------------------------------------------------------------------------
-// Forward
-// ---------------------------------------------------------------------------
+// Byte offsets of a sample's four corners within its (batch, head) plane of
+// value (row pitch `pitch` bytes) and its bilinear cell.  Off-map samples get
+// kOffMap offsets and zero fractions, with ok = false.
+struct Corners {
+    uint32_t o00, o01, o10, o11;
+    float hx, lx, hy, ly;
+    int x0, y0;
+    bool ok;
+};
+
+__device__ __forceinline__ Corners sample_corners(float loc_x, float loc_y, int H, int W, int start,
+                                                  uint32_t pitch) {
+    Corners c;
+    float x, y;
+    c.ok = pixel_coords(loc_x, loc_y, static_cast<float>(W), static_cast<float>(H), x, y);
+    if (!c.ok) {
+        c.o00 = c.o01 = c.o10 = c.o11 = kOffMap;
+        c.hx = c.lx = c.hy = c.ly = 0.0f;
+        c.x0 = c.y0 = 0;
+        return c;
+    }
+    const float fx = floorf(x), fy = floorf(y);
+    c.x0 = static_cast<int>(fx);
+    c.y0 = static_cast<int>(fy);
+    c.lx = x - fx;
+    c.ly = y - fy;
+    c.hx = 1.0f - c.lx;
+    c.hy = 1.0f - c.ly;
+    const bool inx0 = c.x0 >= 0, inx1 = c.x0 + 1 < W, iny0 = c.y0 >= 0, iny1 = c.y0 + 1 < H;
+    const int row = start + c.y0 * W + c.x0;          // may be negative; used only when in map
+    c.o00 = (iny0 & inx0) ? static_cast<uint32_t>(row) * pitch : kOffMap;
+    c.o01 = (iny0 & inx1) ? static_cast<uint32_t>(row + 1) * pitch : kOffMap;
+    c.o10 = (iny1 & inx0) ? static_cast<uint32_t>(row + W) * pitch : kOffMap;
+    c.o11 = (iny1 & inx1) ? static_cast<uint32_t>(row + W + 1) * pitch : kOffMap;
+    return c;
+}
+
+// Plane-local workgroup: queries q0 .. q0 + gcount - 1 of plane (b, m).
+struct PlaneTile {
+    int b, m, q0, gcount, pl;
+    int64_t G0;        // flattened group (b, q0, m)
+};
+
+__device__ __forceinline__ PlaneTile plane_tile(const Problem& pb, int gpb) {
+    PlaneTile t;
+    const int nqc = (pb.Q + gpb - 1) / gpb;
+    const int tile = static_cast<int>(xcd_tile(blockIdx.x, gridDim.x));
+    t.pl = tile / nqc;
+    const int qc = tile - t.pl * nqc;
+    t.b = t.pl / pb.M;
+    t.m = t.pl - t.b * pb.M;
+    t.q0 = qc * gpb;
+    t.gcount = min(gpb, pb.Q - t.q0);
+    t.G0 = (static_cast<int64_t>(t.b) * pb.Q + t.q0) * pb.M + t.m;
+    return t;
+}
+
+// Raw-buffer view of the value rows of plane (b, m): from element
+// (b, 0, m, 0) to the end of batch b.
+template <int E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value, const Problem& pb, int b, int m) {
+    const int64_t batch = static_cast<int64_t>(pb.K) * pb.M * pb.D;
+    const char* base = static_cast<const char*>(value) + (b * batch + static_cast<int64_t>(m) * pb.D) * E;
+    return make_rsrc(base, static_cast<uint32_t>((batch - static_cast<int64_t>(m) * pb.D) * E));
+}
+
+// Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes.
+// LDS: gpb * (8 * L * P + 4) words.
 template <int DT, int VECB, int LPR, int L_CT, int P_CT>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
-                    const void* __restrict__ attw, void* __restrict__ out, Problem pb) {
+                    const void* __restrict__ attw, void* __restrict__ out, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
-    constexpr int GPB = kBlock / LPR;
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
     const int LP = L * P;
+    const int gstride = 8 * LP + 4;
 
-    extern __shared__ float smem[];
-    float* sloc = smem;
-    float* sw = smem + GPB * (2 * LP + 2);
+    extern __shared__ uint32_t sm[];
+    const PlaneTile t = plane_tile(pb, gpb);
+    const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
 
-    const int64_t g0 = xcd_tile(blockIdx.x, gridDim.x) * GPB;
-    const int gcount = static_cast<int>(min(static_cast<int64_t>(GPB), pb.ngroups - g0));
-    stage_groups<DT>(loc, attw, sloc, sw, g0, 1, gcount, LP);
+    // prologue: one lane per sample
+    for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+        const int g = i / LP, lp = i - g * LP, l = lp / P;
+        const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+        const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1),
+                                         pb.lv.H[l], pb.lv.W[l], pb.lv.start[l], pitch);
+        const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        const float wy0 = aw * c.hy, wy1 = aw * c.ly;
+        uint32_t* r = sm + g * gstride + lp * 8;
+        *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
+        *reinterpret_cast<float4*>(r + 4) = make_float4(wy0 * c.hx, wy0 * c.lx, wy1 * c.hx, wy1 * c.lx);
+    }
     __syncthreads();
 
     const int lg = threadIdx.x / LPR, li = threadIdx.x % LPR;
-    if (lg >= gcount || li >= pb.lpr_active) return;
-
-    const int64_t G = g0 + lg;
-    const int m = static_cast<int>(G % pb.M);
-    const int b = static_cast<int>((G / pb.M) / pb.Q);
-    const int pitch = pb.M * pb.D;
-    const char* vb = static_cast<const char*>(value) +
-                     (static_cast<int64_t>(b) * pb.K * pitch + static_cast<int64_t>(m) * pb.D +
-                      li * VEC) * E;
-    const float* my_loc = sloc + lg * (2 * LP + 2);
-    const float* my_w = sw + lg * (LP + 1);
+    if (lg >= t.gcount || li >= pb.lpr_active) return;
+    const __amdgpu_buffer_rsrc_t vr = value_plane<E>(value, pb, t.b, t.m);
+    const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
+    const uint32_t* rec = sm + lg * gstride;
 
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
-
 #pragma unroll
-    for (int l = 0; l < L; ++l) {
-        const int H = pb.lv.H[l], W = pb.lv.W[l], start = pb.lv.start[l];
-        const float Hf = static_cast<float>(H), Wf = static_cast<float>(W);
+    for (int lp = 0; lp < LP; ++lp) {
+        const uint4 o = *reinterpret_cast<const uint4*>(rec + lp * 8);
+        const float4 w = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);
+        float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+        widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v00);
+        widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v01);
+        widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v10);
+        widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v11);
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int lp = l * P + p;
-            float x, y;
-            if (!pixel_coords(my_loc[2 * lp], my_loc[2 * lp + 1], Wf, Hf, x, y)) continue;
-            const Cell c = make_cell(x, y, W, H, start, pitch);
-            const float aw = my_w[lp];
-            const float wy0 = aw * c.hy, wy1 = aw * c.ly;
-            const float w00 = wy0 * c.hx, w01 = wy0 * c.lx, w10 = wy1 * c.hx, w11 = wy1 * c.lx;
-            float v[VEC];
-            if (c.v00) {
-                widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00) * E), v);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += w00 * v[i];
-            }
-            if (c.v01) {
-                widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dx) * E), v);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += w01 * v[i];
-            }
-            if (c.v10) {
-                widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dy) * E), v);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += w10 * v[i];
-            }
-            if (c.v11) {
-                widen<DT, VECB>(load_raw<VECB>(vb + static_cast<int64_t>(c.off00 + c.dy + c.dx) * E), v);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) acc[i] += w11 * v[i];
-            }
-        }
+        for (int i = 0; i < VEC; ++i) acc[i] += w.x * v00[i] + w.y * v01[i] + w.z * v10[i] + w.w * v11[i];
     }
-    char* ob = static_cast<char*>(out) + (G * pb.D + li * VEC) * E;
-    store_raw<VECB>(ob, narrow<DT, VECB>(acc));
+    const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
+    store_raw<VECB>(static_cast<char*>(out) + (G * pb.D + li * VEC) * E, narrow<DT, VECB>(acc));
 }
 
 }  // namespace msda

@@ -84,11 +84,15 @@ def test_invalid_descriptors(kw, code):
 
 
 def test_index_range_limit():
-    # num_keys * heads * dims must stay below 2^31 (32-bit per-batch offsets)
+    # per batch, value and output bytes stay below 2^31 (32-bit byte offsets)
     p, keep = prob(shapes=[(4096, 2048)], M=8, D=256, P=1, Q=1)
     assert _lib.validate(p) == UNSUPPORTED
-    p, keep = prob(shapes=[(4096, 2048)], M=1, D=128, P=1, Q=1)
+    p, keep = prob(shapes=[(4096, 2048)], M=1, D=64, P=1, Q=1)              # 2^31 bytes exactly
+    assert _lib.validate(p) == UNSUPPORTED
+    p, keep = prob(shapes=[(4096, 2048)], M=1, D=64, P=1, Q=1, dtype=1)     # fp16: 2^30 bytes
     assert _lib.validate(p) == OK
+    p, keep = prob(shapes=[(64, 64)], K=None, M=8, D=256, P=1, Q=1 << 18)   # output 2^31 bytes
+    assert _lib.validate(p) == UNSUPPORTED
 
 
 def test_null_descriptor_and_null_shape_arrays():
