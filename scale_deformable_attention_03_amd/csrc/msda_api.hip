@@ -130,14 +130,13 @@ msda::Problem pack(const msda_problem_t* p) {
     return pb;
 }
 
-// The binned backward needs: sample indices per plane within the record
+// The binned backward needs: query indices within the record's 24-bit
 // field, at most kMaxSegments segments per plane, record positions and unit
 // counts within int32.
 int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
 
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
-    const int64_t per_plane = int64_t(p->num_queries) * p->num_levels * p->num_points;
-    return per_plane < (int64_t(1) << msda::kRecSampleBits) && pb.nseg <= msda::kMaxSegments &&
+    return p->num_queries < (1 << msda::kQueryBits) && pb.nseg <= msda::kMaxSegments &&
            max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * pb.nseg < kIndexLimit / 2;
 }
 
@@ -145,7 +144,7 @@ bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
 
 struct Layout {
     bool binned;
-    size_t counts, cursor, nunits, units, records, acc, total;
+    size_t counts, cursor, nunits, units, rkey, rw, acc, total;
     int64_t max_units;
 };
 
@@ -167,8 +166,10 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
         off += 256;
         w.units = off;
         off += round_up(w.max_units * 16);
-        w.records = off;
+        w.rkey = off;
         off += round_up(max_records(p) * 4);
+        w.rw = off;
+        off += round_up(max_records(p) * 8);
     }
     w.acc = off;
     if (p->dtype != MSDA_F32) off += round_up(value_elems(p) * 4);
@@ -275,13 +276,13 @@ struct Fwd {
 template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
-                             const void* w, const void* gout, float* gacc, uint32_t* records,
+                             const void* w, const void* gout, float* gacc, uint32_t* rkey, float2* rw,
                              int32_t* cursor, void* gloc, void* gw, hipStream_t st) {
-        const int gpb = tile_queries(pb, LPR, msda::kMaxWgRecords / 4);
+        const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
         size_t lds = sizeof(uint32_t) * gpb * (12 * LP + 4);
-        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg) + 2 * sizeof(uint32_t) * gpb * LP * 4;
+        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg) + sizeof(uint16_t) * gpb * LP * 4;
         const void* k;
         if (binned)
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)
@@ -289,23 +290,22 @@ struct Grad {
         else
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, false>)
                             : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, false>);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, records, cursor, gloc, gw, pb, gpb);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, rkey, rw, cursor, gloc, gw, pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
 struct Accum {
-    static msda_status_t run(const msda::Problem& pb, int64_t max_units, const void* loc, const void* w,
-                             const void* gout, const uint32_t* records, const int32_t* nunits,
+    static msda_status_t run(const msda::Problem& pb, int64_t max_units, const void* gout,
+                             const uint32_t* rkey, const float2* rw, const int32_t* nunits,
                              const int4* units, float* gacc, hipStream_t st) {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
                            (sizeof(uint32_t) + sizeof(uint16_t)) * msda::kUnitRecords +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
-        const void* k = is_l4p4(pb) ? kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR, 4, 4>)
-                                    : kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR, 0, 0>);
-        return launch(k, max_units, kBlock, lds, st, loc, w, gout, records, nunits, units, gacc, pb);
+        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, kBlock, lds, st, gout, rkey,
+                      rw, nunits, units, gacc, pb);
     }
 };
 
@@ -359,15 +359,16 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
-                                      static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr),
-                                      gloc, gw, st));
+                                      static_cast<uint32_t*>(nullptr), static_cast<float2*>(nullptr),
+                                      static_cast<int32_t*>(nullptr), gloc, gw, st));
         return mark(ev, kStageAccum, st);
     }
     int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
     int32_t* nunits = reinterpret_cast<int32_t*>(ws + lay.nunits);
     int4* units = reinterpret_cast<int4*>(ws + lay.units);
-    uint32_t* records = reinterpret_cast<uint32_t*>(ws + lay.records);
+    uint32_t* rkey = reinterpret_cast<uint32_t*>(ws + lay.rkey);
+    float2* rw = reinterpret_cast<float2*>(ws + lay.rw);
 
     MSDA_TRY(mark(ev, kStageZero, st));
     MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
@@ -381,11 +382,11 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), 1, msda::kScanThreads, 0, st,
                     static_cast<const int32_t*>(counts), cursor, nunits, units, gacc, accumulate, pb));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, records, cursor,
+    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, rkey, rw, cursor,
                                   gloc, gw, st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, loc, w, gout,
-                                 static_cast<const uint32_t*>(records), static_cast<const int32_t*>(nunits),
+    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, gout, static_cast<const uint32_t*>(rkey),
+                                 static_cast<const float2*>(rw), static_cast<const int32_t*>(nunits),
                                  static_cast<const int4*>(units), gacc, st);
 }
 

@@ -8,9 +8,13 @@
 // locations, attention weights.
 //
 // grad_attention_weights and grad_sampling_locations are per-sample
-// reductions over the embedding channels (wave shuffles), computed by the
-// gradient kernel, which gathers the four corner rows exactly as the forward
-// does.
+// reductions over the embedding channels, computed by the gradient kernel,
+// which gathers the four corner rows exactly as the forward does.  With
+// d_ij = <g, v_ij> (g the sample's grad_output row, v_ij its corners) the
+// three reductions follow from four dot products:
+//   grad_w   = hy (hx d00 + lx d01) + ly (hx d10 + lx d11)
+//   grad_x   = W w (hy (d01 - d00) + ly (d11 - d10))
+//   grad_y   = H w ((hx d10 + lx d11) - (hx d00 + lx d01))
 //
 // grad_value is a transposed gather: row (b, key, m) sums w * (bilinear
 // weight) * grad_output[b, q, m] over every sample corner that lands on it.
@@ -19,15 +23,16 @@
 // near 340 G float updates/s, far below what the gather side runs at.  So the
 // backward bins instead:
 //
-//   1. count     each (batch, head) plane's keys are cut into segments; every
-//                in-map corner pair of a sample (the two corners of one image
-//                row) becomes a 4-byte record; count records per segment
-//                (LDS histograms, one global add per non-empty bin).
+//   1. count     each (batch, head) plane's keys are cut into segments; the
+//                in-map corners of one image row of a sample's cell make a
+//                record; count records per segment (LDS histograms, one
+//                global add per non-empty bin).
 //   2. scan      exclusive prefix over the counts gives each segment a record
 //                range and a cursor; segments are split into units of at most
 //                kUnitRecords records.
 //   3. gradient  the gather kernel (grad_w, grad_loc) also writes its records
-//                at positions reserved per workgroup and segment.
+//                at positions reserved per workgroup and segment: the query
+//                and key (4 bytes) and the two corner weights (8 bytes).
 //   4. accumulate  one workgroup per unit: counting-sort the unit's records by
 //                key in LDS, let each worker (LPR lanes) walk a key-sorted slice
 //                accumulating rows in registers, merge into an LDS tile, and
@@ -37,7 +42,7 @@
 //
 // Segment sizes per level are planned on the host from the expected records
 // per key, so that most segments fit one unit.  Outside the envelope of the
-// record format (see binned_ok on the host) the gradient kernel scatters
+// record format (binned_ok on the host) the gradient kernel scatters
 // grad_value with float atomics instead.
 #pragma once
 
@@ -47,35 +52,32 @@
 namespace msda {
 
 // ---- records -----------------------------------------------------------------
-// A record is one image row of one sample's bilinear cell:
-//   bits  0..20  sample index within its (batch, head) plane, q*L*P + l*P + p
-//   bit   21     row: 0 = y0, 1 = y0 + 1
-//   bits 22..23  corners: kBoth (key, key+1), kLeftOnly (key = x0 corner),
-//                kRightOnly (key = x0+1 corner)
-//   bits 24..31  key within its segment
-constexpr int kRecSampleBits = 21;
-constexpr uint32_t kRecSampleMask = (1u << kRecSampleBits) - 1u;
+// A record is one image row (y0 or y0 + 1) of one sample's bilinear cell,
+// restricted to the row's in-map corners of one segment:
+//   key   u32: query index << 8 | key of its first corner within the segment
+//   w2    float2: weight of that key's corner and of the next key's corner
+//         (0 when the row's second corner is off the map or in the next
+//         segment), each w * (1-ly or ly) * (1-lx or lx)
+constexpr int kQueryBits = 24;         // queries per plane for the binned path
 constexpr int kMaxSegKeys = 256;       // keys per segment (8-bit key field)
-constexpr int kUnitRecords = 4096;     // records one accumulation unit sorts
+constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
-constexpr int kMaxWgRecords = 4096;    // records one gradient workgroup stages
+constexpr int kMaxWgSamples = 512;     // samples one gradient workgroup holds
 constexpr int kCountChunk = 4096;      // samples one counting workgroup bins
 constexpr int kScanThreads = 1024;
 constexpr int kMultiList = 2048;
 
-enum RecMode : uint32_t { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
-
-__device__ __forceinline__ uint32_t make_record(uint32_t s, uint32_t row, uint32_t mode, uint32_t key) {
-    return s | (row << 21) | (mode << 22) | (key << 24);
-}
+// Corners of one row that a record covers.
+enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
 
 // Enumerate the records of a valid sample whose cell starts at (x0, y0) on
 // a W x H level (-1 <= x0 < W, -1 <= y0 < H): for each of the rows y0,
 // y0 + 1 that lie on the map, the in-map corners of that row.  A pair whose
 // two corners fall in different segments is split in two records.
+// emit(segment, key within segment, row 0/1, mode).
 template <typename Emit>
-__device__ __forceinline__ void for_each_record(uint32_t s, int x0, int y0, int W, int H, int shift,
-                                                int segbase, Emit&& emit) {
+__device__ __forceinline__ void for_each_record(int x0, int y0, int W, int H, int shift, int segbase,
+                                                Emit&& emit) {
     const int mask = (1 << shift) - 1;
     const bool lin = x0 >= 0, rin = x0 + 1 < W;
 #pragma unroll
@@ -86,15 +88,15 @@ __device__ __forceinline__ void for_each_record(uint32_t s, int x0, int y0, int 
         const int kr = kl + 1;         // right corner key
         if (lin && rin) {
             if ((kl >> shift) == (kr >> shift)) {
-                emit(make_record(s, r, kBoth, kl & mask), segbase + (kl >> shift));
+                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kBoth));
             } else {
-                emit(make_record(s, r, kLeftOnly, kl & mask), segbase + (kl >> shift));
-                emit(make_record(s, r, kRightOnly, kr & mask), segbase + (kr >> shift));
+                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
+                emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
             }
         } else if (lin) {
-            emit(make_record(s, r, kLeftOnly, kl & mask), segbase + (kl >> shift));
+            emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
         } else {
-            emit(make_record(s, r, kRightOnly, kr & mask), segbase + (kr >> shift));
+            emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
         }
     }
 }
@@ -180,8 +182,8 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
                           static_cast<float>(W), static_cast<float>(H), x, y))
             continue;
         const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
-        for_each_record(static_cast<uint32_t>(s), x0, y0, W, H, pb.seg_shift[l], pb.seg_base[l],
-                        [&](uint32_t, int seg) { atomicAdd(&hist[seg], 1); });
+        for_each_record(x0, y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+                        [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
     }
     __syncthreads();
     for (int i = threadIdx.x; i < pb.nseg; i += kBlock)
@@ -269,21 +271,22 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 // 3. gradient (gather): grad_w, grad_loc, and grad_value records or atomics
 // ---------------------------------------------------------------------------
 // Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes, plane-local
-// as in the forward.  A prologue (one lane per sample) computes the corner
-// offsets, the bilinear fractions and the gradient scales into LDS (12
-// words per sample) and, when BINNED, emits the sample's records; the main
-// loop gathers the four corner rows per sample and reduces
-//   grad_w   = <g, sample>,   grad_loc = (W*w*<g, d/dx>, H*w*<g, d/dy>)
-// over the group's lanes.
+// as in the forward.  A prologue (one lane per sample) stores each sample's
+// corner offsets, bilinear fractions and gradient scales in LDS (12 words)
+// and ranks its records within their segments; the main loop gathers the
+// four corner rows of each sample, forms the four dot products with the
+// query's grad_output row and reduces them over the group's lanes; when
+// BINNED, an epilogue reserves the workgroup's record ranges and writes the
+// records.
 // LDS: gpb * (12 * L * P + 4) words; when BINNED also nseg histogram and
-// nseg bases (int32) and 4 record slots per sample (2 words each).
+// nseg bases (int32) and 4 record ranks per sample (uint16).
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                      const void* __restrict__ attw, const void* __restrict__ gout,
-                     float* __restrict__ gacc, uint32_t* __restrict__ records,
-                     int32_t* __restrict__ cursor, void* __restrict__ grad_loc,
-                     void* __restrict__ grad_w, Problem pb, int gpb) {
+                     float* __restrict__ gacc, uint32_t* __restrict__ rkey,
+                     float2* __restrict__ rw, int32_t* __restrict__ cursor,
+                     void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr bool kFixedLP = L_CT != 0 && P_CT != 0;
@@ -296,8 +299,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     uint32_t* srec = sm;
     int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);
     int32_t* lbase = lhist + pb.nseg;
-    uint32_t* lrec = reinterpret_cast<uint32_t*>(lbase + pb.nseg);
-    uint32_t* lsr = lrec + gpb * LP * 4;
+    uint16_t* lrank = reinterpret_cast<uint16_t*>(lbase + pb.nseg);
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
@@ -320,17 +322,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         *reinterpret_cast<float4*>(r + 8) = make_float4(static_cast<float>(W) * aw, static_cast<float>(H) * aw,
                                                         aw * c.hy, aw * c.ly);
         if constexpr (BINNED) {
-            int k = 0;
             if (c.ok) {
-                const uint32_t s = static_cast<uint32_t>((t.q0 + g) * LP + lp);
-                for_each_record(s, c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l], [&](uint32_t rec, int seg) {
-                    const int rank = atomicAdd(&lhist[seg], 1);
-                    lrec[4 * i + k] = rec;
-                    lsr[4 * i + k] = (static_cast<uint32_t>(seg) << 16) | static_cast<uint32_t>(rank);
+                int k = 0;
+                for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l], [&](int seg, int, int, int) {
+                    lrank[4 * i + k] = static_cast<uint16_t>(atomicAdd(&lhist[seg], 1));
                     ++k;
                 });
             }
-            for (; k < 4; ++k) lsr[4 * i + k] = 0xffffffffu;
         }
     }
     __syncthreads();
@@ -359,7 +357,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const uint4 o = *reinterpret_cast<const uint4*>(rec + lp * 12);
             const float4 f = *reinterpret_cast<const float4*>(rec + lp * 12 + 4);   // hx lx hy ly
             const float4 sc = *reinterpret_cast<const float4*>(rec + lp * 12 + 8);  // W*w H*w w*hy w*ly
-            float gw = 0.0f, gx = 0.0f, gy = 0.0f;
+            float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
             if (active) {
                 float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
                 widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v00);
@@ -368,11 +366,10 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v11);
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    const float top = f.x * v00[i] + f.y * v01[i];
-                    const float bot = f.x * v10[i] + f.y * v11[i];
-                    gw += g[i] * (f.z * top + f.w * bot);
-                    gx += g[i] * (f.z * (v01[i] - v00[i]) + f.w * (v11[i] - v10[i]));
-                    gy += g[i] * (bot - top);
+                    d00 += g[i] * v00[i];
+                    d01 += g[i] * v01[i];
+                    d10 += g[i] * v10[i];
+                    d11 += g[i] * v11[i];
                 }
                 if constexpr (!BINNED) {
                     if (o.x != kOffMap)
@@ -385,6 +382,11 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                         for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.w / E + i, sc.w * f.y * g[i]);
                 }
             }
+            const float top = f.x * d00 + f.y * d01;
+            const float bot = f.x * d10 + f.y * d11;
+            float gw = f.z * top + f.w * bot;
+            float gx = f.z * (d01 - d00) + f.w * (d11 - d10);
+            float gy = bot - top;
             // a sample off the map (all four corners at kOffMap) gets exactly
             // zero gradients, whatever grad_output holds
             const bool off = ((o.x & o.y & o.z & o.w) & kOffMap) != 0u;
@@ -423,9 +425,27 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x)
             if (lhist[i] != 0) lbase[i] = atomicAdd(&cursor[static_cast<int64_t>(t.pl) * pb.nseg + i], lhist[i]);
         __syncthreads();
-        for (int i = threadIdx.x; i < t.gcount * LP * 4; i += blockDim.x) {
-            const uint32_t sr = lsr[i];
-            if (sr != 0xffffffffu) records[lbase[sr >> 16] + static_cast<int>(sr & 0xffffu)] = lrec[i];
+        // records: recompute each sample's cell (same arithmetic as the
+        // prologue) and write its records at base + rank
+        for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+            const int g = i / LP, lp = i - g * LP, l = lp / P;
+            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+            const int H = pb.lv.H[l], W = pb.lv.W[l];
+            const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), H,
+                                             W, pb.lv.start[l], pitch);
+            if (!c.ok) continue;
+            const float aw = load_scalar<DT>(attw, si);
+            const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
+            int k = 0;
+            for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+                            [&](int seg, int key, int row, int mode) {
+                                const float wy = aw * (row ? c.ly : c.hy);
+                                const float cl = wy * c.hx, cr = wy * c.lx;
+                                const int pos = lbase[seg] + lrank[4 * i + k];
+                                rkey[pos] = qk | static_cast<uint32_t>(key);
+                                rw[pos] = make_float2(mode == kRightOnly ? cr : cl, mode == kBoth ? cr : 0.0f);
+                                ++k;
+                            });
         }
     }
 }
@@ -435,19 +455,15 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // ---------------------------------------------------------------------------
 // Grid: an upper bound on the unit count, kBlock lanes; workgroups past
 // nunits exit.  LDS: the segment tile (keys * D floats), kUnitRecords
-// records (uint32) and their key order (uint16), 2 * kMaxSegKeys int32.
-template <int DT, int VECB, int LPR, int L_CT, int P_CT>
+// record keys (uint32) and their key order (uint16), 2 * kMaxSegKeys int32.
+template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(kBlock)
-msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ attw,
-                       const void* __restrict__ gout, const uint32_t* __restrict__ records,
-                       const int32_t* __restrict__ nunits, const int4* __restrict__ units,
-                       float* __restrict__ gacc, Problem pb) {
+msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict__ rkey,
+                       const float2* __restrict__ rw, const int32_t* __restrict__ nunits,
+                       const int4* __restrict__ units, float* __restrict__ gacc, Problem pb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr int NW = kBlock / LPR;                 // workers
-    const int L = L_CT ? L_CT : pb.L;
-    const int P = P_CT ? P_CT : pb.P;
-    const int LP = L * P;
     if (static_cast<int>(blockIdx.x) >= nunits[0]) return;
 
     const int4 unit = units[blockIdx.x];
@@ -456,15 +472,14 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
     const int lvl = level_of_segment(pb, seg);
     const int shift = pb.seg_shift[lvl];
     const int k0 = (seg - pb.seg_base[lvl]) << shift;
-    const int H = pb.lv.H[lvl], W = pb.lv.W[lvl];
-    const int nk = min(1 << shift, H * W - k0);
+    const int nk = min(1 << shift, pb.lv.H[lvl] * pb.lv.W[lvl] - k0);
     const int n = unit.z - unit.y;
     const int D = pb.D;
 
     extern __shared__ float smem[];
-    float* tile = smem;                                            // nk * D
-    uint32_t* recs = reinterpret_cast<uint32_t*>(smem + (1 << shift) * D);
-    int32_t* hist = reinterpret_cast<int32_t*>(recs + kUnitRecords);
+    float* tile = smem;                                                  // nk * D
+    uint32_t* keys = reinterpret_cast<uint32_t*>(smem + (1 << shift) * D);
+    int32_t* hist = reinterpret_cast<int32_t*>(keys + kUnitRecords);
     int32_t* cur = hist + kMaxSegKeys;
     uint16_t* order = reinterpret_cast<uint16_t*>(cur + kMaxSegKeys);
 
@@ -472,9 +487,9 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
     for (int i = threadIdx.x; i < kMaxSegKeys; i += kBlock) hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += kBlock) {
-        const uint32_t r = records[unit.y + i];
-        recs[i] = r;
-        atomicAdd(&hist[r >> 24], 1);
+        const uint32_t r = rkey[unit.y + i];
+        keys[i] = r;
+        atomicAdd(&hist[r & 0xffu], 1);
     }
     __syncthreads();
     if (threadIdx.x < 64) {                          // exclusive scan of 256 bins, one wave
@@ -494,31 +509,30 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
     }
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += kBlock)
-        order[atomicAdd(&cur[recs[i] >> 24], 1)] = static_cast<uint16_t>(i);
+        order[atomicAdd(&cur[keys[i] & 0xffu], 1)] = static_cast<uint16_t>(i);
     __syncthreads();
 
     // Workers (LPR lanes each) walk key-sorted slices, accumulating a row in
     // registers while the key holds.  Rows kf..kf+1 and kl..kl+1 of a slice
     // may also receive contributions from neighbouring workers and are merged
     // with LDS adds; every other row is this worker's alone.  Records are
-    // taken kBatch at a time: lanes decode one record each (coordinates,
-    // corner weights, grad_output offset), the worker's lanes then load the
-    // kBatch grad_output rows together and fold them in key order.
+    // taken kBatch at a time: the worker loads their weights and grad_output
+    // rows together, then folds them in key order.
     constexpr int kBatch = 8;
-    constexpr int kPer = kBatch > LPR ? kBatch / LPR : 1;     // records a lane decodes
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
     const int r1 = static_cast<int>(static_cast<int64_t>(n) * (w + 1) / NW);
     if (r0 < r1) {
-        const int kf = static_cast<int>(recs[order[r0]] >> 24), kl = static_cast<int>(recs[order[r1 - 1]] >> 24);
-        const float Hf = static_cast<float>(H), Wf = static_cast<float>(W);
+        const int kf = static_cast<int>(keys[order[r0]] & 0xffu);
+        const int kl = static_cast<int>(keys[order[r1 - 1]] & 0xffu);
         const int64_t gplane = static_cast<int64_t>(b) * pb.Q * pb.M + m;      // group (b, 0, m)
         const __amdgpu_buffer_rsrc_t gr = make_rsrc(
             static_cast<const char*>(gout) + gplane * D * E,
             static_cast<uint32_t>((static_cast<int64_t>(pb.Q) * pb.M - m) * D * E));
         const uint32_t qstride = static_cast<uint32_t>(pb.M * D * E);
         const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
+        const float2* wbase = rw + unit.y;
         auto flush = [&](int row, const float* acc) {
             if (!active || row >= nk) return;
             float* dst = tile + row * D + li * VEC;
@@ -535,58 +549,31 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
         for (int i = 0; i < VEC; ++i) accA[i] = accB[i] = 0.0f;
         int key = -1;
         for (int base = r0; base < r1; base += kBatch) {
-            int dkey[kPer];
-            float dca[kPer], dcb[kPer];
-            uint32_t dgo[kPer];
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int j = li + k * LPR;
-                dkey[k] = -1;
-                dca[k] = dcb[k] = 0.0f;
-                dgo[k] = 0u;
-                if (j < kBatch && base + j < r1) {
-                    const uint32_t rec = recs[order[base + j]];
-                    const int s = static_cast<int>(rec & kRecSampleMask);
-                    const int q = s / LP, lp = s - q * LP;
-                    const int64_t si = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
-                    float x, y;
-                    pixel_coords(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), Wf, Hf, x, y);
-                    const float fx = floorf(x), fy = floorf(y);
-                    const float lx = x - fx, ly = y - fy;
-                    const float aw = load_scalar<DT>(attw, si);
-                    const float wy = aw * (((rec >> 21) & 1u) ? ly : 1.0f - ly);
-                    const float cl = wy * (1.0f - lx), cr = wy * lx;
-                    const uint32_t mode = (rec >> 22) & 3u;
-                    dkey[k] = static_cast<int>(rec >> 24);
-                    dca[k] = mode == kRightOnly ? cr : cl;
-                    dcb[k] = mode == kBoth ? cr : 0.0f;
-                    dgo[k] = static_cast<uint32_t>(q) * qstride;
-                }
-            }
             int bkey[kBatch];
-            float bca[kBatch], bcb[kBatch], gv[kBatch][VEC];
+            float2 bw[kBatch];
+            float gv[kBatch][VEC];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const int src = j % LPR, k = j / LPR < kPer ? j / LPR : 0;
-                bkey[j] = __shfl(dkey[k], src, LPR);
-                bca[j] = __shfl(dca[k], src, LPR);
-                bcb[j] = __shfl(dcb[k], src, LPR);
-                const uint32_t go = static_cast<uint32_t>(__shfl(static_cast<int>(dgo[k]), src, LPR));
-                if (active && bkey[j] >= 0) {
-                    widen<DT, VECB>(buffer_load<VECB>(gr, go + lane_b), gv[j]);
-                } else {
+                bkey[j] = -1;
+                bw[j] = make_float2(0.0f, 0.0f);
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) gv[j][i] = 0.0f;
+                for (int i = 0; i < VEC; ++i) gv[j][i] = 0.0f;
+                if (base + j < r1) {
+                    const int idx = order[base + j];
+                    const uint32_t r = keys[idx];
+                    bkey[j] = static_cast<int>(r & 0xffu);
+                    bw[j] = wbase[idx];
+                    if (active) widen<DT, VECB>(buffer_load<VECB>(gr, (r >> 8) * qstride + lane_b), gv[j]);
                 }
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const int rkey = bkey[j];
-                if (rkey < 0) break;
-                if (rkey != key) {
+                const int rk = bkey[j];
+                if (rk < 0) break;
+                if (rk != key) {
                     if (key >= 0) {
                         flush(key, accA);
-                        if (rkey == key + 1) {
+                        if (rk == key + 1) {
 #pragma unroll
                             for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
                         } else {
@@ -597,12 +584,12 @@ msda_accumulate_kernel(const void* __restrict__ loc, const void* __restrict__ at
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
                     }
-                    key = rkey;
+                    key = rk;
                 }
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    accA[i] += bca[j] * gv[j][i];
-                    accB[i] += bcb[j] * gv[j][i];
+                    accA[i] += bw[j].x * gv[j][i];
+                    accB[i] += bw[j].y * gv[j][i];
                 }
             }
         }
