@@ -338,7 +338,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const bool active = li < pb.lpr_active;
         const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
         const __amdgpu_buffer_rsrc_t vr = value_plane<E>(value, pb, t.b, t.m);
-        const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
+        // lanes past the row read zeros through an off-map offset
+        const uint32_t lane_b = active ? static_cast<uint32_t>(li * VECB) : kOffMap;
         const uint32_t* rec = srec + lg * gstride;
         float* gb = gacc + (static_cast<int64_t>(t.b) * pb.K * pb.M + t.m) * pb.D + li * VEC;
 
@@ -350,61 +351,73 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
         }
         constexpr int kOwn = kFixedLP ? (L_CT * P_CT + LPR - 1) / LPR : 1;
+        constexpr int kSB = kFixedLP && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
         float own_w[kOwn], own_x[kOwn], own_y[kOwn];
 
 #pragma unroll
-        for (int lp = 0; lp < LP; ++lp) {
-            const uint4 o = *reinterpret_cast<const uint4*>(rec + lp * 12);
-            const float4 f = *reinterpret_cast<const float4*>(rec + lp * 12 + 4);   // hx lx hy ly
-            const float4 sc = *reinterpret_cast<const float4*>(rec + lp * 12 + 8);  // W*w H*w w*hy w*ly
-            float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
-            if (active) {
-                float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-                widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v00);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v01);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v10);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v11);
+        for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
+            uint4 o[kSB];
+            float4 f[kSB], sc[kSB];
+            float v[kSB][4][VEC];
+#pragma unroll
+            for (int u = 0; u < kSB; ++u) {
+                const uint32_t* r = rec + (lp0 + u) * 12;
+                o[u] = *reinterpret_cast<const uint4*>(r);
+                f[u] = *reinterpret_cast<const float4*>(r + 4);    // hx lx hy ly
+                sc[u] = *reinterpret_cast<const float4*>(r + 8);   // W*w H*w w*hy w*ly
+                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].x + lane_b), v[u][0]);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].y + lane_b), v[u][1]);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].z + lane_b), v[u][2]);
+                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].w + lane_b), v[u][3]);
+            }
+#pragma unroll
+            for (int u = 0; u < kSB; ++u) {
+                const int lp = lp0 + u;
+                float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    d00 += g[i] * v00[i];
-                    d01 += g[i] * v01[i];
-                    d10 += g[i] * v10[i];
-                    d11 += g[i] * v11[i];
+                    d00 += g[i] * v[u][0][i];
+                    d01 += g[i] * v[u][1][i];
+                    d10 += g[i] * v[u][2][i];
+                    d11 += g[i] * v[u][3][i];
                 }
                 if constexpr (!BINNED) {
-                    if (o.x != kOffMap)
-                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.x / E + i, sc.z * f.x * g[i]);
-                    if (o.y != kOffMap)
-                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.y / E + i, sc.z * f.y * g[i]);
-                    if (o.z != kOffMap)
-                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.z / E + i, sc.w * f.x * g[i]);
-                    if (o.w != kOffMap)
-                        for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o.w / E + i, sc.w * f.y * g[i]);
+                    if (active) {
+                        const float4 ff = f[u], ss = sc[u];
+                        if (o[u].x != kOffMap)
+                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, ss.z * ff.x * g[i]);
+                        if (o[u].y != kOffMap)
+                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, ss.z * ff.y * g[i]);
+                        if (o[u].z != kOffMap)
+                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, ss.w * ff.x * g[i]);
+                        if (o[u].w != kOffMap)
+                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, ss.w * ff.y * g[i]);
+                    }
                 }
-            }
-            const float top = f.x * d00 + f.y * d01;
-            const float bot = f.x * d10 + f.y * d11;
-            float gw = f.z * top + f.w * bot;
-            float gx = f.z * (d01 - d00) + f.w * (d11 - d10);
-            float gy = bot - top;
-            // a sample off the map (all four corners at kOffMap) gets exactly
-            // zero gradients, whatever grad_output holds
-            const bool off = ((o.x & o.y & o.z & o.w) & kOffMap) != 0u;
-            gw = off ? 0.0f : group_sum<LPR>(gw);
-            gx = off ? 0.0f : group_sum<LPR>(gx) * sc.x;
-            gy = off ? 0.0f : group_sum<LPR>(gy) * sc.y;
-            if constexpr (kFixedLP) {
-                // lane lp % LPR keeps this sample's results and writes them below
-                if (li == lp % LPR) {
-                    own_w[lp / LPR] = gw;
-                    own_x[lp / LPR] = gx;
-                    own_y[lp / LPR] = gy;
+                const float top = f[u].x * d00 + f[u].y * d01;
+                const float bot = f[u].x * d10 + f[u].y * d11;
+                const float sw = group_sum<LPR>(f[u].z * top + f[u].w * bot);
+                const float sx = group_sum<LPR>(f[u].z * (d01 - d00) + f[u].w * (d11 - d10));
+                const float sy = group_sum<LPR>(bot - top);
+                // a sample off the map (all four corners at kOffMap) gets exactly
+                // zero gradients, whatever grad_output holds
+                const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
+                const float gw = off ? 0.0f : sw;
+                const float gx = off ? 0.0f : sx * sc[u].x;
+                const float gy = off ? 0.0f : sy * sc[u].y;
+                if constexpr (kFixedLP) {
+                    // lane lp % LPR keeps this sample's results and writes them below
+                    if (li == lp % LPR) {
+                        own_w[lp / LPR] = gw;
+                        own_x[lp / LPR] = gx;
+                        own_y[lp / LPR] = gy;
+                    }
+                } else if (li == 0) {
+                    const int64_t s = G * LP + lp;
+                    store_scalar<DT>(grad_w, s, gw);
+                    store_scalar<DT>(grad_loc, 2 * s, gx);
+                    store_scalar<DT>(grad_loc, 2 * s + 1, gy);
                 }
-            } else if (li == 0) {
-                const int64_t s = G * LP + lp;
-                store_scalar<DT>(grad_w, s, gw);
-                store_scalar<DT>(grad_loc, 2 * s, gx);
-                store_scalar<DT>(grad_loc, 2 * s + 1, gy);
             }
         }
         if constexpr (kFixedLP) {

@@ -253,11 +253,28 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t block, int64_t nblocks) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
-// Sum over the LPR lanes of a group (LPR a power of two, groups aligned).
+// Value of lane (pattern applied to this lane) through a DPP move: row_mirror
+// (0x140) pairs lanes i and 15-i of a 16-lane row, row_half_mirror (0x141)
+// lanes i and 7-i of an 8-lane half row, quad_perm 0x4E / 0xB1 lanes i^2 /
+// i^1 of a quad.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPR lanes of a group (LPR a power of two, groups aligned):
+// cross-row steps by lane permute, the rest by DPP within a row.  Every lane
+// of the group ends with the total.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (LPR >= 16) v += dpp<0x140>(v);
+    if constexpr (LPR >= 8) v += dpp<0x141>(v);
+    if constexpr (LPR >= 4) {
+        v += dpp<0x4E>(v);
+        v += dpp<0xB1>(v);
+    }
     return v;
 }
 

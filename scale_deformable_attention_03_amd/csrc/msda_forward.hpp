@@ -130,17 +130,25 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+    constexpr int kSB = L_CT && P_CT && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
 #pragma unroll
-    for (int lp = 0; lp < LP; ++lp) {
-        const uint4 o = *reinterpret_cast<const uint4*>(rec + lp * 8);
-        const float4 w = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);
-        float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-        widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v00);
-        widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v01);
-        widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v10);
-        widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v11);
+    for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
+        float4 w[kSB];
+        float v[kSB][4][VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += w.x * v00[i] + w.y * v01[i] + w.z * v10[i] + w.w * v11[i];
+        for (int u = 0; u < kSB; ++u) {
+            const uint4 o = *reinterpret_cast<const uint4*>(rec + (lp0 + u) * 8);
+            w[u] = *reinterpret_cast<const float4*>(rec + (lp0 + u) * 8 + 4);
+            widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v[u][0]);
+            widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v[u][1]);
+            widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v[u][2]);
+            widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v[u][3]);
+        }
+#pragma unroll
+        for (int u = 0; u < kSB; ++u)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                acc[i] += w[u].x * v[u][0][i] + w[u].y * v[u][1][i] + w[u].z * v[u][2][i] + w[u].w * v[u][3][i];
     }
     const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
     store_raw<VECB>(static_cast<char*>(out) + (G * pb.D + li * VEC) * E, narrow<DT, VECB>(acc));
