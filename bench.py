@@ -139,6 +139,9 @@ def main() -> int:
                              "tiny_single_level"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device-to-device copy of 512 MiB, 4 times (the reference "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,6 +161,15 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.calibrate_copy:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)     # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "copies": 4}), flush=True)
+        return 0
 
     wl = W.NAMED[args.workload]()
     bs, K, M, D = wl.value.shape
