@@ -173,17 +173,32 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
     for (int i = threadIdx.x; i < pb.nseg; i += kBlock) hist[i] = 0;
     __syncthreads();
     const int s_end = min((chunk + 1) * kCountChunk, nsamp);
-    for (int s = chunk * kCountChunk + threadIdx.x; s < s_end; s += kBlock) {
-        const int q = s / LP, lp = s - q * LP, l = lp / P;
-        const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
-        const int H = pb.lv.H[l], W = pb.lv.W[l];
-        float x, y;
-        if (!pixel_coords(load_scalar<DT>(loc, 2 * i), load_scalar<DT>(loc, 2 * i + 1),
-                          static_cast<float>(W), static_cast<float>(H), x, y))
-            continue;
-        const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
-        for_each_record(x0, y0, W, H, pb.seg_shift[l], pb.seg_base[l],
-                        [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
+    constexpr int kU = 4;                            // samples whose loads fly together
+    for (int s0 = chunk * kCountChunk + threadIdx.x; s0 < s_end; s0 += kU * kBlock) {
+        float lx[kU], ly[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int s = s0 + u * kBlock;
+            lx[u] = ly[u] = -2.0f;                       // off the map
+            if (s < s_end) {
+                const int q = s / LP, lp = s - q * LP;
+                const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
+                lx[u] = load_scalar<DT>(loc, 2 * i);
+                ly[u] = load_scalar<DT>(loc, 2 * i + 1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int s = s0 + u * kBlock;
+            if (s >= s_end) break;
+            const int lp = s % LP, l = lp / P;
+            const int H = pb.lv.H[l], W = pb.lv.W[l];
+            float x, y;
+            if (!pixel_coords(lx[u], ly[u], static_cast<float>(W), static_cast<float>(H), x, y)) continue;
+            const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
+            for_each_record(x0, y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+                            [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < pb.nseg; i += kBlock)
@@ -216,52 +231,71 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
 // {segment, first record, end record, flush-with-atomics} and its length,
 // and zeroed rows for segments split over several units.  With `accumulate`
 // every unit adds into the caller's buffer, which is then left as it is.
+// The counts are walked in chunks of kScanChunk entries, each loaded into
+// LDS with coalesced reads; every lane scans kScanChunk / kScanThreads
+// consecutive entries.
+constexpr int kScanChunk = 8192;
+
 __global__ void __launch_bounds__(kScanThreads)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, int4* __restrict__ units, float* __restrict__ gacc,
                      int accumulate, Problem pb) {
+    constexpr int kPer = kScanChunk / kScanThreads;
+    __shared__ int32_t s_cnt[kScanChunk];
     __shared__ int32_t s_rec[kScanThreads], s_unit[kScanThreads];
     __shared__ int32_t s_multi[kMultiList];
     __shared__ int32_t s_nmulti;
     const int t = threadIdx.x;
     const int n = pb.nplanes * pb.nseg;
-    const int per = (n + kScanThreads - 1) / kScanThreads;
-    const int i0 = min(n, t * per), i1 = min(n, i0 + per);
-    int rsum = 0, usum = 0;
-    for (int i = i0; i < i1; ++i) {
-        const int c = counts[i];
-        rsum += c;
-        usum += units_of(c);
-    }
-    s_rec[t] = rsum;
-    s_unit[t] = usum;
     if (t == 0) s_nmulti = 0;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {     // inclusive scan
-        const int a = t >= off ? s_rec[t - off] : 0;
-        const int u = t >= off ? s_unit[t - off] : 0;
+    int run_rec = 0, run_unit = 0;
+    for (int c0 = 0; c0 < n; c0 += kScanChunk) {
+        const int cn = min(kScanChunk, n - c0);
+        for (int i = t; i < cn; i += kScanThreads) s_cnt[i] = counts[c0 + i];
         __syncthreads();
-        s_rec[t] += a;
-        s_unit[t] += u;
-        __syncthreads();
-    }
-    int rbase = s_rec[t] - rsum, ubase = s_unit[t] - usum;
-    if (t == kScanThreads - 1) nunits[0] = s_unit[t];
-    for (int i = i0; i < i1; ++i) {
-        const int c = counts[i], u = units_of(c);
-        cursor[i] = rbase;
-        const int atomic_flush = (u > 1 || accumulate) ? 1 : 0;
-        for (int j = 0; j < u; ++j)
-            units[ubase + j] = make_int4(i, rbase + j * kUnitRecords, rbase + min(c, (j + 1) * kUnitRecords),
-                                         atomic_flush);
-        if (u > 1 && !accumulate) {
-            const int k = atomicAdd(&s_nmulti, 1);
-            if (k < kMultiList) s_multi[k] = i;
-            else zero_segment(pb, gacc, i, 0, 1);
+        int rsum = 0, usum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = t * kPer + j;
+            if (i < cn) {
+                rsum += s_cnt[i];
+                usum += units_of(s_cnt[i]);
+            }
         }
-        rbase += c;
-        ubase += u;
+        s_rec[t] = rsum;
+        s_unit[t] = usum;
+        __syncthreads();
+        for (int off = 1; off < kScanThreads; off <<= 1) {     // inclusive scan
+            const int a = t >= off ? s_rec[t - off] : 0;
+            const int u = t >= off ? s_unit[t - off] : 0;
+            __syncthreads();
+            s_rec[t] += a;
+            s_unit[t] += u;
+            __syncthreads();
+        }
+        int rbase = run_rec + s_rec[t] - rsum, ubase = run_unit + s_unit[t] - usum;
+        for (int j = 0; j < kPer; ++j) {
+            const int i = t * kPer + j;
+            if (i >= cn) break;
+            const int c = s_cnt[i], u = units_of(c), gi = c0 + i;
+            cursor[gi] = rbase;
+            const int atomic_flush = (u > 1 || accumulate) ? 1 : 0;
+            for (int k = 0; k < u; ++k)
+                units[ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
+                                             rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
+            if (u > 1 && !accumulate) {
+                const int k = atomicAdd(&s_nmulti, 1);
+                if (k < kMultiList) s_multi[k] = gi;
+                else zero_segment(pb, gacc, gi, 0, 1);
+            }
+            rbase += c;
+            ubase += u;
+        }
+        run_rec += s_rec[kScanThreads - 1];
+        run_unit += s_unit[kScanThreads - 1];
+        __syncthreads();
     }
+    if (t == 0) nunits[0] = run_unit;
     __syncthreads();
     const int nm = min(s_nmulti, kMultiList);
     for (int k = 0; k < nm; ++k) zero_segment(pb, gacc, s_multi[k], t, kScanThreads);
@@ -477,9 +511,11 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr int NW = kBlock / LPR;                 // workers
-    if (static_cast<int>(blockIdx.x) >= nunits[0]) return;
-
-    const int4 unit = units[blockIdx.x];
+    const int nu = nunits[0];
+    if (static_cast<int>(blockIdx.x) >= nu) return;
+    // consecutive units (neighbouring segments of one plane) run on one XCD,
+    // so the plane's grad_output rows they gather stay in that XCD's L2
+    const int4 unit = units[xcd_tile(blockIdx.x, nu)];
     const int pl = unit.x / pb.nseg, seg = unit.x - pl * pb.nseg;
     const int b = pl / pb.M, m = pl - b * pb.M;
     const int lvl = level_of_segment(pb, seg);
@@ -531,7 +567,7 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
     // with LDS adds; every other row is this worker's alone.  Records are
     // taken kBatch at a time: the worker loads their weights and grad_output
     // rows together, then folds them in key order.
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
