@@ -384,86 +384,77 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 #pragma unroll
             for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
         }
-        constexpr int kOwn = kFixedLP ? (L_CT * P_CT + LPR - 1) / LPR : 1;
-        constexpr int kSB = kFixedLP && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
-        float own_w[kOwn], own_x[kOwn], own_y[kOwn];
-
+        // Samples go in chunks of kC (LPR, or all of them when fewer): lane li
+        // of the group keeps the results of the chunk's sample li and stores
+        // them after the chunk, so a group's stores are contiguous.  Within a
+        // chunk, kSB samples' corner loads are in flight together.
+        constexpr int kC = kFixedLP ? (LPR < L_CT * P_CT ? LPR : L_CT * P_CT) : 1;
+        constexpr int kSB = kC % 4 == 0 ? 4 : 1;
+#pragma unroll 1
+        for (int c0 = 0; c0 < LP; c0 += kC) {
+            float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f;
 #pragma unroll
-        for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
-            uint4 o[kSB];
-            float4 f[kSB], sc[kSB];
-            float v[kSB][4][VEC];
+            for (int b0 = 0; b0 < kC; b0 += kSB) {
+                uint4 o[kSB];
+                Raw<VECB> raw[kSB][4];
 #pragma unroll
-            for (int u = 0; u < kSB; ++u) {
-                const uint32_t* r = rec + (lp0 + u) * 12;
-                o[u] = *reinterpret_cast<const uint4*>(r);
-                f[u] = *reinterpret_cast<const float4*>(r + 4);    // hx lx hy ly
-                sc[u] = *reinterpret_cast<const float4*>(r + 8);   // W*w H*w w*hy w*ly
-                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].x + lane_b), v[u][0]);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].y + lane_b), v[u][1]);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].z + lane_b), v[u][2]);
-                widen<DT, VECB>(buffer_load<VECB>(vr, o[u].w + lane_b), v[u][3]);
-            }
-#pragma unroll
-            for (int u = 0; u < kSB; ++u) {
-                const int lp = lp0 + u;
-                float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    d00 += g[i] * v[u][0][i];
-                    d01 += g[i] * v[u][1][i];
-                    d10 += g[i] * v[u][2][i];
-                    d11 += g[i] * v[u][3][i];
+                for (int u = 0; u < kSB; ++u) {
+                    o[u] = *reinterpret_cast<const uint4*>(rec + (c0 + b0 + u) * 12);
+                    raw[u][0] = buffer_load<VECB>(vr, o[u].x + lane_b);
+                    raw[u][1] = buffer_load<VECB>(vr, o[u].y + lane_b);
+                    raw[u][2] = buffer_load<VECB>(vr, o[u].z + lane_b);
+                    raw[u][3] = buffer_load<VECB>(vr, o[u].w + lane_b);
                 }
-                if constexpr (!BINNED) {
-                    if (active) {
-                        const float4 ff = f[u], ss = sc[u];
-                        if (o[u].x != kOffMap)
-                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, ss.z * ff.x * g[i]);
-                        if (o[u].y != kOffMap)
-                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, ss.z * ff.y * g[i]);
-                        if (o[u].z != kOffMap)
-                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, ss.w * ff.x * g[i]);
-                        if (o[u].w != kOffMap)
-                            for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, ss.w * ff.y * g[i]);
+#pragma unroll
+                for (int u = 0; u < kSB; ++u) {
+                    const int lp = c0 + b0 + u;
+                    const float4 f = *reinterpret_cast<const float4*>(rec + lp * 12 + 4);    // hx lx hy ly
+                    const float4 sc = *reinterpret_cast<const float4*>(rec + lp * 12 + 8);   // W*w H*w w*hy w*ly
+                    float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+                    widen<DT, VECB>(raw[u][0], v00);
+                    widen<DT, VECB>(raw[u][1], v01);
+                    widen<DT, VECB>(raw[u][2], v10);
+                    widen<DT, VECB>(raw[u][3], v11);
+                    float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) {
+                        d00 += g[i] * v00[i];
+                        d01 += g[i] * v01[i];
+                        d10 += g[i] * v10[i];
+                        d11 += g[i] * v11[i];
+                    }
+                    if constexpr (!BINNED) {
+                        if (active) {
+                            if (o[u].x != kOffMap)
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, sc.z * f.x * g[i]);
+                            if (o[u].y != kOffMap)
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, sc.z * f.y * g[i]);
+                            if (o[u].z != kOffMap)
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, sc.w * f.x * g[i]);
+                            if (o[u].w != kOffMap)
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, sc.w * f.y * g[i]);
+                        }
+                    }
+                    const float top = f.x * d00 + f.y * d01;
+                    const float bot = f.x * d10 + f.y * d11;
+                    const float sw = group_sum<LPR>(f.z * top + f.w * bot);
+                    const float sx = group_sum<LPR>(f.z * (d01 - d00) + f.w * (d11 - d10));
+                    const float sy = group_sum<LPR>(bot - top);
+                    // a sample off the map (all four corners at kOffMap) gets exactly
+                    // zero gradients, whatever grad_output holds
+                    const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
+                    if (li == b0 + u) {
+                        own_w = off ? 0.0f : sw;
+                        own_x = off ? 0.0f : sx * sc.x;
+                        own_y = off ? 0.0f : sy * sc.y;
                     }
                 }
-                const float top = f[u].x * d00 + f[u].y * d01;
-                const float bot = f[u].x * d10 + f[u].y * d11;
-                const float sw = group_sum<LPR>(f[u].z * top + f[u].w * bot);
-                const float sx = group_sum<LPR>(f[u].z * (d01 - d00) + f[u].w * (d11 - d10));
-                const float sy = group_sum<LPR>(bot - top);
-                // a sample off the map (all four corners at kOffMap) gets exactly
-                // zero gradients, whatever grad_output holds
-                const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
-                const float gw = off ? 0.0f : sw;
-                const float gx = off ? 0.0f : sx * sc[u].x;
-                const float gy = off ? 0.0f : sy * sc[u].y;
-                if constexpr (kFixedLP) {
-                    // lane lp % LPR keeps this sample's results and writes them below
-                    if (li == lp % LPR) {
-                        own_w[lp / LPR] = gw;
-                        own_x[lp / LPR] = gx;
-                        own_y[lp / LPR] = gy;
-                    }
-                } else if (li == 0) {
-                    const int64_t s = G * LP + lp;
-                    store_scalar<DT>(grad_w, s, gw);
-                    store_scalar<DT>(grad_loc, 2 * s, gx);
-                    store_scalar<DT>(grad_loc, 2 * s + 1, gy);
-                }
             }
-        }
-        if constexpr (kFixedLP) {
-#pragma unroll
-            for (int k = 0; k < kOwn; ++k) {
-                const int lp = li + k * LPR;
-                if (lp < L_CT * P_CT) {
-                    const int64_t s = G * (L_CT * P_CT) + lp;
-                    store_scalar<DT>(grad_w, s, own_w[k]);
-                    store_scalar<DT>(grad_loc, 2 * s, own_x[k]);
-                    store_scalar<DT>(grad_loc, 2 * s + 1, own_y[k]);
-                }
+            if (li < kC) {
+                const int64_t s = G * LP + c0 + li;
+                store_scalar<DT>(grad_w, s, own_w);
+                store_scalar<DT>(grad_loc, 2 * s, own_x);
+                store_scalar<DT>(grad_loc, 2 * s + 1, own_y);
             }
         }
     }
@@ -600,45 +591,50 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
         for (int base = r0; base < r1; base += kBatch) {
             int bkey[kBatch];
             float2 bw[kBatch];
-            float gv[kBatch][VEC];
+            Raw<VECB> graw[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 bkey[j] = -1;
                 bw[j] = make_float2(0.0f, 0.0f);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) gv[j][i] = 0.0f;
                 if (base + j < r1) {
                     const int idx = order[base + j];
                     const uint32_t r = keys[idx];
                     bkey[j] = static_cast<int>(r & 0xffu);
                     bw[j] = wbase[idx];
-                    if (active) widen<DT, VECB>(buffer_load<VECB>(gr, (r >> 8) * qstride + lane_b), gv[j]);
+                    // lanes past the row read zeros through an off-map offset
+                    graw[j] = buffer_load<VECB>(gr, active ? (r >> 8) * qstride + lane_b : kOffMap);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VECB / 4; ++i) graw[j].w[i] = 0u;
                 }
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const int rk = bkey[j];
-                if (rk < 0) break;
-                if (rk != key) {
-                    if (key >= 0) {
-                        flush(key, accA);
-                        if (rk == key + 1) {
+                if (rk >= 0) {                               // records past the slice are -1
+                    if (rk != key) {
+                        if (key >= 0) {
+                            flush(key, accA);
+                            if (rk == key + 1) {
 #pragma unroll
-                            for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
-                        } else {
-                            flush(key + 1, accB);
+                                for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
+                            } else {
+                                flush(key + 1, accB);
 #pragma unroll
-                            for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
+                                for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
+                            }
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
                         }
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
+                        key = rk;
                     }
-                    key = rk;
-                }
+                    float gv[VEC];
+                    widen<DT, VECB>(graw[j], gv);
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    accA[i] += bw[j].x * gv[j][i];
-                    accB[i] += bw[j].y * gv[j][i];
+                    for (int i = 0; i < VEC; ++i) {
+                        accA[i] += bw[j].x * gv[i];
+                        accB[i] += bw[j].y * gv[i];
+                    }
                 }
             }
         }

@@ -131,24 +131,29 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
     constexpr int kSB = L_CT && P_CT && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
-#pragma unroll
+#pragma unroll 2
     for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
         float4 w[kSB];
-        float v[kSB][4][VEC];
+        Raw<VECB> raw[kSB][4];
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
             const uint4 o = *reinterpret_cast<const uint4*>(rec + (lp0 + u) * 8);
             w[u] = *reinterpret_cast<const float4*>(rec + (lp0 + u) * 8 + 4);
-            widen<DT, VECB>(buffer_load<VECB>(vr, o.x + lane_b), v[u][0]);
-            widen<DT, VECB>(buffer_load<VECB>(vr, o.y + lane_b), v[u][1]);
-            widen<DT, VECB>(buffer_load<VECB>(vr, o.z + lane_b), v[u][2]);
-            widen<DT, VECB>(buffer_load<VECB>(vr, o.w + lane_b), v[u][3]);
+            raw[u][0] = buffer_load<VECB>(vr, o.x + lane_b);
+            raw[u][1] = buffer_load<VECB>(vr, o.y + lane_b);
+            raw[u][2] = buffer_load<VECB>(vr, o.z + lane_b);
+            raw[u][3] = buffer_load<VECB>(vr, o.w + lane_b);
         }
 #pragma unroll
-        for (int u = 0; u < kSB; ++u)
+        for (int u = 0; u < kSB; ++u) {
+            float v0[VEC], v1[VEC], v2[VEC], v3[VEC];
+            widen<DT, VECB>(raw[u][0], v0);
+            widen<DT, VECB>(raw[u][1], v1);
+            widen<DT, VECB>(raw[u][2], v2);
+            widen<DT, VECB>(raw[u][3], v3);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i)
-                acc[i] += w[u].x * v[u][0][i] + w[u].y * v[u][1][i] + w[u].z * v[u][2][i] + w[u].w * v[u][3][i];
+            for (int i = 0; i < VEC; ++i) acc[i] += w[u].x * v0[i] + w[u].y * v1[i] + w[u].z * v2[i] + w[u].w * v3[i];
+        }
     }
     const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
     store_raw<VECB>(static_cast<char*>(out) + (G * pb.D + li * VEC) * E, narrow<DT, VECB>(acc));
