@@ -96,7 +96,10 @@ int floor_log2(int64_t v) {
 // binned backward: level l gets segments of 2^shift keys, sized so that a
 // segment receives about kUnitRecords / 2 records when the samples spread
 // evenly over the level (two records per sample and level, Q*P samples per
-// level and plane).  A tile of 2^shift keys * D floats stays within 32 KB.
+// level and plane), but never fewer than 32 keys: a denser level spreads a
+// segment over several units (merged with atomics) rather than letting
+// many workers of one unit fold into the same few rows.  A tile of
+// 2^shift keys * D floats stays within 32 KB.
 msda::Problem pack(const msda_problem_t* p) {
     msda::Problem pb;
     memset(&pb, 0, sizeof(pb));
@@ -120,6 +123,7 @@ msda::Problem pack(const msda_problem_t* p) {
         const double per_key = 2.0 * double(p->num_queries) * p->num_points / double(H * W);
         const double keys = per_key > 0 ? (msda::kUnitRecords / 2) / per_key : double(msda::kMaxSegKeys);
         int shift = keys >= 1.0 ? floor_log2(static_cast<int64_t>(keys)) : 0;
+        if (shift < 5) shift = 5;
         if (shift > max_shift) shift = max_shift;
         pb.seg_shift[l] = shift;
         pb.seg_base[l] = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
@@ -144,7 +148,7 @@ bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
 
 struct Layout {
     bool binned;
-    size_t counts, cursor, nunits, units, rkey, rw, acc, total;
+    size_t counts, cursor, nunits, multi, units, rkey, rw, acc, total;
     int64_t max_units;
 };
 
@@ -162,8 +166,10 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
         off += round_up(nbins * 4);
         w.cursor = off;
         off += round_up(nbins * 4);
-        w.nunits = off;
+        w.nunits = off;          // [0] unit count, [1] count of multi-unit segments
         off += 256;
+        w.multi = off;
+        off += round_up(nbins * 4);
         w.units = off;
         off += round_up(w.max_units * 16);
         w.rkey = off;
@@ -277,7 +283,8 @@ template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
                              const void* w, const void* gout, float* gacc, uint32_t* rkey, float2* rw,
-                             int32_t* cursor, void* gloc, void* gw, hipStream_t st) {
+                             int32_t* cursor, const int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
+                             hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
@@ -290,7 +297,8 @@ struct Grad {
         else
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, false>)
                             : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, false>);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, rkey, rw, cursor, gloc, gw, pb, gpb);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, rkey, rw, cursor, nunits, multi, gloc,
+                      gw, pb, gpb);
     }
 };
 
@@ -360,12 +368,14 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
                                       static_cast<uint32_t*>(nullptr), static_cast<float2*>(nullptr),
-                                      static_cast<int32_t*>(nullptr), gloc, gw, st));
+                                      static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                                      static_cast<const int32_t*>(nullptr), gloc, gw, st));
         return mark(ev, kStageAccum, st);
     }
     int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
     int32_t* nunits = reinterpret_cast<int32_t*>(ws + lay.nunits);
+    int32_t* multi = reinterpret_cast<int32_t*>(ws + lay.multi);
     int4* units = reinterpret_cast<int4*>(ws + lay.units);
     uint32_t* rkey = reinterpret_cast<uint32_t*>(ws + lay.rkey);
     float2* rw = reinterpret_cast<float2*>(ws + lay.rw);
@@ -380,10 +390,11 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     }
     MSDA_TRY(mark(ev, kStageScan, st));
     MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), 1, msda::kScanThreads, 0, st,
-                    static_cast<const int32_t*>(counts), cursor, nunits, units, gacc, accumulate, pb));
+                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb));
     MSDA_TRY(mark(ev, kStageGrad, st));
     MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, rkey, rw, cursor,
-                                  gloc, gw, st));
+                                  static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), gloc, gw,
+                                  st));
     MSDA_TRY(mark(ev, kStageAccum, st));
     return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, gout, static_cast<const uint32_t*>(rkey),
                                  static_cast<const float2*>(rw), static_cast<const int32_t*>(nunits),

@@ -65,7 +65,6 @@ constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 512;     // samples one gradient workgroup holds
 constexpr int kCountChunk = 4096;      // samples one counting workgroup bins
 constexpr int kScanThreads = 1024;
-constexpr int kMultiList = 2048;
 
 // Corners of one row that a record covers.
 enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
@@ -228,9 +227,11 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
 }
 
 // One workgroup.  counts -> cursor (exclusive prefix), the unit list
-// {segment, first record, end record, flush-with-atomics} and its length,
-// and zeroed rows for segments split over several units.  With `accumulate`
-// every unit adds into the caller's buffer, which is then left as it is.
+// {segment, first record, end record, flush-with-atomics} and its length
+// (nunits[0]), and the list of segments split over several units
+// (nunits[1] entries of `multi`), whose rows the gradient kernel zeroes.
+// With `accumulate` every unit adds into the caller's buffer, which is then
+// left as it is (and no segment is listed).
 // The counts are walked in chunks of kScanChunk entries, each loaded into
 // LDS with coalesced reads; every lane scans kScanChunk / kScanThreads
 // consecutive entries.
@@ -238,12 +239,11 @@ constexpr int kScanChunk = 8192;
 
 __global__ void __launch_bounds__(kScanThreads)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
-                     int32_t* __restrict__ nunits, int4* __restrict__ units, float* __restrict__ gacc,
+                     int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
                      int accumulate, Problem pb) {
     constexpr int kPer = kScanChunk / kScanThreads;
     __shared__ int32_t s_cnt[kScanChunk];
     __shared__ int32_t s_rec[kScanThreads], s_unit[kScanThreads];
-    __shared__ int32_t s_multi[kMultiList];
     __shared__ int32_t s_nmulti;
     const int t = threadIdx.x;
     const int n = pb.nplanes * pb.nseg;
@@ -283,11 +283,7 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
             for (int k = 0; k < u; ++k)
                 units[ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
                                              rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
-            if (u > 1 && !accumulate) {
-                const int k = atomicAdd(&s_nmulti, 1);
-                if (k < kMultiList) s_multi[k] = gi;
-                else zero_segment(pb, gacc, gi, 0, 1);
-            }
+            if (u > 1 && !accumulate) multi[atomicAdd(&s_nmulti, 1)] = gi;
             rbase += c;
             ubase += u;
         }
@@ -295,10 +291,10 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
         run_unit += s_unit[kScanThreads - 1];
         __syncthreads();
     }
-    if (t == 0) nunits[0] = run_unit;
-    __syncthreads();
-    const int nm = min(s_nmulti, kMultiList);
-    for (int k = 0; k < nm; ++k) zero_segment(pb, gacc, s_multi[k], t, kScanThreads);
+    if (t == 0) {
+        nunits[0] = run_unit;
+        nunits[1] = s_nmulti;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -311,7 +307,8 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 // four corner rows of each sample, forms the four dot products with the
 // query's grad_output row and reduces them over the group's lanes; when
 // BINNED, an epilogue reserves the workgroup's record ranges and writes the
-// records.
+// records, and workgroup i zeroes the rows of the multi-unit segments i,
+// i + gridDim.x, ... of the scan's list (the accumulation adds into them).
 // LDS: gpb * (12 * L * P + 4) words; when BINNED also nseg histogram and
 // nseg bases (int32) and 4 record ranks per sample (uint16).
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
@@ -320,6 +317,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                      const void* __restrict__ attw, const void* __restrict__ gout,
                      float* __restrict__ gacc, uint32_t* __restrict__ rkey,
                      float2* __restrict__ rw, int32_t* __restrict__ cursor,
+                     const int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
@@ -485,6 +483,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                 ++k;
                             });
         }
+        const int nm = nunits[1];
+        for (int e = blockIdx.x; e < nm; e += gridDim.x) zero_segment(pb, gacc, multi[e], threadIdx.x, blockDim.x);
     }
 }
 
@@ -558,7 +558,7 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
     // with LDS adds; every other row is this worker's alone.  Records are
     // taken kBatch at a time: the worker loads their weights and grad_output
     // rows together, then folds them in key order.
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 8;
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
