@@ -104,9 +104,119 @@ def load_traffic(digest: str, kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(kernel, {})
-    if rec.get("kernel_digest") != digest or ent.get("workload") != workload:
+    if rec.get("kernel_digest") != digest or not isinstance(ent, dict) or ent.get("workload") != workload:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+# The profiling commands whose output --ingest-profiles reads (REPO is the
+# repository root, DIR the directory later handed to --ingest-profiles; run
+# from /tmp with TMPDIR=/tmp).
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
+             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- "
+                  "python3 REPO/bench.py --calibrate-copy",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- "
+                  "python3 REPO/bench.py --calibrate-copy",
+}
+COPY_BYTES = 512 << 20           # one --calibrate-copy dispatch reads and writes this much
+
+
+def _short(name: str) -> str:
+    """Kernel name without template arguments and parameters."""
+    base = name.split("(")[0].replace("void ", "").strip()
+    return base.split("<")[0].split("::")[-1]
+
+
+def _counter_csv(d: str, counter: str) -> dict:
+    """{kernel: [values per dispatch]} of one rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    out = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def ingest_profiles(d: str, workload: str) -> None:
+    """Turn the raw rocprofv3 output of PROFILE_COMMANDS (under d) into the
+    short text summaries and profiles/traffic.json (HBM bytes per launch of
+    each msda kernel, for the roofline's traffic field).
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for a plain copy of COPY_BYTES (the runtime's copy kernel):
+    scale = COPY_BYTES / (counter KiB * 1024)."""
+    import csv
+    import glob
+    digest = kernel_digest()
+    cf = _counter_csv(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
+    cw = _counter_csv(os.path.join(d, "copy_write"), "WRITE_SIZE")
+    copy_k = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy_k:
+        raise RuntimeError("no copy kernel in the calibration runs")
+    kc = max(copy_k, key=lambda k: np.mean(cf[k]))
+    fetch_scale = COPY_BYTES / (np.mean(cf[kc]) * 1024.0)
+    write_scale = COPY_BYTES / (np.mean(cw[kc]) * 1024.0)
+    fetch = _counter_csv(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _counter_csv(os.path.join(d, "write"), "WRITE_SIZE")
+    rec = {"kernel_digest": digest, "workload": workload,
+           "calibration": {"copy_kernel": _short(kc), "copy_bytes": COPY_BYTES,
+                           "fetch_kib": round(float(np.mean(cf[kc])), 1), "fetch_scale": round(fetch_scale, 4),
+                           "write_kib": round(float(np.mean(cw[kc])), 1), "write_scale": round(write_scale, 4)},
+           "commands": {k: PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")}}
+    rows = []
+    for k in sorted(set(fetch) | set(write)):
+        if "msda" not in k:
+            continue
+        f_kib = float(np.mean(fetch.get(k, [0.0])))
+        w_kib = float(np.mean(write.get(k, [0.0])))
+        hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
+        ent = {"workload": workload, "dispatches": len(fetch.get(k, [])), "fetch_kib": round(f_kib, 1),
+               "write_kib": round(w_kib, 1), "hbm_bytes_per_launch": int(round(hbm))}
+        rec.setdefault(_short(k), ent)
+        rows.append((_short(k), k, ent))
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    md = [f"# HBM traffic per launch, msda kernels, workload {workload}", "",
+          f"Kernel sources digest {digest}. FETCH_SIZE / WRITE_SIZE are rocprofv3 per-dispatch",
+          "values in KiB, averaged over the dispatches of the run; bytes = KiB * 1024 * scale, with the",
+          f"scale taken from a plain {COPY_BYTES >> 20} MiB device copy ({_short(kc)}):",
+          f"FETCH_SIZE read {rec['calibration']['fetch_kib']} KiB -> scale {fetch_scale:.4f};",
+          f"WRITE_SIZE read {rec['calibration']['write_kib']} KiB -> scale {write_scale:.4f}.",
+          "The counters see traffic between L2 and the memory side (Infinity Cache included).", "",
+          "Commands (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", ""]
+    md += [f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    md += ["", "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes per launch (scaled) |",
+           "|---|---|---|---|---|"]
+    for short, _, e in rows:
+        md.append(f"| {short} | {e['dispatches']} | {e['fetch_kib']} | {e['write_kib']} | "
+                  f"{e['hbm_bytes_per_launch'] / 1e6:.1f} MB |")
+    with open(os.path.join(ROOT, "profiles", f"msda_kernels_{workload}_hbm_traffic.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    stats = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        md = [f"# Kernel trace statistics, workload {workload}", "",
+              f"Kernel sources digest {digest}. rocprofv3 --stats over a short bench run",
+              "(30 timed + 5 warm-up steps, plus the per-stage profiling pass).", "",
+              "Command (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
+              f"    {PROFILE_COMMANDS['trace']}", "",
+              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+        for r in csv.DictReader(open(stats[0])):
+            ns = {k: float(r.get(k) or "nan") for k in ("AverageNs", "MinNs", "MaxNs", "Percentage")}
+            md.append(f"| {r.get('Name', '?')[:110]} | {r.get('Calls', '?')} | {ns['AverageNs'] / 1e3:.2f} | "
+                      f"{ns['MinNs'] / 1e3:.2f} | {ns['MaxNs'] / 1e3:.2f} | {ns['Percentage']:.1f}% |")
+        with open(os.path.join(ROOT, "profiles", f"msda_kernels_{workload}_kernel_trace.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -139,10 +249,16 @@ def main() -> int:
                              "tiny_single_level"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ingest-profiles", metavar="DIR",
+                    help="summarise the rocprofv3 output of the profiling commands under DIR into profiles/ "
+                         "(no GPU needed) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device-to-device copy of 512 MiB, 4 times (the reference "
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.ingest_profiles:
+        ingest_profiles(args.ingest_profiles, args.workload)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

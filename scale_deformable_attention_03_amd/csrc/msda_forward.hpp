@@ -131,7 +131,10 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
     constexpr int kSB = L_CT && P_CT && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
-#pragma unroll 2
+    // 16-bit values widen to twice the registers; unrolling further than
+    // two batches there costs occupancy
+    constexpr int kUnroll = E == 4 ? 4 : 2;
+#pragma unroll kUnroll
     for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
         float4 w[kSB];
         Raw<VECB> raw[kSB][4];
