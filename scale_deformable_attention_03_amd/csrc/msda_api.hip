@@ -310,10 +310,10 @@ struct Accum {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
-                           (sizeof(uint32_t) + sizeof(uint16_t)) * msda::kUnitRecords +
+                           (sizeof(float2) + sizeof(uint32_t)) * msda::kSortedSlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
-        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, kBlock, lds, st, gout, rkey,
-                      rw, nunits, units, gacc, pb);
+        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::kAccBlock, lds, st,
+                      gout, rkey, rw, nunits, units, gacc, pb);
     }
 };
 

@@ -491,17 +491,26 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // ---------------------------------------------------------------------------
 // 4. accumulate
 // ---------------------------------------------------------------------------
-// Grid: an upper bound on the unit count, kBlock lanes; workgroups past
-// nunits exit.  LDS: the segment tile (keys * D floats), kUnitRecords
-// record keys (uint32) and their key order (uint16), 2 * kMaxSegKeys int32.
+// Grid: an upper bound on the unit count, kAccBlock lanes; workgroups past
+// nunits exit.  LDS: the segment tile (keys * D floats), the unit's records
+// sorted by key (kUnitRecords weight pairs and keys, padded), 2 * kMaxSegKeys
+// int32.
+constexpr int kAccBlock = 512;
+constexpr int kAccPerLane = kUnitRecords / kAccBlock;
+// Sorted position i lives at i + i / 32 (keys) and 2 * (i + i / 32) (weight
+// pairs): workers read positions 32 apart in lockstep, and the padding puts
+// those reads in different LDS banks.
+constexpr int kSortedSlots = kUnitRecords + kUnitRecords / 32;
+__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+
 template <int DT, int VECB, int LPR>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kAccBlock)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict__ rkey,
                        const float2* __restrict__ rw, const int32_t* __restrict__ nunits,
                        const int4* __restrict__ units, float* __restrict__ gacc, Problem pb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
-    constexpr int NW = kBlock / LPR;                 // workers
+    constexpr int NW = kAccBlock / LPR;              // workers
     const int nu = nunits[0];
     if (static_cast<int>(blockIdx.x) >= nu) return;
     // consecutive units (neighbouring segments of one plane) run on one XCD,
@@ -518,18 +527,26 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
 
     extern __shared__ float smem[];
     float* tile = smem;                                                  // nk * D
-    uint32_t* keys = reinterpret_cast<uint32_t*>(smem + (1 << shift) * D);
-    int32_t* hist = reinterpret_cast<int32_t*>(keys + kUnitRecords);
+    float2* sw = reinterpret_cast<float2*>(smem + (1 << shift) * D);     // sorted weights
+    uint32_t* skey = reinterpret_cast<uint32_t*>(sw + kSortedSlots);     // sorted keys
+    int32_t* hist = reinterpret_cast<int32_t*>(skey + kSortedSlots);
     int32_t* cur = hist + kMaxSegKeys;
-    uint16_t* order = reinterpret_cast<uint16_t*>(cur + kMaxSegKeys);
 
-    for (int i = threadIdx.x; i < nk * D; i += kBlock) tile[i] = 0.0f;
-    for (int i = threadIdx.x; i < kMaxSegKeys; i += kBlock) hist[i] = 0;
+    for (int i = threadIdx.x; i < nk * D; i += kAccBlock) tile[i] = 0.0f;
+    for (int i = threadIdx.x; i < kMaxSegKeys; i += kAccBlock) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const uint32_t r = rkey[unit.y + i];
-        keys[i] = r;
-        atomicAdd(&hist[r & 0xffu], 1);
+    // counting sort by the key byte: records are read once, coalesced, and
+    // held in registers until their sorted slot is known
+    uint32_t rk[kAccPerLane];
+    float2 rv[kAccPerLane];
+#pragma unroll
+    for (int j = 0; j < kAccPerLane; ++j) {
+        const int i = threadIdx.x + j * kAccBlock;
+        if (i < n) {
+            rk[j] = rkey[unit.y + i];
+            rv[j] = rw[unit.y + i];
+            atomicAdd(&hist[rk[j] & 0xffu], 1);
+        }
     }
     __syncthreads();
     if (threadIdx.x < 64) {                          // exclusive scan of 256 bins, one wave
@@ -548,31 +565,38 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
         for (int j = 0; j < 4; ++j) { cur[4 * lane + j] = run; run += v[j]; }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kBlock)
-        order[atomicAdd(&cur[keys[i] & 0xffu], 1)] = static_cast<uint16_t>(i);
+#pragma unroll
+    for (int j = 0; j < kAccPerLane; ++j) {
+        const int i = threadIdx.x + j * kAccBlock;
+        if (i < n) {
+            const int pos = padded(atomicAdd(&cur[rk[j] & 0xffu], 1));
+            skey[pos] = rk[j];
+            sw[pos] = rv[j];
+        }
+    }
     __syncthreads();
 
-    // Workers (LPR lanes each) walk key-sorted slices, accumulating a row in
-    // registers while the key holds.  Rows kf..kf+1 and kl..kl+1 of a slice
-    // may also receive contributions from neighbouring workers and are merged
-    // with LDS adds; every other row is this worker's alone.  Records are
-    // taken kBatch at a time: the worker loads their weights and grad_output
-    // rows together, then folds them in key order.
+    // Workers (LPR lanes each) walk equal slices of the sorted records,
+    // accumulating rows key and key + 1 in registers while the key holds.
+    // Rows kf..kf+1 and kl..kl+1 of a slice may also receive contributions
+    // from neighbouring workers and are merged with LDS adds; every other row
+    // is this worker's alone and is stored.  Records are taken kBatch at a
+    // time: the worker loads their grad_output rows together, then folds
+    // them in key order.
     constexpr int kBatch = 8;
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
     const int r1 = static_cast<int>(static_cast<int64_t>(n) * (w + 1) / NW);
     if (r0 < r1) {
-        const int kf = static_cast<int>(keys[order[r0]] & 0xffu);
-        const int kl = static_cast<int>(keys[order[r1 - 1]] & 0xffu);
+        const int kf = static_cast<int>(skey[padded(r0)] & 0xffu);
+        const int kl = static_cast<int>(skey[padded(r1 - 1)] & 0xffu);
         const int64_t gplane = static_cast<int64_t>(b) * pb.Q * pb.M + m;      // group (b, 0, m)
         const __amdgpu_buffer_rsrc_t gr = make_rsrc(
             static_cast<const char*>(gout) + gplane * D * E,
             static_cast<uint32_t>((static_cast<int64_t>(pb.Q) * pb.M - m) * D * E));
         const uint32_t qstride = static_cast<uint32_t>(pb.M * D * E);
         const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
-        const float2* wbase = rw + unit.y;
         auto flush = [&](int row, const float* acc) {
             if (!active || row >= nk) return;
             float* dst = tile + row * D + li * VEC;
@@ -596,17 +620,15 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
             for (int j = 0; j < kBatch; ++j) {
                 bkey[j] = -1;
                 bw[j] = make_float2(0.0f, 0.0f);
+                uint32_t off = kOffMap;                   // past the slice: zeros
                 if (base + j < r1) {
-                    const int idx = order[base + j];
-                    const uint32_t r = keys[idx];
+                    const int pj = padded(base + j);
+                    const uint32_t r = skey[pj];
                     bkey[j] = static_cast<int>(r & 0xffu);
-                    bw[j] = wbase[idx];
-                    // lanes past the row read zeros through an off-map offset
-                    graw[j] = buffer_load<VECB>(gr, active ? (r >> 8) * qstride + lane_b : kOffMap);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VECB / 4; ++i) graw[j].w[i] = 0u;
+                    bw[j] = sw[pj];
+                    if (active) off = (r >> 8) * qstride + lane_b;
                 }
+                graw[j] = buffer_load<VECB>(gr, off);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
@@ -644,20 +666,21 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
     __syncthreads();
 
     // Write the segment's rows: row k is key start + k0 + k of plane (b, m).
-    const int atomic_flush = unit.w;
-    const int q4 = D / 4;
+    // A segment split over several units adds with float atomics, lane i on
+    // element i of a row (the lane-contiguous pattern); otherwise one 16-byte
+    // store per lane.
     const int64_t row0 = (static_cast<int64_t>(b) * pb.K + pb.lv.start[lvl] + k0) * pb.M + m;
-    for (int i = threadIdx.x; i < nk * q4; i += kBlock) {
-        const int k = i / q4, c4 = i - k * q4;
-        float* dst = gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + 4 * c4;
-        const float* src = tile + k * D + 4 * c4;
-        if (atomic_flush) {
-            atomic_add_f32(dst + 0, src[0]);
-            atomic_add_f32(dst + 1, src[1]);
-            atomic_add_f32(dst + 2, src[2]);
-            atomic_add_f32(dst + 3, src[3]);
-        } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(src[0], src[1], src[2], src[3]);
+    if (unit.w) {
+        for (int i = threadIdx.x; i < nk * D; i += kAccBlock) {
+            const int k = i / D, d = i - k * D;
+            atomic_add_f32(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + d, tile[i]);
+        }
+    } else {
+        const int q4 = D / 4;
+        for (int i = threadIdx.x; i < nk * q4; i += kAccBlock) {
+            const int k = i / q4, c4 = i - k * q4;
+            *reinterpret_cast<float4*>(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + 4 * c4) =
+                *reinterpret_cast<const float4*>(tile + k * D + 4 * c4);
         }
     }
 }
