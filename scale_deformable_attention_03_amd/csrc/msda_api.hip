@@ -94,7 +94,7 @@ int floor_log2(int64_t v) {
 
 // Problem descriptor for the kernels, including the key segments of the
 // binned backward: level l gets segments of 2^shift keys, sized so that a
-// segment receives about kUnitRecords / 2 records when the samples spread
+// segment receives about 3/4 kUnitRecords records when the samples spread
 // evenly over the level (two records per sample and level, Q*P samples per
 // level and plane), but never fewer than 32 keys: a denser level spreads a
 // segment over several units (merged with atomics) rather than letting
@@ -121,7 +121,7 @@ msda::Problem pack(const msda_problem_t* p) {
         pb.lv.W[l] = static_cast<int32_t>(W);
         pb.lv.start[l] = static_cast<int32_t>(p->level_start_index[l]);
         const double per_key = 2.0 * double(p->num_queries) * p->num_points / double(H * W);
-        const double keys = per_key > 0 ? (msda::kUnitRecords / 2) / per_key : double(msda::kMaxSegKeys);
+        const double keys = per_key > 0 ? (3 * msda::kUnitRecords / 4) / per_key : double(msda::kMaxSegKeys);
         int shift = keys >= 1.0 ? floor_log2(static_cast<int64_t>(keys)) : 0;
         if (shift < 5) shift = 5;
         if (shift > max_shift) shift = max_shift;

@@ -611,52 +611,47 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
         float accA[VEC], accB[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) accA[i] = accB[i] = 0.0f;
-        int key = -1;
+        int key = kf;
         for (int base = r0; base < r1; base += kBatch) {
             int bkey[kBatch];
             float2 bw[kBatch];
             Raw<VECB> graw[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                bkey[j] = -1;
-                bw[j] = make_float2(0.0f, 0.0f);
-                uint32_t off = kOffMap;                   // past the slice: zeros
-                if (base + j < r1) {
-                    const int pj = padded(base + j);
-                    const uint32_t r = skey[pj];
-                    bkey[j] = static_cast<int>(r & 0xffu);
-                    bw[j] = sw[pj];
-                    if (active) off = (r >> 8) * qstride + lane_b;
-                }
-                graw[j] = buffer_load<VECB>(gr, off);
+                // a position past the slice re-reads the slice's last record
+                // and takes zero weight and zero grad_output: it adds nothing
+                // and, having the last key, never flushes out of order
+                const bool in = base + j < r1;
+                const int pj = padded(in ? base + j : r1 - 1);
+                const uint32_t r = skey[pj];
+                const float2 wv = sw[pj];
+                bkey[j] = static_cast<int>(r & 0xffu);
+                bw[j] = in ? wv : make_float2(0.0f, 0.0f);
+                graw[j] = buffer_load<VECB>(gr, in && active ? (r >> 8) * qstride + lane_b : kOffMap);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const int rk = bkey[j];
-                if (rk >= 0) {                               // records past the slice are -1
-                    if (rk != key) {
-                        if (key >= 0) {
-                            flush(key, accA);
-                            if (rk == key + 1) {
+                if (rk != key) {
+                    flush(key, accA);
+                    if (rk == key + 1) {
 #pragma unroll
-                                for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
-                            } else {
-                                flush(key + 1, accB);
+                        for (int i = 0; i < VEC; ++i) accA[i] = accB[i];
+                    } else {
+                        flush(key + 1, accB);
 #pragma unroll
-                                for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
-                            }
-#pragma unroll
-                            for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
-                        }
-                        key = rk;
+                        for (int i = 0; i < VEC; ++i) accA[i] = 0.0f;
                     }
-                    float gv[VEC];
-                    widen<DT, VECB>(graw[j], gv);
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) {
-                        accA[i] += bw[j].x * gv[i];
-                        accB[i] += bw[j].y * gv[i];
-                    }
+                    for (int i = 0; i < VEC; ++i) accB[i] = 0.0f;
+                    key = rk;
+                }
+                float gv[VEC];
+                widen<DT, VECB>(graw[j], gv);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    accA[i] += bw[j].x * gv[i];
+                    accB[i] += bw[j].y * gv[i];
                 }
             }
         }
