@@ -148,7 +148,7 @@ bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
 
 struct Layout {
     bool binned;
-    size_t counts, cursor, nunits, multi, units, rkey, rw, acc, total;
+    size_t counts, cursor, nunits, multi, units, recs, acc, total;
     int64_t max_units;
 };
 
@@ -172,10 +172,8 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
         off += round_up(nbins * 4);
         w.units = off;
         off += round_up(w.max_units * 16);
-        w.rkey = off;
-        off += round_up(max_records(p) * 4);
-        w.rw = off;
-        off += round_up(max_records(p) * 8);
+        w.recs = off;
+        off += round_up(max_records(p) * 12);
     }
     w.acc = off;
     if (p->dtype != MSDA_F32) off += round_up(value_elems(p) * 4);
@@ -282,14 +280,15 @@ struct Fwd {
 template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
-                             const void* w, const void* gout, float* gacc, uint32_t* rkey, float2* rw,
-                             int32_t* cursor, const int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
+                             const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor, const int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
                              hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
         size_t lds = sizeof(uint32_t) * gpb * (12 * LP + 4);
-        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg) + sizeof(uint16_t) * gpb * LP * 4;
+        if (binned)
+            lds += sizeof(int32_t) * (2 * size_t(pb.nseg) + (pb.nseg & 1)) + sizeof(int2) * gpb * LP +
+                   sizeof(uint16_t) * gpb * LP * 4;
         const void* k;
         if (binned)
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)
@@ -297,23 +296,23 @@ struct Grad {
         else
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, false>)
                             : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, false>);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, rkey, rw, cursor, nunits, multi, gloc,
-                      gw, pb, gpb);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, recs, cursor, nunits, multi, gloc, gw,
+                      pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
 struct Accum {
     static msda_status_t run(const msda::Problem& pb, int64_t max_units, const void* gout,
-                             const uint32_t* rkey, const float2* rw, const int32_t* nunits,
-                             const int4* units, float* gacc, hipStream_t st) {
+                             const uint3* recs, const int32_t* nunits, const int4* units, float* gacc,
+                             hipStream_t st) {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
                            (sizeof(float2) + sizeof(uint32_t)) * msda::kSortedSlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
         return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::kAccBlock, lds, st,
-                      gout, rkey, rw, nunits, units, gacc, pb);
+                      gout, recs, nunits, units, gacc, pb);
     }
 };
 
@@ -367,8 +366,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
-                                      static_cast<uint32_t*>(nullptr), static_cast<float2*>(nullptr),
-                                      static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                                      static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
                                       static_cast<const int32_t*>(nullptr), gloc, gw, st));
         return mark(ev, kStageAccum, st);
     }
@@ -377,8 +375,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     int32_t* nunits = reinterpret_cast<int32_t*>(ws + lay.nunits);
     int32_t* multi = reinterpret_cast<int32_t*>(ws + lay.multi);
     int4* units = reinterpret_cast<int4*>(ws + lay.units);
-    uint32_t* rkey = reinterpret_cast<uint32_t*>(ws + lay.rkey);
-    float2* rw = reinterpret_cast<float2*>(ws + lay.rw);
+    uint3* recs = reinterpret_cast<uint3*>(ws + lay.recs);
 
     MSDA_TRY(mark(ev, kStageZero, st));
     MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
@@ -392,12 +389,12 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), 1, msda::kScanThreads, 0, st,
                     static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, rkey, rw, cursor,
+    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, recs, cursor,
                                   static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, gout, static_cast<const uint32_t*>(rkey),
-                                 static_cast<const float2*>(rw), static_cast<const int32_t*>(nunits),
+    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, gout, static_cast<const uint3*>(recs),
+                                 static_cast<const int32_t*>(nunits),
                                  static_cast<const int4*>(units), gacc, st);
 }
 

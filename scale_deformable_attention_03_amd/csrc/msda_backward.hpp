@@ -60,6 +60,7 @@ namespace msda {
 //         segment), each w * (1-ly or ly) * (1-lx or lx)
 constexpr int kQueryBits = 24;         // queries per plane for the binned path
 constexpr int kMaxSegKeys = 256;       // keys per segment (8-bit key field)
+constexpr int kNoCell = -0x40000000;   // cell marker of a sample off the map
 constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 512;     // samples one gradient workgroup holds
@@ -182,8 +183,9 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
             if (s < s_end) {
                 const int q = s / LP, lp = s - q * LP;
                 const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
-                lx[u] = load_scalar<DT>(loc, 2 * i);
-                ly[u] = load_scalar<DT>(loc, 2 * i + 1);
+                const float2 xy = load_pair<DT>(loc, i);
+                lx[u] = xy.x;
+                ly[u] = xy.y;
             }
         }
 #pragma unroll
@@ -315,8 +317,7 @@ template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                      const void* __restrict__ attw, const void* __restrict__ gout,
-                     float* __restrict__ gacc, uint32_t* __restrict__ rkey,
-                     float2* __restrict__ rw, int32_t* __restrict__ cursor,
+                     float* __restrict__ gacc, uint3* __restrict__ recs, int32_t* __restrict__ cursor,
                      const int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
@@ -331,7 +332,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     uint32_t* srec = sm;
     int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);
     int32_t* lbase = lhist + pb.nseg;
-    uint16_t* lrank = reinterpret_cast<uint16_t*>(lbase + pb.nseg);
+    int2* lxy = reinterpret_cast<int2*>(lbase + pb.nseg + (pb.nseg & 1));   // cell of each sample
+    uint16_t* lrank = reinterpret_cast<uint16_t*>(lxy + gpb * LP);
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
@@ -345,8 +347,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
         const int H = pb.lv.H[l], W = pb.lv.W[l];
-        const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), H, W,
-                                         pb.lv.start[l], pitch);
+        const float2 xy = load_pair<DT>(loc, si);
+        const Corners c = sample_corners(xy.x, xy.y, H, W, pb.lv.start[l], pitch);
         const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         uint32_t* r = srec + g * gstride + lp * 12;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
@@ -354,6 +356,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         *reinterpret_cast<float4*>(r + 8) = make_float4(static_cast<float>(W) * aw, static_cast<float>(H) * aw,
                                                         aw * c.hy, aw * c.ly);
         if constexpr (BINNED) {
+            lxy[i] = make_int2(c.ok ? c.x0 : kNoCell, c.y0);
             if (c.ok) {
                 int k = 0;
                 for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l], [&](int seg, int, int, int) {
@@ -451,8 +454,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             if (li < kC) {
                 const int64_t s = G * LP + c0 + li;
                 store_scalar<DT>(grad_w, s, own_w);
-                store_scalar<DT>(grad_loc, 2 * s, own_x);
-                store_scalar<DT>(grad_loc, 2 * s + 1, own_y);
+                store_pair<DT>(grad_loc, s, own_x, own_y);
             }
         }
     }
@@ -461,25 +463,25 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x)
             if (lhist[i] != 0) lbase[i] = atomicAdd(&cursor[static_cast<int64_t>(t.pl) * pb.nseg + i], lhist[i]);
         __syncthreads();
-        // records: recompute each sample's cell (same arithmetic as the
-        // prologue) and write its records at base + rank
+        // records, from the prologue's cell and weights in LDS, at base + rank
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+            const int2 cell = lxy[i];
+            if (cell.x == kNoCell) continue;
             const int g = i / LP, lp = i - g * LP, l = lp / P;
-            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
             const int H = pb.lv.H[l], W = pb.lv.W[l];
-            const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1), H,
-                                             W, pb.lv.start[l], pitch);
-            if (!c.ok) continue;
-            const float aw = load_scalar<DT>(attw, si);
+            const uint32_t* r = srec + g * gstride + lp * 12;
+            const float4 f = *reinterpret_cast<const float4*>(r + 4);     // hx lx hy ly
+            const float4 sc = *reinterpret_cast<const float4*>(r + 8);    // W*w H*w w*hy w*ly
             const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
             int k = 0;
-            for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+            for_each_record(cell.x, cell.y, W, H, pb.seg_shift[l], pb.seg_base[l],
                             [&](int seg, int key, int row, int mode) {
-                                const float wy = aw * (row ? c.ly : c.hy);
-                                const float cl = wy * c.hx, cr = wy * c.lx;
+                                const float wy = row ? sc.w : sc.z;
+                                const float cl = wy * f.x, cr = wy * f.y;
                                 const int pos = lbase[seg] + lrank[4 * i + k];
-                                rkey[pos] = qk | static_cast<uint32_t>(key);
-                                rw[pos] = make_float2(mode == kRightOnly ? cr : cl, mode == kBoth ? cr : 0.0f);
+                                recs[pos] = make_uint3(qk | static_cast<uint32_t>(key),
+                                                       __float_as_uint(mode == kRightOnly ? cr : cl),
+                                                       __float_as_uint(mode == kBoth ? cr : 0.0f));
                                 ++k;
                             });
         }
@@ -505,8 +507,8 @@ __device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
 
 template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(kAccBlock)
-msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict__ rkey,
-                       const float2* __restrict__ rw, const int32_t* __restrict__ nunits,
+msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
+                       const int32_t* __restrict__ nunits,
                        const int4* __restrict__ units, float* __restrict__ gacc, Problem pb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
@@ -543,8 +545,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint32_t* __restrict
     for (int j = 0; j < kAccPerLane; ++j) {
         const int i = threadIdx.x + j * kAccBlock;
         if (i < n) {
-            rk[j] = rkey[unit.y + i];
-            rv[j] = rw[unit.y + i];
+            const uint3 rec = recs[unit.y + i];
+            rk[j] = rec.x;
+            rv[j] = make_float2(__uint_as_float(rec.y), __uint_as_float(rec.z));
             atomicAdd(&hist[rk[j] & 0xffu], 1);
         }
     }

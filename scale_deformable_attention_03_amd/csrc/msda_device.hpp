@@ -91,6 +91,29 @@ __device__ __forceinline__ void store_scalar(void* base, int64_t i, float v) {
     }
 }
 
+// Elements 2i and 2i + 1 (a location's x and y) in one load / one store.
+template <int DT>
+__device__ __forceinline__ float2 load_pair(const void* base, int64_t i) {
+    if constexpr (DT == kF32) {
+        return static_cast<const float2*>(base)[i];
+    } else {
+        const uint32_t w = static_cast<const uint32_t*>(base)[i];
+        if constexpr (DT == kF16) return make_float2(f16_bits_to_f32(w & 0xffffu), f16_bits_to_f32(w >> 16));
+        else return make_float2(bf16_bits_to_f32(w & 0xffffu), bf16_bits_to_f32(w >> 16));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_pair(void* base, int64_t i, float a, float b) {
+    if constexpr (DT == kF32) {
+        static_cast<float2*>(base)[i] = make_float2(a, b);
+    } else if constexpr (DT == kF16) {
+        static_cast<uint32_t*>(base)[i] = f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+    } else {
+        static_cast<uint32_t*>(base)[i] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    }
+}
+
 // ---- vector row slices -------------------------------------------------------
 
 // VECB raw bytes of a row, held in 32-bit words.

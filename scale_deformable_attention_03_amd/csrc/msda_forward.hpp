@@ -111,8 +111,8 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-        const Corners c = sample_corners(load_scalar<DT>(loc, 2 * si), load_scalar<DT>(loc, 2 * si + 1),
-                                         pb.lv.H[l], pb.lv.W[l], pb.lv.start[l], pitch);
+        const float2 xy = load_pair<DT>(loc, si);
+        const Corners c = sample_corners(xy.x, xy.y, pb.lv.H[l], pb.lv.W[l], pb.lv.start[l], pitch);
         const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         const float wy0 = aw * c.hy, wy1 = aw * c.ly;
         uint32_t* r = sm + g * gstride + lp * 8;
