@@ -309,7 +309,7 @@ struct Accum {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
-                           (sizeof(float2) + sizeof(uint32_t)) * msda::kSortedSlots +
+                           sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
         return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::kAccBlock, lds, st,
                       gout, recs, nunits, units, gacc, pb);

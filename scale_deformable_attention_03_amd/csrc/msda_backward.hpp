@@ -499,11 +499,14 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // int32.
 constexpr int kAccBlock = 512;
 constexpr int kAccPerLane = kUnitRecords / kAccBlock;
-// Sorted position i lives at i + i / 32 (keys) and 2 * (i + i / 32) (weight
-// pairs): workers read positions 32 apart in lockstep, and the padding puts
-// those reads in different LDS banks.
-constexpr int kSortedSlots = kUnitRecords + kUnitRecords / 32;
-__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+// Sorted record i: key at word i + 4 * (i / 32), weight pair at pair slot
+// i + 2 * (i / 32).  Workers start 8-aligned batches about 32 records apart
+// and read them with 16-byte vector reads; the padding keeps those reads
+// aligned and puts the eight workers of a wave in different LDS banks.
+constexpr int kSortedKeySlots = kUnitRecords + kUnitRecords / 8 + 8;
+constexpr int kSortedPairSlots = kUnitRecords + kUnitRecords / 16 + 8;
+__device__ __forceinline__ int key_slot(int i) { return i + 4 * (i >> 5); }
+__device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 
 template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(kAccBlock)
@@ -530,8 +533,8 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     extern __shared__ float smem[];
     float* tile = smem;                                                  // nk * D
     float2* sw = reinterpret_cast<float2*>(smem + (1 << shift) * D);     // sorted weights
-    uint32_t* skey = reinterpret_cast<uint32_t*>(sw + kSortedSlots);     // sorted keys
-    int32_t* hist = reinterpret_cast<int32_t*>(skey + kSortedSlots);
+    uint32_t* skey = reinterpret_cast<uint32_t*>(sw + kSortedPairSlots); // sorted keys
+    int32_t* hist = reinterpret_cast<int32_t*>(skey + kSortedKeySlots);
     int32_t* cur = hist + kMaxSegKeys;
 
     for (int i = threadIdx.x; i < nk * D; i += kAccBlock) tile[i] = 0.0f;
@@ -572,14 +575,14 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     for (int j = 0; j < kAccPerLane; ++j) {
         const int i = threadIdx.x + j * kAccBlock;
         if (i < n) {
-            const int pos = padded(atomicAdd(&cur[rk[j] & 0xffu], 1));
-            skey[pos] = rk[j];
-            sw[pos] = rv[j];
+            const int pos = atomicAdd(&cur[rk[j] & 0xffu], 1);
+            skey[key_slot(pos)] = rk[j];
+            sw[pair_slot(pos)] = rv[j];
         }
     }
     __syncthreads();
 
-    // Workers (LPR lanes each) walk equal slices of the sorted records,
+    // Workers (LPR lanes each) walk equal 8-aligned slices of the sorted records,
     // accumulating rows key and key + 1 in registers while the key holds.
     // Rows kf..kf+1 and kl..kl+1 of a slice may also receive contributions
     // from neighbouring workers and are merged with LDS adds; every other row
@@ -589,11 +592,13 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     constexpr int kBatch = 8;
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
-    const int r0 = static_cast<int>(static_cast<int64_t>(n) * w / NW);
-    const int r1 = static_cast<int>(static_cast<int64_t>(n) * (w + 1) / NW);
+    static_assert(kBatch == 8, "batches are read as two 16-byte key vectors");
+    const int nb = (n + kBatch - 1) / kBatch;        // 8-record batches
+    const int r0 = kBatch * static_cast<int>(static_cast<int64_t>(nb) * w / NW);
+    const int r1 = min(n, kBatch * static_cast<int>(static_cast<int64_t>(nb) * (w + 1) / NW));
     if (r0 < r1) {
-        const int kf = static_cast<int>(skey[padded(r0)] & 0xffu);
-        const int kl = static_cast<int>(skey[padded(r1 - 1)] & 0xffu);
+        const int kf = static_cast<int>(skey[key_slot(r0)] & 0xffu);
+        const int kl = static_cast<int>(skey[key_slot(r1 - 1)] & 0xffu);
         const int64_t gplane = static_cast<int64_t>(b) * pb.Q * pb.M + m;      // group (b, 0, m)
         const __amdgpu_buffer_rsrc_t gr = make_rsrc(
             static_cast<const char*>(gout) + gplane * D * E,
@@ -619,18 +624,27 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
             int bkey[kBatch];
             float2 bw[kBatch];
             Raw<VECB> graw[kBatch];
+            // the batch's 8 keys and weight pairs: 2 + 4 vector reads
+            // (positions past the unit's end read padding and are masked)
+            const uint4 ka = *reinterpret_cast<const uint4*>(skey + key_slot(base));
+            const uint4 kb = *reinterpret_cast<const uint4*>(skey + key_slot(base) + 4);
+            const float4 wa = *reinterpret_cast<const float4*>(sw + pair_slot(base));
+            const float4 wb = *reinterpret_cast<const float4*>(sw + pair_slot(base) + 2);
+            const float4 wc = *reinterpret_cast<const float4*>(sw + pair_slot(base) + 4);
+            const float4 wd = *reinterpret_cast<const float4*>(sw + pair_slot(base) + 6);
+            const uint32_t rr[kBatch] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+            const float2 ww[kBatch] = {make_float2(wa.x, wa.y), make_float2(wa.z, wa.w), make_float2(wb.x, wb.y),
+                                       make_float2(wb.z, wb.w), make_float2(wc.x, wc.y), make_float2(wc.z, wc.w),
+                                       make_float2(wd.x, wd.y), make_float2(wd.z, wd.w)};
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                // a position past the slice re-reads the slice's last record
-                // and takes zero weight and zero grad_output: it adds nothing
-                // and, having the last key, never flushes out of order
+                // a position past the slice takes the previous key, zero
+                // weights and zero grad_output: it adds nothing and never
+                // flushes
                 const bool in = base + j < r1;
-                const int pj = padded(in ? base + j : r1 - 1);
-                const uint32_t r = skey[pj];
-                const float2 wv = sw[pj];
-                bkey[j] = static_cast<int>(r & 0xffu);
-                bw[j] = in ? wv : make_float2(0.0f, 0.0f);
-                graw[j] = buffer_load<VECB>(gr, in && active ? (r >> 8) * qstride + lane_b : kOffMap);
+                bkey[j] = in ? static_cast<int>(rr[j] & 0xffu) : (j > 0 ? bkey[j > 0 ? j - 1 : 0] : key);
+                bw[j] = in ? ww[j] : make_float2(0.0f, 0.0f);
+                graw[j] = buffer_load<VECB>(gr, in && active ? (rr[j] >> 8) * qstride + lane_b : kOffMap);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
