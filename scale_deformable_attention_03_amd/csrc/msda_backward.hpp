@@ -542,17 +542,14 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     __syncthreads();
     // counting sort by the key byte: records are read once, coalesced, and
     // held in registers until their sorted slot is known
-    uint32_t rk[kAccPerLane];
-    float2 rv[kAccPerLane];
+    uint3 rec[kAccPerLane];
+    if (n > 0) {
+        // all loads in flight together (positions past n re-read the last record)
 #pragma unroll
-    for (int j = 0; j < kAccPerLane; ++j) {
-        const int i = threadIdx.x + j * kAccBlock;
-        if (i < n) {
-            const uint3 rec = recs[unit.y + i];
-            rk[j] = rec.x;
-            rv[j] = make_float2(__uint_as_float(rec.y), __uint_as_float(rec.z));
-            atomicAdd(&hist[rk[j] & 0xffu], 1);
-        }
+        for (int j = 0; j < kAccPerLane; ++j) rec[j] = recs[unit.y + min(static_cast<int>(threadIdx.x) + j * kAccBlock, n - 1)];
+#pragma unroll
+        for (int j = 0; j < kAccPerLane; ++j)
+            if (static_cast<int>(threadIdx.x) + j * kAccBlock < n) atomicAdd(&hist[rec[j].x & 0xffu], 1);
     }
     __syncthreads();
     if (threadIdx.x < 64) {                          // exclusive scan of 256 bins, one wave
@@ -575,10 +572,18 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     for (int j = 0; j < kAccPerLane; ++j) {
         const int i = threadIdx.x + j * kAccBlock;
         if (i < n) {
-            const int pos = atomicAdd(&cur[rk[j] & 0xffu], 1);
-            skey[key_slot(pos)] = rk[j];
-            sw[pair_slot(pos)] = rv[j];
+            const int pos = atomicAdd(&cur[rec[j].x & 0xffu], 1);
+            skey[key_slot(pos)] = rec[j].x;
+            sw[pair_slot(pos)] = make_float2(__uint_as_float(rec[j].y), __uint_as_float(rec[j].z));
         }
+    }
+    // pad to whole 8-record batches: the largest key, zero weights and a
+    // query index one past the last, whose grad_output reads fall outside the
+    // buffer and return zeros
+    const int n8 = (n + 7) & ~7;
+    if (static_cast<int>(threadIdx.x) < n8 - n) {
+        skey[key_slot(n + threadIdx.x)] = (static_cast<uint32_t>(pb.Q) << 8) | 0xffu;
+        sw[pair_slot(n + threadIdx.x)] = make_float2(0.0f, 0.0f);
     }
     __syncthreads();
 
@@ -593,9 +598,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     const int w = threadIdx.x / LPR, li = threadIdx.x % LPR;
     const bool active = li < pb.lpr_active;
     static_assert(kBatch == 8, "batches are read as two 16-byte key vectors");
-    const int nb = (n + kBatch - 1) / kBatch;        // 8-record batches
+    const int nb = n8 / kBatch;                      // whole 8-record batches
     const int r0 = kBatch * static_cast<int>(static_cast<int64_t>(nb) * w / NW);
-    const int r1 = min(n, kBatch * static_cast<int>(static_cast<int64_t>(nb) * (w + 1) / NW));
+    const int r1 = kBatch * static_cast<int>(static_cast<int64_t>(nb) * (w + 1) / NW);
     if (r0 < r1) {
         const int kf = static_cast<int>(skey[key_slot(r0)] & 0xffu);
         const int kl = static_cast<int>(skey[key_slot(r1 - 1)] & 0xffu);
@@ -604,7 +609,8 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
             static_cast<const char*>(gout) + gplane * D * E,
             static_cast<uint32_t>((static_cast<int64_t>(pb.Q) * pb.M - m) * D * E));
         const uint32_t qstride = static_cast<uint32_t>(pb.M * D * E);
-        const uint32_t lane_b = static_cast<uint32_t>(li * VECB);
+        // lanes past the row read zeros through an out-of-range offset
+        const uint32_t lane_b = active ? static_cast<uint32_t>(li * VECB) : kOffMap;
         auto flush = [&](int row, const float* acc) {
             if (!active || row >= nk) return;
             float* dst = tile + row * D + li * VEC;
@@ -625,7 +631,6 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
             float2 bw[kBatch];
             Raw<VECB> graw[kBatch];
             // the batch's 8 keys and weight pairs: 2 + 4 vector reads
-            // (positions past the unit's end read padding and are masked)
             const uint4 ka = *reinterpret_cast<const uint4*>(skey + key_slot(base));
             const uint4 kb = *reinterpret_cast<const uint4*>(skey + key_slot(base) + 4);
             const float4 wa = *reinterpret_cast<const float4*>(sw + pair_slot(base));
@@ -638,13 +643,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
                                        make_float2(wd.x, wd.y), make_float2(wd.z, wd.w)};
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                // a position past the slice takes the previous key, zero
-                // weights and zero grad_output: it adds nothing and never
-                // flushes
-                const bool in = base + j < r1;
-                bkey[j] = in ? static_cast<int>(rr[j] & 0xffu) : (j > 0 ? bkey[j > 0 ? j - 1 : 0] : key);
-                bw[j] = in ? ww[j] : make_float2(0.0f, 0.0f);
-                graw[j] = buffer_load<VECB>(gr, in && active ? (rr[j] >> 8) * qstride + lane_b : kOffMap);
+                bkey[j] = static_cast<int>(rr[j] & 0xffu);
+                bw[j] = ww[j];
+                graw[j] = buffer_load<VECB>(gr, (rr[j] >> 8) * qstride + lane_b);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
