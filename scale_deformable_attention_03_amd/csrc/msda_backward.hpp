@@ -153,6 +153,46 @@ __device__ __forceinline__ void lds_add_f32(float* p, float v) {
     }
 }
 
+// dst[0..N) += v[0..N) in LDS.  For even N (dst 8-byte aligned): N/2 64-bit
+// compare-and-swaps per round, all issued before any result is checked; a
+// pair already added re-swaps the value it last saw with itself, which
+// changes nothing.  Odd N falls back to one 32-bit loop per float.
+template <int N>
+__device__ __forceinline__ void lds_add_f32xN(float* dst, const float* v) {
+    if constexpr (N % 2 != 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) lds_add_f32(dst + i, v[i]);
+    } else {
+        constexpr int NP = N / 2;
+        uint64_t* u = reinterpret_cast<uint64_t*>(dst);
+        uint64_t seen[NP];
+        bool done[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            seen[i] = __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            done[i] = false;
+        }
+        bool all;
+        do {
+            all = true;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const float lo = __uint_as_float(static_cast<uint32_t>(seen[i])) + v[2 * i];
+                const float hi = __uint_as_float(static_cast<uint32_t>(seen[i] >> 32)) + v[2 * i + 1];
+                const uint64_t sum = static_cast<uint64_t>(__float_as_uint(lo)) |
+                                     (static_cast<uint64_t>(__float_as_uint(hi)) << 32);
+                uint64_t expect = seen[i];
+                const bool ok = __hip_atomic_compare_exchange_strong(u + i, &expect, done[i] ? seen[i] : sum,
+                                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (!done[i]) seen[i] = expect;
+                done[i] = done[i] || ok;
+                all = all && done[i];
+            }
+        } while (!all);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 1. count
 // ---------------------------------------------------------------------------
@@ -509,7 +549,7 @@ __device__ __forceinline__ int key_slot(int i) { return i + 4 * (i >> 5); }
 __device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 
 template <int DT, int VECB, int LPR>
-__global__ void __launch_bounds__(kAccBlock)
+__global__ void __launch_bounds__(kAccBlock, DT == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits,
                        const int4* __restrict__ units, float* __restrict__ gacc, Problem pb) {
@@ -618,8 +658,7 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) dst[i] = acc[i];
             } else {
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) lds_add_f32(dst + i, acc[i]);
+                lds_add_f32xN<VEC>(dst, acc);
             }
         };
         float accA[VEC], accB[VEC];
