@@ -139,9 +139,18 @@ msda::Problem pack(const msda_problem_t* p) {
 // counts within int32.
 int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
 
+// Per plane: at most 4 records per sample, so a fixed region of
+// plane_records; at most one unit per segment plus one per kUnitRecords.
+int64_t plane_records(const msda_problem_t* p) {
+    return 4 * int64_t(p->num_queries) * p->num_levels * p->num_points;
+}
+int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
+    return pb.nseg + (plane_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
+}
+
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
     return p->num_queries < (1 << msda::kQueryBits) && pb.nseg <= msda::kMaxSegments &&
-           max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * pb.nseg < kIndexLimit / 2;
+           max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * plane_units(p, pb) < kIndexLimit / 2;
 }
 
 // ---- workspace layout --------------------------------------------------------
@@ -161,13 +170,15 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
     size_t off = 0;
     if (w.binned) {
         const int64_t nbins = int64_t(pb.nplanes) * pb.nseg;
-        w.max_units = nbins + (max_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
-        w.counts = off;
-        off += round_up(nbins * 4);
+        w.max_units = int64_t(pb.nplanes) * plane_units(p, pb);
+        w.counts = off;          // nbins counts, then the scan's ticket counter
+        off += round_up(nbins * 4 + 4);
         w.cursor = off;
         off += round_up(nbins * 4);
-        w.nunits = off;          // [0] unit count, [1] count of multi-unit segments
-        off += 256;
+        // [p] units of plane p, [nplanes + p] its multi-unit segments,
+        // [2 nplanes + p] units before plane p, [3 nplanes] all units
+        w.nunits = off;
+        off += round_up((size_t(pb.nplanes) * 3 + 1) * 4);
         w.multi = off;
         off += round_up(nbins * 4);
         w.units = off;
@@ -303,7 +314,7 @@ struct Grad {
 
 template <int DT, int VECB, int LPR>
 struct Accum {
-    static msda_status_t run(const msda::Problem& pb, int64_t max_units, const void* gout,
+    static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
                              const uint3* recs, const int32_t* nunits, const int4* units, float* gacc,
                              hipStream_t st) {
         int max_shift = 0;
@@ -312,7 +323,7 @@ struct Accum {
                            sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
         return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::kAccBlock, lds, st,
-                      gout, recs, nunits, units, gacc, pb);
+                      gout, recs, nunits, units, gacc, pb, plane_units);
     }
 };
 
@@ -378,7 +389,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     uint3* recs = reinterpret_cast<uint3*>(ws + lay.recs);
 
     MSDA_TRY(mark(ev, kStageZero, st));
-    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
+    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4 + 4), st));
     MSDA_TRY(mark(ev, kStageCount, st));
     switch (problem->dtype) {
         case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, loc, counts, st)); break;
@@ -386,14 +397,17 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         default: MSDA_TRY(count_launch<kBF16>(pb, loc, counts, st)); break;
     }
     MSDA_TRY(mark(ev, kStageScan, st));
-    MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), 1, msda::kScanThreads, 0, st,
-                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb));
+    MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
+                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units,
+                    counts + size_t(pb.nplanes) * pb.nseg, accumulate, pb,
+                    static_cast<int>(plane_records(problem)), static_cast<int>(plane_units(problem, pb))));
     MSDA_TRY(mark(ev, kStageGrad, st));
     MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, recs, cursor,
                                   static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, gout, static_cast<const uint3*>(recs),
+    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
+                                 gout, static_cast<const uint3*>(recs),
                                  static_cast<const int32_t*>(nunits),
                                  static_cast<const int4*>(units), gacc, st);
 }

@@ -65,7 +65,6 @@ constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 512;     // samples one gradient workgroup holds
 constexpr int kCountChunk = 4096;      // samples one counting workgroup bins
-constexpr int kScanThreads = 1024;
 
 // Corners of one row that a record covers.
 enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
@@ -268,75 +267,111 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
     }
 }
 
-// One workgroup.  counts -> cursor (exclusive prefix), the unit list
-// {segment, first record, end record, flush-with-atomics} and its length
-// (nunits[0]), and the list of segments split over several units
-// (nunits[1] entries of `multi`), whose rows the gradient kernel zeroes.
-// With `accumulate` every unit adds into the caller's buffer, which is then
-// left as it is (and no segment is listed).
-// The counts are walked in chunks of kScanChunk entries, each loaded into
-// LDS with coalesced reads; every lane scans kScanChunk / kScanThreads
-// consecutive entries.
-constexpr int kScanChunk = 8192;
+// One workgroup per plane (b, m).  Plane p owns a fixed record region
+// [p * plane_records, ...) and a fixed unit region [p * plane_units, ...), so
+// planes need no common prefix.  counts -> cursor (the plane's exclusive
+// prefix plus its region base), the plane's units {segment, first record,
+// end record, flush-with-atomics} and their number (nunits[p]), and the
+// plane's segments split over several units (nunits[nplanes + p] entries of
+// multi[p * nseg ...]), whose rows the gradient kernel zeroes.  With
+// `accumulate` every unit adds into the caller's buffer, which is then left
+// as it is (and no segment is listed).  Every lane scans kScanPer
+// consecutive segments; lanes combine through a wave scan and the wave
+// totals.  The last workgroup to finish (a ticket counter in the zeroed
+// counts area) writes the exclusive prefix of the planes' unit counts to
+// nunits[2 * nplanes ...], with the total at nunits[3 * nplanes], so that
+// the accumulation can walk all units in one dense order.
+constexpr int kScanPer = kMaxSegments / kBlock;
 
-__global__ void __launch_bounds__(kScanThreads)
+__global__ void __launch_bounds__(kBlock)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
-                     int accumulate, Problem pb) {
-    constexpr int kPer = kScanChunk / kScanThreads;
-    __shared__ int32_t s_cnt[kScanChunk];
-    __shared__ int32_t s_rec[kScanThreads], s_unit[kScanThreads];
-    __shared__ int32_t s_nmulti;
-    const int t = threadIdx.x;
-    const int n = pb.nplanes * pb.nseg;
+                     int32_t* __restrict__ ticket, int accumulate, Problem pb, int plane_records, int plane_units) {
+    __shared__ int32_t s_cnt[kMaxSegments];
+    __shared__ int32_t s_wrec[kBlock / 64], s_wunit[kBlock / 64];
+    __shared__ int32_t s_nmulti, s_last;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int pl = blockIdx.x, n = pb.nseg;
+    const int64_t cbase = static_cast<int64_t>(pl) * n;
     if (t == 0) s_nmulti = 0;
-    int run_rec = 0, run_unit = 0;
-    for (int c0 = 0; c0 < n; c0 += kScanChunk) {
-        const int cn = min(kScanChunk, n - c0);
-        for (int i = t; i < cn; i += kScanThreads) s_cnt[i] = counts[c0 + i];
-        __syncthreads();
-        int rsum = 0, usum = 0;
+    for (int i = t; i < n; i += kBlock) s_cnt[i] = counts[cbase + i];
+    __syncthreads();
+    int rsum = 0, usum = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = t * kPer + j;
-            if (i < cn) {
-                rsum += s_cnt[i];
-                usum += units_of(s_cnt[i]);
-            }
+    for (int j = 0; j < kScanPer; ++j) {
+        const int i = t * kScanPer + j;
+        if (i < n) {
+            rsum += s_cnt[i];
+            usum += units_of(s_cnt[i]);
         }
-        s_rec[t] = rsum;
-        s_unit[t] = usum;
+    }
+    int rinc = rsum, uinc = usum;                    // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int ru = __shfl_up(rinc, o, 64), uu = __shfl_up(uinc, o, 64);
+        if (lane >= o) {
+            rinc += ru;
+            uinc += uu;
+        }
+    }
+    if (lane == 63) {
+        s_wrec[wave] = rinc;
+        s_wunit[wave] = uinc;
+    }
+    __syncthreads();
+    int rbase = rinc - rsum, ubase = uinc - usum;
+    for (int w = 0; w < wave; ++w) {
+        rbase += s_wrec[w];
+        ubase += s_wunit[w];
+    }
+    rbase += pl * plane_records;
+    const int ufirst = pl * plane_units;
+#pragma unroll 1
+    for (int j = 0; j < kScanPer; ++j) {
+        const int i = t * kScanPer + j;
+        if (i >= n) break;
+        const int c = s_cnt[i], u = units_of(c);
+        const int gi = static_cast<int>(cbase) + i;
+        cursor[gi] = rbase;
+        const int atomic_flush = (u > 1 || accumulate) ? 1 : 0;
+        for (int k = 0; k < u; ++k)
+            units[ufirst + ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
+                                                  rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
+        if (u > 1 && !accumulate) multi[cbase + atomicAdd(&s_nmulti, 1)] = gi;
+        rbase += c;
+        ubase += u;
+    }
+    __syncthreads();
+    if (t == kBlock - 1) {
+        nunits[pl] = ubase;                          // the last lane's running count is the total
+        nunits[pb.nplanes + pl] = s_nmulti;
+        __threadfence();
+        s_last = atomicAdd(ticket, 1) == pb.nplanes - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every plane's count is written and visible: prefix over planes,
+    // kBlock planes per round
+    __threadfence();
+    int run = 0;
+    for (int p0 = 0; p0 < pb.nplanes; p0 += kBlock) {
+        const int p = p0 + t;
+        const int c = p < pb.nplanes ? __hip_atomic_load(nunits + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        int inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += up;
+        }
+        if (lane == 63) s_wunit[wave] = inc;
         __syncthreads();
-        for (int off = 1; off < kScanThreads; off <<= 1) {     // inclusive scan
-            const int a = t >= off ? s_rec[t - off] : 0;
-            const int u = t >= off ? s_unit[t - off] : 0;
-            __syncthreads();
-            s_rec[t] += a;
-            s_unit[t] += u;
-            __syncthreads();
-        }
-        int rbase = run_rec + s_rec[t] - rsum, ubase = run_unit + s_unit[t] - usum;
-        for (int j = 0; j < kPer; ++j) {
-            const int i = t * kPer + j;
-            if (i >= cn) break;
-            const int c = s_cnt[i], u = units_of(c), gi = c0 + i;
-            cursor[gi] = rbase;
-            const int atomic_flush = (u > 1 || accumulate) ? 1 : 0;
-            for (int k = 0; k < u; ++k)
-                units[ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
-                                             rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
-            if (u > 1 && !accumulate) multi[atomicAdd(&s_nmulti, 1)] = gi;
-            rbase += c;
-            ubase += u;
-        }
-        run_rec += s_rec[kScanThreads - 1];
-        run_unit += s_unit[kScanThreads - 1];
+        int base = run + inc - c;
+        for (int w = 0; w < wave; ++w) base += s_wunit[w];
+        if (p < pb.nplanes) nunits[2 * pb.nplanes + p] = base;
+        for (int w = 0; w < kBlock / 64; ++w) run += s_wunit[w];
         __syncthreads();
     }
-    if (t == 0) {
-        nunits[0] = run_unit;
-        nunits[1] = s_nmulti;
-    }
+    if (t == 0) nunits[3 * pb.nplanes] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -525,16 +560,20 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                 ++k;
                             });
         }
-        const int nm = nunits[1];
-        for (int e = blockIdx.x; e < nm; e += gridDim.x) zero_segment(pb, gacc, multi[e], threadIdx.x, blockDim.x);
+        // this plane's multi-unit segments, spread over the plane's workgroups
+        const int nm = nunits[pb.nplanes + t.pl];
+        const int nqc = (pb.Q + gpb - 1) / gpb;
+        for (int e = t.q0 / gpb; e < nm; e += nqc)
+            zero_segment(pb, gacc, multi[static_cast<int64_t>(t.pl) * pb.nseg + e], threadIdx.x, blockDim.x);
     }
 }
 
 // ---------------------------------------------------------------------------
 // 4. accumulate
 // ---------------------------------------------------------------------------
-// Grid: an upper bound on the unit count, kAccBlock lanes; workgroups past
-// nunits exit.  LDS: the segment tile (keys * D floats), the unit's records
+// Grid: nplanes * plane_units (the bound), kAccBlock lanes; workgroups past
+// the total unit count exit, and the others take the units of all planes in
+// plane order, remapped so that each XCD gets a contiguous run.  LDS: the segment tile (keys * D floats), the unit's records
 // sorted by key (kUnitRecords weight pairs and keys, padded), 2 * kMaxSegKeys
 // int32.
 constexpr int kAccBlock = 512;
@@ -552,15 +591,27 @@ template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(kAccBlock, DT == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits,
-                       const int4* __restrict__ units, float* __restrict__ gacc, Problem pb) {
+                       const int4* __restrict__ units, float* __restrict__ gacc, Problem pb, int plane_units) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr int NW = kAccBlock / LPR;              // workers
-    const int nu = nunits[0];
-    if (static_cast<int>(blockIdx.x) >= nu) return;
     // consecutive units (neighbouring segments of one plane) run on one XCD,
     // so the plane's grad_output rows they gather stay in that XCD's L2
-    const int4 unit = units[xcd_tile(blockIdx.x, nu)];
+    const int np = pb.nplanes, total = nunits[3 * np];
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    // workgroups 0 .. total-1 cover the units; each XCD gets a contiguous run
+    const int r = static_cast<int>(xcd_tile(blockIdx.x, total));
+    // the unit's plane: the number of planes whose first unit is <= r, less
+    // one, counted 64 planes per load with a ballot
+    const int lane = threadIdx.x & 63;
+    int lo = -1;
+    for (int c0 = 0; c0 < np; c0 += 64) {
+        const int v = c0 + lane < np ? nunits[2 * np + c0 + lane] : 0x7fffffff;
+        const int k = __popcll(__ballot(v <= r));
+        lo += k;
+        if (k < 64) break;
+    }
+    const int4 unit = units[static_cast<int64_t>(lo) * plane_units + (r - nunits[2 * np + lo])];
     const int pl = unit.x / pb.nseg, seg = unit.x - pl * pb.nseg;
     const int b = pl / pb.M, m = pl - b * pb.M;
     const int lvl = level_of_segment(pb, seg);
