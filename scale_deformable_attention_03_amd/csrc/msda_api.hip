@@ -322,7 +322,7 @@ struct Accum {
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
                            sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
-        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::kAccBlock, lds, st,
+        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::acc_block(LPR), lds, st,
                       gout, recs, nunits, units, gacc, pb, plane_units);
     }
 };

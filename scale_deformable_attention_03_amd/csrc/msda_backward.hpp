@@ -571,13 +571,15 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // ---------------------------------------------------------------------------
 // 4. accumulate
 // ---------------------------------------------------------------------------
-// Grid: nplanes * plane_units (the bound), kAccBlock lanes; workgroups past
+// Grid: nplanes * plane_units (the bound), acc_block(LPR) lanes; workgroups past
 // the total unit count exit, and the others take the units of all planes in
 // plane order, remapped so that each XCD gets a contiguous run.  LDS: the segment tile (keys * D floats), the unit's records
 // sorted by key (kUnitRecords weight pairs and keys, padded), 2 * kMaxSegKeys
 // int32.
-constexpr int kAccBlock = 512;
-constexpr int kAccPerLane = kUnitRecords / kAccBlock;
+// 64 workers of LPR lanes (at most 1024 lanes): the number of slice
+// boundaries per unit, and so the LDS compare-and-swap work, stays the same
+// for every row width.
+constexpr int acc_block(int lpr) { return 64 * lpr < 1024 ? 64 * lpr : 1024; }
 // Sorted record i: key at word i + 4 * (i / 32), weight pair at pair slot
 // i + 2 * (i / 32).  Workers start 8-aligned batches about 32 records apart
 // and read them with 16-byte vector reads; the padding keeps those reads
@@ -588,12 +590,14 @@ __device__ __forceinline__ int key_slot(int i) { return i + 4 * (i >> 5); }
 __device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 
 template <int DT, int VECB, int LPR>
-__global__ void __launch_bounds__(kAccBlock, DT == kF32 ? 6 : 5)
+__global__ void __launch_bounds__(acc_block(LPR), DT == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits,
                        const int4* __restrict__ units, float* __restrict__ gacc, Problem pb, int plane_units) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
+    constexpr int kAccBlock = acc_block(LPR);
+    constexpr int kAccPerLane = kUnitRecords / kAccBlock;
     constexpr int NW = kAccBlock / LPR;              // workers
     // consecutive units (neighbouring segments of one plane) run on one XCD,
     // so the plane's grad_output rows they gather stay in that XCD's L2
