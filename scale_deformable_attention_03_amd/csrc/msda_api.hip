@@ -135,8 +135,8 @@ msda::Problem pack(const msda_problem_t* p) {
 }
 
 // The binned backward needs: query indices within the record's 24-bit
-// field, at most kMaxSegments segments per plane, record positions and unit
-// counts within int32.
+// field, level extents within the 16-bit cell fields, at most kMaxSegments
+// segments per plane, record positions and unit counts within int32.
 int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
 
 // Per plane: at most 4 records per sample, so a fixed region of
@@ -149,6 +149,9 @@ int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
 }
 
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
+    for (int l = 0; l < p->num_levels; ++l)
+        if (p->spatial_shapes[2 * l] > msda::kMaxBinnedExtent || p->spatial_shapes[2 * l + 1] > msda::kMaxBinnedExtent)
+            return false;
     return p->num_queries < (1 << msda::kQueryBits) && pb.nseg <= msda::kMaxSegments &&
            max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * plane_units(p, pb) < kIndexLimit / 2;
 }
@@ -296,10 +299,8 @@ struct Grad {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
-        size_t lds = sizeof(uint32_t) * gpb * (12 * LP + 4);
-        if (binned)
-            lds += sizeof(int32_t) * (2 * size_t(pb.nseg) + (pb.nseg & 1)) + sizeof(int2) * gpb * LP +
-                   sizeof(uint16_t) * gpb * LP * 4;
+        size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4);
+        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg);
         const void* k;
         if (binned)
             k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)

@@ -60,10 +60,11 @@ namespace msda {
 //         segment), each w * (1-ly or ly) * (1-lx or lx)
 constexpr int kQueryBits = 24;         // queries per plane for the binned path
 constexpr int kMaxSegKeys = 256;       // keys per segment (8-bit key field)
-constexpr int kNoCell = -0x40000000;   // cell marker of a sample off the map
+constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the map
 constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
-constexpr int kMaxWgSamples = 512;     // samples one gradient workgroup holds
+constexpr int kMaxWgSamples = 1024;    // samples one gradient workgroup holds
+constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path (16-bit cell fields)
 constexpr int kCountChunk = 4096;      // samples one counting workgroup bins
 
 // Corners of one row that a record covers.
@@ -379,15 +380,16 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 // ---------------------------------------------------------------------------
 // Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes, plane-local
 // as in the forward.  A prologue (one lane per sample) stores each sample's
-// corner offsets, bilinear fractions and gradient scales in LDS (12 words)
-// and ranks its records within their segments; the main loop gathers the
-// four corner rows of each sample, forms the four dot products with the
-// query's grad_output row and reduces them over the group's lanes; when
-// BINNED, an epilogue reserves the workgroup's record ranges and writes the
-// records, and workgroup i zeroes the rows of the multi-unit segments i,
-// i + gridDim.x, ... of the scan's list (the accumulation adds into them).
-// LDS: gpb * (12 * L * P + 4) words; when BINNED also nseg histogram and
-// nseg bases (int32) and 4 record ranks per sample (uint16).
+// corner offsets, fractions lx, ly, attention weight and packed cell
+// (x0 + 1, y0 + 1) in LDS (8 words; hx, hy and the weight products are
+// recomputed from them with the same roundings) and counts its records per
+// segment; the main loop gathers the four corner rows of each sample, forms
+// the four dot products with the query's grad_output row and reduces them
+// over the group's lanes; when BINNED, an epilogue reserves the workgroup's
+// record ranges, writes the records, and has the plane's workgroups zero the
+// rows of the plane's multi-unit segments (the accumulation adds into them).
+// LDS: gpb * (8 * L * P + 4) words; when BINNED also 2 * nseg int32 (counts,
+// then cursors, and bases).
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
@@ -401,14 +403,12 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
     const int LP = L * P;
-    const int gstride = 12 * LP + 4;
+    const int gstride = 8 * LP + 4;
 
     extern __shared__ uint32_t sm[];
     uint32_t* srec = sm;
     int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);
     int32_t* lbase = lhist + pb.nseg;
-    int2* lxy = reinterpret_cast<int2*>(lbase + pb.nseg + (pb.nseg & 1));   // cell of each sample
-    uint16_t* lrank = reinterpret_cast<uint16_t*>(lxy + gpb * LP);
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
@@ -425,20 +425,16 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const float2 xy = load_pair<DT>(loc, si);
         const Corners c = sample_corners(xy.x, xy.y, H, W, pb.lv.start[l], pitch);
         const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
-        uint32_t* r = srec + g * gstride + lp * 12;
+        uint32_t* r = srec + g * gstride + lp * 8;
+        const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
+                                   : kNoCell;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
-        *reinterpret_cast<float4*>(r + 4) = make_float4(c.hx, c.lx, c.hy, c.ly);
-        *reinterpret_cast<float4*>(r + 8) = make_float4(static_cast<float>(W) * aw, static_cast<float>(H) * aw,
-                                                        aw * c.hy, aw * c.ly);
+        *reinterpret_cast<uint4*>(r + 4) = make_uint4(__float_as_uint(c.lx), __float_as_uint(c.ly),
+                                                      __float_as_uint(aw), cell);
         if constexpr (BINNED) {
-            lxy[i] = make_int2(c.ok ? c.x0 : kNoCell, c.y0);
-            if (c.ok) {
-                int k = 0;
-                for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l], [&](int seg, int, int, int) {
-                    lrank[4 * i + k] = static_cast<uint16_t>(atomicAdd(&lhist[seg], 1));
-                    ++k;
-                });
-            }
+            if (c.ok)
+                for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+                                [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
         }
     }
     __syncthreads();
@@ -475,7 +471,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 Raw<VECB> raw[kSB][4];
 #pragma unroll
                 for (int u = 0; u < kSB; ++u) {
-                    o[u] = *reinterpret_cast<const uint4*>(rec + (c0 + b0 + u) * 12);
+                    o[u] = *reinterpret_cast<const uint4*>(rec + (c0 + b0 + u) * 8);
                     raw[u][0] = buffer_load<VECB>(vr, o[u].x + lane_b);
                     raw[u][1] = buffer_load<VECB>(vr, o[u].y + lane_b);
                     raw[u][2] = buffer_load<VECB>(vr, o[u].z + lane_b);
@@ -484,8 +480,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 #pragma unroll
                 for (int u = 0; u < kSB; ++u) {
                     const int lp = c0 + b0 + u;
-                    const float4 f = *reinterpret_cast<const float4*>(rec + lp * 12 + 4);    // hx lx hy ly
-                    const float4 sc = *reinterpret_cast<const float4*>(rec + lp * 12 + 8);   // W*w H*w w*hy w*ly
+                    const float4 fr = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);    // lx ly w cell
+                    const float4 f = make_float4(1.0f - fr.x, fr.x, 1.0f - fr.y, fr.y);      // hx lx hy ly
+                    const float wy0 = fr.z * f.z, wy1 = fr.z * f.w;                          // w*hy w*ly
                     float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
                     widen<DT, VECB>(raw[u][0], v00);
                     widen<DT, VECB>(raw[u][1], v01);
@@ -502,13 +499,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     if constexpr (!BINNED) {
                         if (active) {
                             if (o[u].x != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, sc.z * f.x * g[i]);
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, wy0 * f.x * g[i]);
                             if (o[u].y != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, sc.z * f.y * g[i]);
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, wy0 * f.y * g[i]);
                             if (o[u].z != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, sc.w * f.x * g[i]);
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, wy1 * f.x * g[i]);
                             if (o[u].w != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, sc.w * f.y * g[i]);
+                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, wy1 * f.y * g[i]);
                         }
                     }
                     const float top = f.x * d00 + f.y * d01;
@@ -520,9 +517,10 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     // zero gradients, whatever grad_output holds
                     const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
                     if (li == b0 + u) {
+                        const int l = lp / P;                // uniform across the wave
                         own_w = off ? 0.0f : sw;
-                        own_x = off ? 0.0f : sx * sc.x;
-                        own_y = off ? 0.0f : sy * sc.y;
+                        own_x = off ? 0.0f : sx * (static_cast<float>(pb.lv.W[l]) * fr.z);
+                        own_y = off ? 0.0f : sy * (static_cast<float>(pb.lv.H[l]) * fr.z);
                     }
                 }
             }
@@ -535,29 +533,31 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     }
     if constexpr (BINNED) {
         __syncthreads();
-        for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x)
+        for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) {
             if (lhist[i] != 0) lbase[i] = atomicAdd(&cursor[static_cast<int64_t>(t.pl) * pb.nseg + i], lhist[i]);
+            lhist[i] = 0;                            // reused as the record cursor
+        }
         __syncthreads();
-        // records, from the prologue's cell and weights in LDS, at base + rank
+        // records, from the prologue's cell and weights in LDS, at base + a
+        // slot taken from the segment's cursor
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-            const int2 cell = lxy[i];
-            if (cell.x == kNoCell) continue;
             const int g = i / LP, lp = i - g * LP, l = lp / P;
+            const uint32_t* r = srec + g * gstride + lp * 8;
+            const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
+            const uint32_t cell = __float_as_uint(fr.w);
+            if (cell == kNoCell) continue;
             const int H = pb.lv.H[l], W = pb.lv.W[l];
-            const uint32_t* r = srec + g * gstride + lp * 12;
-            const float4 f = *reinterpret_cast<const float4*>(r + 4);     // hx lx hy ly
-            const float4 sc = *reinterpret_cast<const float4*>(r + 8);    // W*w H*w w*hy w*ly
+            const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
+            const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
             const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
-            int k = 0;
-            for_each_record(cell.x, cell.y, W, H, pb.seg_shift[l], pb.seg_base[l],
-                            [&](int seg, int key, int row, int mode) {
-                                const float wy = row ? sc.w : sc.z;
-                                const float cl = wy * f.x, cr = wy * f.y;
-                                const int pos = lbase[seg] + lrank[4 * i + k];
+            for_each_record(static_cast<int>(cell & 0xffffu) - 1, static_cast<int>(cell >> 16) - 1, W, H,
+                            pb.seg_shift[l], pb.seg_base[l], [&](int seg, int key, int row, int mode) {
+                                const float wy = row ? wy1 : wy0;
+                                const float cl = wy * hx, cr = wy * fr.x;
+                                const int pos = lbase[seg] + atomicAdd(&lhist[seg], 1);
                                 recs[pos] = make_uint3(qk | static_cast<uint32_t>(key),
                                                        __float_as_uint(mode == kRightOnly ? cr : cl),
                                                        __float_as_uint(mode == kBoth ? cr : 0.0f));
-                                ++k;
                             });
         }
         // this plane's multi-unit segments, spread over the plane's workgroups
