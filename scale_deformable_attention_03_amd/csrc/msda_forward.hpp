@@ -130,10 +130,12 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
-    constexpr int kSB = L_CT && P_CT && (L_CT * P_CT) % 4 == 0 ? 4 : 1;   // samples whose loads fly together
-    // 16-bit values widen to twice the registers; unrolling further than
-    // two batches there costs occupancy
-    constexpr int kUnroll = E == 4 ? 4 : 2;
+    // samples whose loads fly together; bf16 widens each element with its own
+    // shift or mask, so fewer of its rows are held at once
+    constexpr int kSBMax = DT == kBF16 ? 2 : 4;
+    constexpr int kSB = L_CT && P_CT && (L_CT * P_CT) % kSBMax == 0 ? kSBMax : 1;
+    // 16-bit values widen to twice the registers: at most two batches unrolled
+    constexpr int kUnroll = E == 4 ? 4 : (DT == kF16 ? 2 : 1);
 #pragma unroll kUnroll
     for (int lp0 = 0; lp0 < LP; lp0 += kSB) {
         float4 w[kSB];
@@ -149,13 +151,27 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         }
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
-            float v0[VEC], v1[VEC], v2[VEC], v3[VEC];
-            widen<DT, VECB>(raw[u][0], v0);
-            widen<DT, VECB>(raw[u][1], v1);
-            widen<DT, VECB>(raw[u][2], v2);
-            widen<DT, VECB>(raw[u][3], v3);
+            if constexpr (DT == kBF16) {
+                // one corner row at a time: each widened element feeds its FMA
+                // at once, so few widened values are live together
+                const float wc[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] += w[u].x * v0[i] + w[u].y * v1[i] + w[u].z * v2[i] + w[u].w * v3[i];
+                for (int c = 0; c < 4; ++c) {
+                    float v[VEC];
+                    widen<DT, VECB>(raw[u][c], v);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] += wc[c] * v[i];
+                }
+            } else {
+                float v0[VEC], v1[VEC], v2[VEC], v3[VEC];
+                widen<DT, VECB>(raw[u][0], v0);
+                widen<DT, VECB>(raw[u][1], v1);
+                widen<DT, VECB>(raw[u][2], v2);
+                widen<DT, VECB>(raw[u][3], v3);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    acc[i] += w[u].x * v0[i] + w[u].y * v1[i] + w[u].z * v2[i] + w[u].w * v3[i];
+            }
         }
     }
     const int64_t G = t.G0 + static_cast<int64_t>(lg) * pb.M;
