@@ -461,7 +461,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // them after the chunk, so a group's stores are contiguous.  Within a
         // chunk, kSB samples' corner loads are in flight together.
         constexpr int kC = kFixedLP ? (LPR < L_CT * P_CT ? LPR : L_CT * P_CT) : 1;
-        constexpr int kSB = kC % 4 == 0 ? 4 : 1;
+        // (two for float32, whose occupancy then doubles; four for 16-bit rows)
+        constexpr int kSBMax = E == 4 ? 2 : 4;
+        constexpr int kSB = kC % kSBMax == 0 ? kSBMax : 1;
 #pragma unroll 1
         for (int c0 = 0; c0 < LP; c0 += kC) {
             float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f;
