@@ -210,6 +210,8 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
     const int pl = blockIdx.x / nchunks, chunk = blockIdx.x - pl * nchunks;
     const int b = pl / pb.M, m = pl - b * pb.M;
 
+    __shared__ int4 s_lv[kMaxLevels];
+    stage_levels(pb, s_lv);
     for (int i = threadIdx.x; i < pb.nseg; i += kBlock) hist[i] = 0;
     __syncthreads();
     const int s_end = min((chunk + 1) * kCountChunk, nsamp);
@@ -233,11 +235,12 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
             const int s = s0 + u * kBlock;
             if (s >= s_end) break;
             const int lp = s % LP, l = lp / P;
-            const int H = pb.lv.H[l], W = pb.lv.W[l];
+            const int4 lv = s_lv[l];
+            const int H = lv.x, W = lv.y;
             float x, y;
             if (!pixel_coords(lx[u], ly[u], static_cast<float>(W), static_cast<float>(H), x, y)) continue;
             const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
-            for_each_record(x0, y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+            for_each_record(x0, y0, W, H, lv.w & 0xff, lv.w >> 8,
                             [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
         }
     }
@@ -412,18 +415,20 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
-    if constexpr (BINNED) {
+    __shared__ int4 s_lv[kMaxLevels];
+    stage_levels(pb, s_lv);
+    if constexpr (BINNED)
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) lhist[i] = 0;
-        __syncthreads();
-    }
+    __syncthreads();
 
     // prologue: one lane per sample
     for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-        const int H = pb.lv.H[l], W = pb.lv.W[l];
+        const int4 lv = s_lv[l];
+        const int H = lv.x, W = lv.y;
         const float2 xy = load_pair<DT>(loc, si);
-        const Corners c = sample_corners(xy.x, xy.y, H, W, pb.lv.start[l], pitch);
+        const Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
         const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         uint32_t* r = srec + g * gstride + lp * 8;
         const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
@@ -433,7 +438,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                                       __float_as_uint(aw), cell);
         if constexpr (BINNED) {
             if (c.ok)
-                for_each_record(c.x0, c.y0, W, H, pb.seg_shift[l], pb.seg_base[l],
+                for_each_record(c.x0, c.y0, W, H, lv.w & 0xff, lv.w >> 8,
                                 [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
         }
     }
@@ -548,12 +553,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
             const uint32_t cell = __float_as_uint(fr.w);
             if (cell == kNoCell) continue;
-            const int H = pb.lv.H[l], W = pb.lv.W[l];
+            const int4 lv = s_lv[l];
+            const int H = lv.x, W = lv.y;
             const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
             const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
             const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
             for_each_record(static_cast<int>(cell & 0xffffu) - 1, static_cast<int>(cell >> 16) - 1, W, H,
-                            pb.seg_shift[l], pb.seg_base[l], [&](int seg, int key, int row, int mode) {
+                            lv.w & 0xff, lv.w >> 8, [&](int seg, int key, int row, int mode) {
                                 const float wy = row ? wy1 : wy0;
                                 const float cl = wy * hx, cr = wy * fr.x;
                                 const int pos = lbase[seg] + atomicAdd(&lhist[seg], 1);

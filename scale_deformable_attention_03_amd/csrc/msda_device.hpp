@@ -45,6 +45,17 @@ struct Problem {
     int32_t seg_base[kMaxLevels + 1];
 };
 
+// ---- per-level table in LDS ------------------------------------------------
+
+// Per-sample code indexes the level table with a per-lane level, which from
+// kernel arguments would be a vector memory load per sample; a workgroup
+// copies the table into LDS once instead.  Row l: (H, W, start, seg), seg =
+// segment shift | first segment << 8.
+__device__ __forceinline__ void stage_levels(const Problem& pb, int4* lt) {
+    for (int l = threadIdx.x; l < pb.L; l += blockDim.x)
+        lt[l] = make_int4(pb.lv.H[l], pb.lv.W[l], pb.lv.start[l], pb.seg_shift[l] | (pb.seg_base[l] << 8));
+}
+
 // ---- scalar conversions --------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -106,13 +106,17 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     extern __shared__ uint32_t sm[];
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
+    __shared__ int4 s_lv[kMaxLevels];
+    stage_levels(pb, s_lv);
+    __syncthreads();
 
     // prologue: one lane per sample
     for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
         const float2 xy = load_pair<DT>(loc, si);
-        const Corners c = sample_corners(xy.x, xy.y, pb.lv.H[l], pb.lv.W[l], pb.lv.start[l], pitch);
+        const int4 lv = s_lv[l];
+        const Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
         const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         const float wy0 = aw * c.hy, wy1 = aw * c.ly;
         uint32_t* r = sm + g * gstride + lp * 8;
