@@ -317,14 +317,14 @@ template <int DT, int VECB, int LPR>
 struct Accum {
     static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
                              const uint3* recs, const int32_t* nunits, const int4* units, float* gacc,
-                             hipStream_t st) {
+                             void* gfinal, hipStream_t st) {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
                            sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
         return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::acc_block(LPR), lds, st,
-                      gout, recs, nunits, units, gacc, pb, plane_units);
+                      gout, recs, nunits, units, gacc, gfinal, pb, plane_units);
     }
 };
 
@@ -362,11 +362,16 @@ msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
     return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
 }
 
-// The backward into the float32 buffer gacc.  accumulate = 0: gacc is
-// overwritten in full; accumulate = 1: gacc is added to.
+// The backward.  accumulate = 1: grad_value is added into the float32
+// buffer gacc (gfinal unused).  accumulate = 0: grad_value is overwritten
+// into gfinal, the caller's tensor of the problem's dtype; gacc is gfinal for
+// float32 and the workspace's float32 buffer for 16-bit dtypes, which then
+// holds only rows the kernels add into (and is rounded into gfinal at the
+// end).
 msda_status_t backward_into(const msda_problem_t* problem, const void* value, const void* loc,
-                            const void* w, const void* gout, float* gacc, void* gloc, void* gw,
+                            const void* w, const void* gout, float* gacc, void* gfinal, void* gloc, void* gw,
                             char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
+    const bool narrow16 = !accumulate && problem->dtype != MSDA_F32;
     const msda::Problem pb = pack(problem);
     const Layout lay = layout(problem, pb);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
@@ -378,9 +383,19 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
-                                      static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
-                                      static_cast<const int32_t*>(nullptr), gloc, gw, st));
-        return mark(ev, kStageAccum, st);
+                                      static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
+                                      static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                                      gloc, gw, st));
+        MSDA_TRY(mark(ev, kStageAccum, st));
+        MSDA_TRY(mark(ev, kStageNarrow, st));
+        if (narrow16) {
+            const int64_t n8 = value_elems(problem) / 8;
+            const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
+                                                       : kfn(&msda::msda_narrow_kernel<kBF16>);
+            MSDA_TRY(launch(k, fill_blocks(n8), kBlock, 0, st, reinterpret_cast<const float4*>(gacc),
+                            static_cast<uint4*>(gfinal), n8));
+        }
+        return MSDA_SUCCESS;
     }
     int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
@@ -407,10 +422,18 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
                                   static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    return by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
-                                 gout, static_cast<const uint3*>(recs),
-                                 static_cast<const int32_t*>(nunits),
-                                 static_cast<const int4*>(units), gacc, st);
+    MSDA_TRY(by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
+                                   gout, static_cast<const uint3*>(recs), static_cast<const int32_t*>(nunits),
+                                   static_cast<const int4*>(units), gacc, narrow16 ? gfinal : nullptr, st));
+    MSDA_TRY(mark(ev, kStageNarrow, st));
+    if (narrow16) {
+        const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_segments_kernel<kF16>)
+                                                   : kfn(&msda::msda_narrow_segments_kernel<kBF16>);
+        MSDA_TRY(launch(k, int64_t(pb.nplanes) * msda::kNarrowPerPlane, kBlock, 0, st,
+                        static_cast<const float*>(gacc), gfinal, static_cast<const int32_t*>(nunits),
+                        static_cast<const int32_t*>(multi), pb));
+    }
+    return MSDA_SUCCESS;
 }
 
 msda_status_t backward_call(const msda_problem_t* problem, const void* value, const void* sampling_locations,
@@ -431,16 +454,8 @@ msda_status_t backward_call(const msda_problem_t* problem, const void* value, co
     const Layout lay = layout(problem, pack(problem));
     float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
                                              : reinterpret_cast<float*>(ws + lay.acc);
-    MSDA_TRY(backward_into(problem, value, sampling_locations, attention_weights, grad_output, gacc,
+    MSDA_TRY(backward_into(problem, value, sampling_locations, attention_weights, grad_output, gacc, grad_value,
                            grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
-    MSDA_TRY(mark(ev, kStageNarrow, stream));
-    if (problem->dtype != MSDA_F32) {
-        const int64_t n8 = nv / 8;
-        const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
-                                                   : kfn(&msda::msda_narrow_kernel<kBF16>);
-        MSDA_TRY(launch(k, fill_blocks(n8), kBlock, 0, stream, reinterpret_cast<const float4*>(gacc),
-                        static_cast<uint4*>(grad_value), n8));
-    }
     return mark(ev, kStageEnd, stream);
 }
 
@@ -520,7 +535,7 @@ msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void
         MSDA_TRY(check_ptr(workspace, 1));
     }
     if (value_elems(problem) == 0) return MSDA_SUCCESS;
-    return backward_into(problem, value, sampling_locations, attention_weights, grad_output, grad_value_acc,
+    return backward_into(problem, value, sampling_locations, attention_weights, grad_output, grad_value_acc, nullptr,
                          grad_sampling_locations, grad_attention_weights, static_cast<char*>(workspace), 1,
                          nullptr, stream);
 }

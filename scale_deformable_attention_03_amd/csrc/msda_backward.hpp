@@ -271,6 +271,42 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
     }
 }
 
+// Round the float32 rows of plane-global segment `gs` to dtype DT into
+// `out`, 8 elements per lane step, lanes t, t+nt, ...
+template <int DT>
+__device__ void narrow_segment(const Problem& pb, const float* gacc, void* out, int gs, int t, int nt) {
+    const int pl = gs / pb.nseg, seg = gs - pl * pb.nseg;
+    const int b = pl / pb.M, m = pl - b * pb.M;
+    const int l = level_of_segment(pb, seg);
+    const int k0 = (seg - pb.seg_base[l]) << pb.seg_shift[l];
+    const int nk = min(1 << pb.seg_shift[l], pb.lv.H[l] * pb.lv.W[l] - k0);
+    const int d8 = pb.D / 8;
+    for (int i = t; i < nk * d8; i += nt) {
+        const int k = i / d8, c = i - k * d8;
+        const int64_t e = ((static_cast<int64_t>(b) * pb.K + pb.lv.start[l] + k0 + k) * pb.M + m) * pb.D + 8 * c;
+        const float4 a = *reinterpret_cast<const float4*>(gacc + e);
+        const float4 z = *reinterpret_cast<const float4*>(gacc + e + 4);
+        const float f[8] = {a.x, a.y, a.z, a.w, z.x, z.y, z.z, z.w};
+        const Raw<16> r = narrow<DT, 16>(f);
+        *reinterpret_cast<uint4*>(static_cast<char*>(out) + e * 2) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    }
+}
+
+// 16-bit dtypes: the rows of the segments split over several units (the
+// only rows the accumulation leaves in the float32 workspace), rounded into
+// grad_value.  Grid: nplanes * kNarrowPerPlane workgroups.
+constexpr int kNarrowPerPlane = 8;
+
+template <int DT>
+__global__ void __launch_bounds__(kBlock)
+msda_narrow_segments_kernel(const float* __restrict__ gacc, void* __restrict__ out,
+                            const int32_t* __restrict__ nunits, const int32_t* __restrict__ multi, Problem pb) {
+    const int pl = blockIdx.x / kNarrowPerPlane, sub = blockIdx.x - pl * kNarrowPerPlane;
+    const int nm = nunits[pb.nplanes + pl];
+    for (int e = sub; e < nm; e += kNarrowPerPlane)
+        narrow_segment<DT>(pb, gacc, out, multi[static_cast<int64_t>(pl) * pb.nseg + e], threadIdx.x, kBlock);
+}
+
 // One workgroup per plane (b, m).  Plane p owns a fixed record region
 // [p * plane_records, ...) and a fixed unit region [p * plane_units, ...), so
 // planes need no common prefix.  counts -> cursor (the plane's exclusive
@@ -601,7 +637,8 @@ template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(acc_block(LPR), DT == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits,
-                       const int4* __restrict__ units, float* __restrict__ gacc, Problem pb, int plane_units) {
+                       const int4* __restrict__ units, float* __restrict__ gacc, void* __restrict__ gfinal,
+                       Problem pb, int plane_units) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr int kAccBlock = acc_block(LPR);
@@ -782,20 +819,31 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
 
     // Write the segment's rows: row k is key start + k0 + k of plane (b, m).
     // A segment split over several units adds with float atomics, lane i on
-    // element i of a row (the lane-contiguous pattern); otherwise one 16-byte
-    // store per lane.
+    // element i of a row (the lane-contiguous pattern), into the float32
+    // buffer gacc.  Otherwise the rows are complete: one 16-byte store per
+    // lane, float32 into gacc, or for 16-bit dtypes 8 elements rounded once
+    // straight into grad_value (gfinal).
     const int64_t row0 = (static_cast<int64_t>(b) * pb.K + pb.lv.start[lvl] + k0) * pb.M + m;
     if (unit.w) {
         for (int i = threadIdx.x; i < nk * D; i += kAccBlock) {
             const int k = i / D, d = i - k * D;
             atomic_add_f32(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + d, tile[i]);
         }
-    } else {
+    } else if constexpr (DT == kF32) {
         const int q4 = D / 4;
         for (int i = threadIdx.x; i < nk * q4; i += kAccBlock) {
             const int k = i / q4, c4 = i - k * q4;
             *reinterpret_cast<float4*>(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + 4 * c4) =
                 *reinterpret_cast<const float4*>(tile + k * D + 4 * c4);
+        }
+    } else {
+        const int q8 = D / 8;
+        for (int i = threadIdx.x; i < nk * q8; i += kAccBlock) {
+            const int k = i / q8, c8 = i - k * q8;
+            const float* src = tile + k * D + 8 * c8;
+            const Raw<16> r = narrow<DT, 16>(src);
+            const int64_t e = (row0 + static_cast<int64_t>(k) * pb.M) * D + 8 * c8;
+            *reinterpret_cast<uint4*>(static_cast<char*>(gfinal) + e * 2) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
         }
     }
 }
