@@ -174,12 +174,13 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
     if (w.binned) {
         const int64_t nbins = int64_t(pb.nplanes) * pb.nseg;
         w.max_units = int64_t(pb.nplanes) * plane_units(p, pb);
-        w.counts = off;          // nbins counts, then the scan's ticket counter
-        off += round_up(nbins * 4 + 4);
+        w.counts = off;
+        off += round_up(nbins * 4);
         w.cursor = off;
         off += round_up(nbins * 4);
-        // [p] units of plane p, [nplanes + p] its multi-unit segments,
-        // [2 nplanes + p] units before plane p, [3 nplanes] all units
+        // [p] units of plane p, [nplanes + p] its multi-unit segments (both
+        // from the scan), [2 nplanes + p] units before plane p and
+        // [3 nplanes] all units (from the gradient kernel)
         w.nunits = off;
         off += round_up((size_t(pb.nplanes) * 3 + 1) * 4);
         w.multi = off;
@@ -294,8 +295,8 @@ struct Fwd {
 template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
-                             const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor, const int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
-                             hipStream_t st) {
+                             const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor,
+                             int32_t* nunits, const int32_t* multi, void* gloc, void* gw, hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
@@ -372,6 +373,14 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
                             const void* w, const void* gout, float* gacc, void* gfinal, void* gloc, void* gw,
                             char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
     const bool narrow16 = !accumulate && problem->dtype != MSDA_F32;
+    if (sample_elems(problem) == 0) {
+        // no samples (Q = 0): grad_value is zero and nothing else is written
+        MSDA_TRY(mark(ev, kStageZero, st));
+        if (!accumulate)
+            MSDA_TRY(zero_bytes(gfinal, size_t(value_elems(problem)) * (problem->dtype == MSDA_F32 ? 4 : 2), st));
+        for (int stage = kStageCount; stage <= kStageNarrow; ++stage) MSDA_TRY(mark(ev, stage, st));
+        return MSDA_SUCCESS;
+    }
     const msda::Problem pb = pack(problem);
     const Layout lay = layout(problem, pb);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
@@ -384,7 +393,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
                                       static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
-                                      static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                                      static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
                                       gloc, gw, st));
         MSDA_TRY(mark(ev, kStageAccum, st));
         MSDA_TRY(mark(ev, kStageNarrow, st));
@@ -405,7 +414,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     uint3* recs = reinterpret_cast<uint3*>(ws + lay.recs);
 
     MSDA_TRY(mark(ev, kStageZero, st));
-    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4 + 4), st));
+    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
     MSDA_TRY(mark(ev, kStageCount, st));
     switch (problem->dtype) {
         case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, loc, counts, st)); break;
@@ -414,12 +423,11 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     }
     MSDA_TRY(mark(ev, kStageScan, st));
     MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
-                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units,
-                    counts + size_t(pb.nplanes) * pb.nseg, accumulate, pb,
+                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb,
                     static_cast<int>(plane_records(problem)), static_cast<int>(plane_units(problem, pb))));
     MSDA_TRY(mark(ev, kStageGrad, st));
     MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, recs, cursor,
-                                  static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), gloc, gw,
+                                  nunits, static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
     MSDA_TRY(by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),

@@ -317,19 +317,16 @@ msda_narrow_segments_kernel(const float* __restrict__ gacc, void* __restrict__ o
 // `accumulate` every unit adds into the caller's buffer, which is then left
 // as it is (and no segment is listed).  Every lane scans kScanPer
 // consecutive segments; lanes combine through a wave scan and the wave
-// totals.  The last workgroup to finish (a ticket counter in the zeroed
-// counts area) writes the exclusive prefix of the planes' unit counts to
-// nunits[2 * nplanes ...], with the total at nunits[3 * nplanes], so that
-// the accumulation can walk all units in one dense order.
+// totals.
 constexpr int kScanPer = kMaxSegments / kBlock;
 
 __global__ void __launch_bounds__(kBlock)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
-                     int32_t* __restrict__ ticket, int accumulate, Problem pb, int plane_records, int plane_units) {
+                     int accumulate, Problem pb, int plane_records, int plane_units) {
     __shared__ int32_t s_cnt[kMaxSegments];
     __shared__ int32_t s_wrec[kBlock / 64], s_wunit[kBlock / 64];
-    __shared__ int32_t s_nmulti, s_last;
+    __shared__ int32_t s_nmulti;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int pl = blockIdx.x, n = pb.nseg;
     const int64_t cbase = static_cast<int64_t>(pl) * n;
@@ -385,33 +382,7 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
     if (t == kBlock - 1) {
         nunits[pl] = ubase;                          // the last lane's running count is the total
         nunits[pb.nplanes + pl] = s_nmulti;
-        __threadfence();
-        s_last = atomicAdd(ticket, 1) == pb.nplanes - 1;
     }
-    __syncthreads();
-    if (!s_last) return;
-    // every plane's count is written and visible: prefix over planes,
-    // kBlock planes per round
-    __threadfence();
-    int run = 0;
-    for (int p0 = 0; p0 < pb.nplanes; p0 += kBlock) {
-        const int p = p0 + t;
-        const int c = p < pb.nplanes ? __hip_atomic_load(nunits + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        int inc = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int up = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += up;
-        }
-        if (lane == 63) s_wunit[wave] = inc;
-        __syncthreads();
-        int base = run + inc - c;
-        for (int w = 0; w < wave; ++w) base += s_wunit[w];
-        if (p < pb.nplanes) nunits[2 * pb.nplanes + p] = base;
-        for (int w = 0; w < kBlock / 64; ++w) run += s_wunit[w];
-        __syncthreads();
-    }
-    if (t == 0) nunits[3 * pb.nplanes] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -434,7 +405,7 @@ __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                      const void* __restrict__ attw, const void* __restrict__ gout,
                      float* __restrict__ gacc, uint3* __restrict__ recs, int32_t* __restrict__ cursor,
-                     const int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
+                     int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
@@ -604,6 +575,24 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                                        __float_as_uint(mode == kBoth ? cr : 0.0f));
                             });
         }
+        // workgroup 0 also lays the planes' units out in one dense order for
+        // the accumulation: units before each plane, and their total
+        if (blockIdx.x == 0 && threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            int run = 0;
+            for (int c0 = 0; c0 < pb.nplanes; c0 += 64) {
+                const int v = c0 + lane < pb.nplanes ? nunits[c0 + lane] : 0;
+                int inc = v;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int up = __shfl_up(inc, o, 64);
+                    if (lane >= o) inc += up;
+                }
+                if (c0 + lane < pb.nplanes) nunits[2 * pb.nplanes + c0 + lane] = run + inc - v;
+                run += __shfl(inc, 63, 64);
+            }
+            if (lane == 0) nunits[3 * pb.nplanes] = run;
+        }
         // this plane's multi-unit segments, spread over the plane's workgroups
         const int nm = nunits[pb.nplanes + t.pl];
         const int nqc = (pb.Q + gpb - 1) / gpb;
@@ -617,7 +606,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // ---------------------------------------------------------------------------
 // Grid: nplanes * plane_units (the bound), acc_block(LPR) lanes; workgroups past
 // the total unit count exit, and the others take the units of all planes in
-// plane order, remapped so that each XCD gets a contiguous run.  LDS: the segment tile (keys * D floats), the unit's records
+// plane order (nunits[2 nplanes + p]: units before plane p, written by the
+// gradient kernel; nunits[3 nplanes]: all units), remapped so that each XCD
+// gets a contiguous run.  LDS: the segment tile (keys * D floats), the unit's records
 // sorted by key (kUnitRecords weight pairs and keys, padded), 2 * kMaxSegKeys
 // int32.
 // 64 workers of LPR lanes (at most 1024 lanes): the number of slice
