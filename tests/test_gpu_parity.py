@@ -169,20 +169,54 @@ def test_nan_inf_locations_contribute_nothing():
 # empty problems, determinism, streams, autograd
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("bs,Q", [(0, 5), (2, 0)])
-def test_empty_problem(bs, Q):
+def test_empty_problem(bs, Q, dtype):
     from scale_deformable_attention_03_amd import ops
+    dt = W.DTYPES[dtype]
     shapes = np.array([(4, 5)])
-    v = torch.randn(bs, 20, 2, 8, device="cuda")
-    loc = torch.rand(bs, Q, 2, 1, 2, 2, device="cuda")
-    w = torch.rand(bs, Q, 2, 1, 2, device="cuda")
+    v = torch.randn(bs, 20, 2, 8, device="cuda").to(dt)
+    loc = torch.rand(bs, Q, 2, 1, 2, 2, device="cuda").to(dt)
+    w = torch.rand(bs, Q, 2, 1, 2, device="cuda").to(dt)
     out = ops.forward(v, shapes, [0], loc, w)
     assert out.shape == (bs, Q, 16)
     gv = torch.full_like(v, 7.0)
-    g = torch.randn(bs, Q, 16, device="cuda")
+    g = torch.randn(bs, Q, 16, device="cuda").to(dt)
     gv, gl, gw = ops.backward(v, shapes, [0], loc, w, g, grads=(gv, torch.empty_like(loc), torch.empty_like(w)))
     torch.cuda.synchronize()
     assert (gv == 0).all(), "grad_value is zeroed even when no query samples it"
+
+
+def test_backward_accumulate_without_queries_leaves_buffer():
+    """Q = 0 through msda_backward_accumulate adds nothing."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    shapes = np.array([(4, 5)])
+    v = torch.randn(2, 20, 2, 8, device="cuda")
+    loc = torch.rand(2, 0, 2, 1, 2, 2, device="cuda")
+    w = torch.rand(2, 0, 2, 1, 2, device="cuda")
+    g = torch.randn(2, 0, 16, device="cuda")
+    prob, keep = ops.problem_for(v, shapes, [0], loc)
+    need = max(_lib.workspace_bytes(prob), 16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    acc = torch.full(v.shape, 0.5, dtype=torch.float32, device="cuda")
+    _lib.backward_accumulate(prob, v.data_ptr(), loc.data_ptr(), w.data_ptr(), g.data_ptr(), acc.data_ptr(),
+                             loc.data_ptr(), w.data_ptr(), ws.data_ptr(), need,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (acc == 0.5).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_segments_split_over_units(dtype):
+    """A 4x4 level sampled 16,000 times per head: each segment holds far more
+    records than one accumulation unit, so its rows are zeroed, added with
+    float atomics and (16-bit) rounded from the float32 workspace, while a
+    sparse 30x40 level beside it is written straight from the tile."""
+    wl = W.make("split_units", 2, [(4, 4), (30, 40)], 2, 16, 4, 2000, dtype, seed=21,
+                loc_dist="uniform", loc_args=(-0.05, 1.05))
+    t = to_device(wl)
+    check_forward(wl, gpu_forward(wl, t))
+    check_backward(wl, gpu_backward(wl, t))
 
 
 def test_forward_bitwise_repeatable_and_backward_stable():
