@@ -10,7 +10,9 @@ accumulation, built with ``-O2 -ffp-contract=off``).  This module only builds
 that file with gcc, loads it with ctypes and marshals numpy arrays.
 
 Every float input is widened exactly to float32 by the caller (fp16/bf16 ->
-fp32 is exact); outputs are float64.
+fp32 is exact); outputs are float64.  The C core takes the attention weights
+as float64: float32 weights are widened here (exactly); the fused prologue
+(``forward_fused`` / ``backward_fused``) passes its float64 softmax weights.
 """
 from __future__ import annotations
 
@@ -65,6 +67,14 @@ def _f32(a) -> np.ndarray:
     return a
 
 
+def _w64(a) -> np.ndarray:
+    """Attention weights as float64: float32 widened exactly, float64 as is."""
+    a = np.asarray(a)
+    if a.dtype not in (np.float32, np.float64):
+        raise TypeError(f"oracle takes float32 or float64 attention weights, got {a.dtype}")
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
 def _dims(spatial_shapes, level_start_index, value, loc):
     shapes = np.ascontiguousarray(np.asarray(spatial_shapes, dtype=np.int64).reshape(-1, 2))
     starts = np.ascontiguousarray(np.asarray(level_start_index, dtype=np.int64).reshape(-1))
@@ -84,7 +94,7 @@ def forward(value, spatial_shapes, level_start_index, sampling_locations, attent
             nthreads: int = 0) -> np.ndarray:
     """Oracle forward; returns float64 ``[bs, Q, M*D]``."""
     lib = _load()
-    value, loc, w = _f32(value), _f32(sampling_locations), _f32(attention_weights)
+    value, loc, w = _f32(value), _f32(sampling_locations), _w64(attention_weights)
     shapes, starts, (bs, K, M, D, L, P, Q) = _dims(spatial_shapes, level_start_index, value, loc)
     if w.shape != (bs, Q, M, L, P):
         raise ValueError("attention_weights shape")
@@ -99,7 +109,7 @@ def forward_one(value, spatial_shapes, level_start_index, sampling_locations,
                 attention_weights, b: int, q: int, m: int) -> np.ndarray:
     """Oracle forward at one (b, q, m); returns float64 ``[D]``."""
     lib = _load()
-    value, loc, w = _f32(value), _f32(sampling_locations), _f32(attention_weights)
+    value, loc, w = _f32(value), _f32(sampling_locations), _w64(attention_weights)
     shapes, starts, (bs, K, M, D, L, P, Q) = _dims(spatial_shapes, level_start_index, value, loc)
     if not (0 <= b < bs and 0 <= q < Q and 0 <= m < M):
         raise IndexError("(b, q, m) out of range")
@@ -114,7 +124,7 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations, atten
              grad_output, nthreads: int = 0):
     """Oracle backward; returns float64 ``(grad_value, grad_loc, grad_w)``."""
     lib = _load()
-    value, loc, w = _f32(value), _f32(sampling_locations), _f32(attention_weights)
+    value, loc, w = _f32(value), _f32(sampling_locations), _w64(attention_weights)
     g = _f32(grad_output)
     shapes, starts, (bs, K, M, D, L, P, Q) = _dims(spatial_shapes, level_start_index, value, loc)
     if w.shape != (bs, Q, M, L, P) or g.shape != (bs, Q, M * D):
@@ -126,3 +136,90 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations, atten
                         value.ctypes.data, loc.ctypes.data, w.ctypes.data, g.ctypes.data,
                         gv.ctypes.data, gl.ctypes.data, gw.ctypes.data, int(nthreads))
     return gv, gl, gw
+
+
+# ---- fused prologue ------------------------------------------------------------
+# The step MSDeformAttn.forward takes before the core ("Deformable DETR
+# walkthrough" (zhangshiyu.com/post/59697), section 2.2.4; both reference-point
+# forms also in sections 2.4.1 and 2.4.2, step 3): sampling locations from
+# reference points and offsets, attention weights from a softmax over each
+# head's L*P logits.
+
+
+def sampling_locations_from(reference_points, sampling_offsets, spatial_shapes) -> np.ndarray:
+    """Sampling locations ``[bs, Q, M, L, P, 2]`` in float32.
+
+    2-d reference points ``[bs, Q, L, 2]``: ref + offset / (W_l, H_l), the
+    offset normaliser being the level's (width, height).
+    4-d reference points ``[bs, Q, L, 4]`` (box centre x, y and size w, h):
+    ref_xy + offset / P * ref_wh * 0.5.
+    The module computes in float32; each operation here is one float32
+    operation, rounded in the order the expression is written.
+    """
+    ref, off = _f32(reference_points), _f32(sampling_offsets)
+    shapes = np.asarray(spatial_shapes, dtype=np.int64).reshape(-1, 2)
+    bs, Q, M, L, P, two = off.shape
+    if two != 2 or ref.shape[:3] != (bs, Q, L) or ref.shape[3] not in (2, 4) or shapes.shape[0] != L:
+        raise ValueError("inconsistent shapes")
+    r = ref[:, :, None, :, None, :]                                 # broadcast over heads and points
+    if ref.shape[3] == 2:
+        norm = np.stack([shapes[:, 1], shapes[:, 0]], -1).astype(np.float32)   # (W, H) per level
+        return (r + off / norm[None, None, None, :, None, :]).astype(np.float32)
+    t = off / np.float32(P)
+    t = t * r[..., 2:]
+    t = t * np.float32(0.5)
+    return (r[..., :2] + t).astype(np.float32)
+
+
+def softmax_weights(attention_logits) -> np.ndarray:
+    """Attention weights ``[bs, Q, M, L, P]``: softmax over each (b, q, m)'s
+    L*P logits, in float64 (exp(v - max) / sum)."""
+    a = _f32(attention_logits).astype(np.float64)
+    bs, Q, M, L, P = a.shape
+    v = a.reshape(bs, Q, M, L * P)
+    e = np.exp(v - v.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).reshape(bs, Q, M, L, P)
+
+
+def forward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                  attention_logits, nthreads: int = 0) -> np.ndarray:
+    """Oracle of the fused forward: locations and weights as above, then the
+    core (``forward``)."""
+    loc = sampling_locations_from(reference_points, sampling_offsets, spatial_shapes)
+    w = softmax_weights(attention_logits)
+    return forward(value, spatial_shapes, level_start_index, loc, w, nthreads)
+
+
+def location_jacobian(reference_points, spatial_shapes, num_heads: int, num_points: int) -> np.ndarray:
+    """d loc / d offset per sample and coordinate, ``[bs, Q, M, L, P, 2]``
+    float64: 1 / (W_l, H_l) for 2-d reference points, ref_wh * 0.5 / P for
+    4-d ones (the location is affine in the offset)."""
+    ref = _f32(reference_points).astype(np.float64)
+    shapes = np.asarray(spatial_shapes, dtype=np.int64).reshape(-1, 2)
+    bs, Q, L, rd = ref.shape
+    if rd == 2:
+        j = np.stack([1.0 / shapes[:, 1], 1.0 / shapes[:, 0]], -1)[None, None, None, :, None, :]
+    else:
+        j = ref[:, :, None, :, None, 2:] * 0.5 / num_points
+    return np.broadcast_to(j, (bs, Q, num_heads, L, num_points, 2)).copy()
+
+
+def backward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                   attention_logits, grad_output, nthreads: int = 0):
+    """Oracle of the fused backward; returns float64
+    ``(grad_value, grad_sampling_offsets, grad_attention_logits)``.
+
+    The core's gradients (``backward``) at the formed locations and weights,
+    then the chain rule through the prologue: the location gradient times
+    d loc / d offset, and the softmax's backward,
+    d L / d logit_i = w_i * (g_i - sum_k w_k g_k) over the head's L*P entries,
+    g being the gradient of the weights.
+    """
+    loc = sampling_locations_from(reference_points, sampling_offsets, spatial_shapes)
+    w = softmax_weights(attention_logits)
+    gv, gl, gw = backward(value, spatial_shapes, level_start_index, loc, w, grad_output, nthreads)
+    bs, Q, M, L, P, _ = gl.shape
+    goff = gl * location_jacobian(reference_points, spatial_shapes, M, P)
+    wf, gf = w.reshape(bs, Q, M, L * P), gw.reshape(bs, Q, M, L * P)
+    glog = wf * (gf - (wf * gf).sum(axis=-1, keepdims=True))
+    return gv, goff, glog.reshape(bs, Q, M, L, P)

@@ -26,7 +26,9 @@
  *   MSDeformAttnFunction.backward).
  *
  * Arithmetic:
- *   - float inputs arrive already widened (exactly) to float32;
+ *   - float inputs arrive already widened (exactly) to float32, except the
+ *     attention weights, which arrive as float64 (a float32 weight widened
+ *     exactly, or a float64 softmax weight of the fused prologue);
  *   - the pixel coordinate is formed in float32 with two separate roundings,
  *     x = (loc_x * W) - 0.5, y = (loc_y * H) - 0.5 (align_corners=False maps
  *     normalised 0 and 1 to the outer pixel edges, so pixel centres land on
@@ -121,7 +123,7 @@ int oracle_threads(int nthreads)
  */
 void oracle_forward_one(int64_t K, int64_t M, int64_t D, int64_t L, int64_t P, int64_t Q,
                         const int64_t *shapes, const int64_t *starts, const float *value,
-                        const float *loc, const float *attw, int64_t b, int64_t q, int64_t m,
+                        const float *loc, const double *attw, int64_t b, int64_t q, int64_t m,
                         double *out_d)
 {
     int64_t bq = b * Q + q;
@@ -138,7 +140,7 @@ void oracle_forward_one(int64_t K, int64_t M, int64_t D, int64_t L, int64_t P, i
             const float *v01 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0, s.x0 + 1);
             const float *v10 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0 + 1, s.x0);
             const float *v11 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0 + 1, s.x0 + 1);
-            double w = (double)attw[idx];
+            double w = attw[idx];
             for (int64_t d = 0; d < D; ++d) {
                 double smp = s.hy * s.hx * row_at(v00, d) + s.hy * s.lx * row_at(v01, d) +
                              s.ly * s.hx * row_at(v10, d) + s.ly * s.lx * row_at(v11, d);
@@ -151,7 +153,7 @@ void oracle_forward_one(int64_t K, int64_t M, int64_t D, int64_t L, int64_t P, i
 /* Forward over the whole problem: out[bs, Q, M*D]. */
 void oracle_forward(int64_t bs, int64_t K, int64_t M, int64_t D, int64_t L, int64_t P,
                     int64_t Q, const int64_t *shapes, const int64_t *starts,
-                    const float *value, const float *loc, const float *attw,
+                    const float *value, const float *loc, const double *attw,
                     double *out, int nthreads)
 {
     set_threads(nthreads);
@@ -175,7 +177,7 @@ void oracle_forward(int64_t bs, int64_t K, int64_t M, int64_t D, int64_t L, int6
  */
 void oracle_backward(int64_t bs, int64_t K, int64_t M, int64_t D, int64_t L, int64_t P,
                      int64_t Q, const int64_t *shapes, const int64_t *starts,
-                     const float *value, const float *loc, const float *attw,
+                     const float *value, const float *loc, const double *attw,
                      const float *grad_out, double *grad_value, double *grad_loc,
                      double *grad_w, int nthreads)
 {
@@ -202,7 +204,7 @@ void oracle_backward(int64_t bs, int64_t K, int64_t M, int64_t D, int64_t L, int
                     const float *v01 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0, s.x0 + 1);
                     const float *v10 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0 + 1, s.x0);
                     const float *v11 = corner_row(value, K, M, D, b, m, s0, H, W, s.y0 + 1, s.x0 + 1);
-                    double w = (double)attw[idx];
+                    double w = attw[idx];
                     double gw = 0.0, gx = 0.0, gy = 0.0;
                     for (int64_t d = 0; d < D; ++d) {
                         double a = row_at(v00, d), bb = row_at(v01, d);
@@ -242,7 +244,7 @@ void oracle_backward(int64_t bs, int64_t K, int64_t M, int64_t D, int64_t L, int
                     bilinear_t s = make_sample(loc[2 * idx], loc[2 * idx + 1], H, W);
                     if (!s.valid)
                         continue;
-                    double w = (double)attw[idx];
+                    double w = attw[idx];
                     const int64_t dy[4] = {0, 0, 1, 1}, dx[4] = {0, 1, 0, 1};
                     const double cw[4] = {s.hy * s.hx, s.hy * s.lx, s.ly * s.hx, s.ly * s.lx};
                     for (int c = 0; c < 4; ++c) {
