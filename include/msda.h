@@ -236,6 +236,69 @@ msda_status_t msda_backward_profile(const msda_problem_t *problem,
                                     hipEvent_t *stage_events,
                                     hipStream_t stream);
 
+/*
+ * Fused prologue: the step that feeds the core in MSDeformAttn.forward
+ * ("Deformable DETR walkthrough" (zhangshiyu.com/post/59697), section 2.2.4;
+ * the two reference-point forms in sections 2.4.1 and 2.4.2, step 3), done
+ * inside the kernels instead of as separate passes over HBM:
+ *
+ *   ref_dims = 2:  loc[b,q,m,l,p] = ref[b,q,l] + off[b,q,m,l,p] / (W_l, H_l)
+ *   ref_dims = 4:  loc[b,q,m,l,p] = ref[b,q,l,0:2] +
+ *                                   off[b,q,m,l,p] / P * ref[b,q,l,2:4] * 0.5
+ *   w[b,q,m,:,:]  = softmax of logit[b,q,m,:,:] over its L*P entries
+ *
+ * then the core as in msda_forward.  Each location is formed in float32
+ * one operation at a time in the order written (no fused multiply-add); the
+ * softmax subtracts the group's maximum, sums exp in float32 and divides.
+ *   reference_points  [batch, num_queries, num_levels, ref_dims] (x, y) or
+ *                     (x, y, w, h), normalised, problem dtype
+ *   sampling_offsets  [batch, num_queries, num_heads, num_levels, num_points, 2]
+ *                     (x, y), in pixels of the level (2-d) or in units of
+ *                     P half-box sizes (4-d)
+ *   attention_logits  [batch, num_queries, num_heads, num_levels, num_points]
+ * ref_dims must be 2 or 4 (MSDA_ERROR_INVALID_VALUE otherwise).  Pointers,
+ * ownership, streams and errors as for msda_forward.
+ */
+msda_status_t msda_forward_fused(const msda_problem_t *problem,
+                                 int32_t ref_dims,
+                                 const void *value,
+                                 const void *reference_points,
+                                 const void *sampling_offsets,
+                                 const void *attention_logits,
+                                 void *output,
+                                 hipStream_t stream);
+
+/*
+ * msda_backward_fused: gradients of sum(grad_output * output) of
+ * msda_forward_fused with respect to value, sampling_offsets and
+ * attention_logits (not reference_points: the pages detach refined
+ * reference points before they reach the attention, section 2.4.1 step 2,
+ * and the encoder's are a fixed grid).
+ *   grad_value             as msda_backward
+ *   grad_sampling_offsets  = grad_sampling_locations * d loc / d off, i.e.
+ *                            divided by (W_l, H_l) (2-d) or multiplied by
+ *                            ref_wh * 0.5 / P (4-d); zero off the map
+ *   grad_attention_logits  = w * (g - sum over the group of w * g), with g
+ *                            the gradient of the weights as in msda_backward
+ *                            (a sample off the map has g = 0 but still
+ *                            receives the second term)
+ * Same workspace (msda_backward_workspace_bytes), kernels, ownership and
+ * error codes as msda_backward; all three gradients are overwritten.
+ */
+msda_status_t msda_backward_fused(const msda_problem_t *problem,
+                                  int32_t ref_dims,
+                                  const void *value,
+                                  const void *reference_points,
+                                  const void *sampling_offsets,
+                                  const void *attention_logits,
+                                  const void *grad_output,
+                                  void *grad_value,
+                                  void *grad_sampling_offsets,
+                                  void *grad_attention_logits,
+                                  void *workspace,
+                                  size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* msda_status_string: a static, human-readable name for a status code. */
 const char *msda_status_string(msda_status_t status);
 

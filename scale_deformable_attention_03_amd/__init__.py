@@ -6,7 +6,8 @@ points below load that library on first use and raise ImportError if it has
 not been built; there is no other implementation to fall back to.
 """
 
-_OPS = ("MSDeformAttnFunction", "ms_deform_attn", "forward", "backward", "problem_for")
+_OPS = ("MSDeformAttnFunction", "ms_deform_attn", "forward", "backward", "problem_for",
+        "MSDeformAttnFusedFunction", "ms_deform_attn_fused", "forward_fused", "backward_fused")
 
 
 def __getattr__(name):

@@ -17,8 +17,8 @@ MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
 STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
           3: "MSDA_ERROR_MISALIGNED", 4: "MSDA_ERROR_HIP"}
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
-           "msda_backward_accumulate", "msda_backward_profile", "msda_status_string",
-           "msda_abi_version")
+           "msda_backward_accumulate", "msda_backward_profile", "msda_forward_fused",
+           "msda_backward_fused", "msda_status_string", "msda_abi_version")
 BACKWARD_STAGES = ("zero_counts", "count", "scan", "gradient", "accumulate", "narrow")
 
 
@@ -86,6 +86,11 @@ def _load():
     lib.msda_backward_accumulate.restype = ctypes.c_int
     lib.msda_backward_profile.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.msda_backward_profile.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.msda_forward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.msda_forward_fused.restype = ctypes.c_int
+    lib.msda_backward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msda_backward_fused.restype = ctypes.c_int
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
@@ -134,3 +139,19 @@ def backward_profile(problem: Problem, value: int, loc: int, w: int, gout: int, 
                                    workspace, workspace_bytes_, events, stream)
     if st != 0:
         raise MsdaError(st, "msda_backward_profile")
+
+
+def forward_fused(problem: Problem, ref_dims: int, value: int, ref: int, off: int, logits: int, out: int,
+                  stream: int) -> None:
+    st = lib.msda_forward_fused(ctypes.byref(problem), ref_dims, value, ref, off, logits, out, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_forward_fused")
+
+
+def backward_fused(problem: Problem, ref_dims: int, value: int, ref: int, off: int, logits: int, gout: int,
+                   gvalue: int, goff: int, glogits: int, workspace: int, workspace_bytes_: int,
+                   stream: int) -> None:
+    st = lib.msda_backward_fused(ctypes.byref(problem), ref_dims, value, ref, off, logits, gout, gvalue,
+                                 goff, glogits, workspace, workspace_bytes_, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_fused")

@@ -280,37 +280,59 @@ int64_t plane_blocks(const msda::Problem& pb, int gpb) {
     return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
 }
 
+// Reference-point form of a call: 0 (locations and weights given), 2 or 4
+// (reference points, offsets and logits given; the fused prologue).
+template <int DT, int VECB, int LPR, int REF>
+const void* fwd_kernel(const msda::Problem& pb) {
+    return is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4, REF>)
+                       : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0, REF>);
+}
+
+template <int DT, int VECB, int LPR, bool BINNED, int REF>
+const void* grad_kernel(const msda::Problem& pb) {
+    return is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, BINNED, REF>)
+                       : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, BINNED, REF>);
+}
+
+// LDS of the fused prologue: logits and their exponentials.
+size_t fused_lds(int ref_dims, int gpb, int LP) { return ref_dims ? sizeof(float) * 2 * size_t(gpb) * LP : 0; }
+
 template <int DT, int VECB, int LPR>
 struct Fwd {
-    static msda_status_t run(const msda::Problem& pb, const void* v, const void* loc, const void* w,
-                             void* out, hipStream_t st) {
+    static msda_status_t run(const msda::Problem& pb, int ref_dims, const void* v, const void* ref,
+                             const void* loc, const void* w, void* out, hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, 1024);
-        const size_t lds = sizeof(uint32_t) * gpb * (8 * pb.L * pb.P + 4);
-        const void* k = is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4>)
-                                    : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0>);
-        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, out, pb, gpb);
+        const int LP = pb.L * pb.P;
+        const size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
+        const void* k = ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
+                        : ref_dims == 2 ? fwd_kernel<DT, VECB, LPR, 2>(pb)
+                                        : fwd_kernel<DT, VECB, LPR, 4>(pb);
+        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, out, pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
 struct Grad {
-    static msda_status_t run(const msda::Problem& pb, bool binned, const void* v, const void* loc,
-                             const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor,
-                             int32_t* nunits, const int32_t* multi, void* gloc, void* gw, hipStream_t st) {
+    static msda_status_t run(const msda::Problem& pb, bool binned, int ref_dims, const void* v, const void* ref,
+                             const void* loc, const void* w, const void* gout, float* gacc, uint3* recs,
+                             int32_t* cursor, int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
+                             hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
-        size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4);
+        size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
         if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg);
         const void* k;
         if (binned)
-            k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, true>)
-                            : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, true>);
+            k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, true, 0>(pb)
+                : ref_dims == 2 ? grad_kernel<DT, VECB, LPR, true, 2>(pb)
+                                : grad_kernel<DT, VECB, LPR, true, 4>(pb);
         else
-            k = is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, false>)
-                            : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, false>);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, gout, gacc, recs, cursor, nunits, multi, gloc, gw,
-                      pb, gpb);
+            k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, false, 0>(pb)
+                : ref_dims == 2 ? grad_kernel<DT, VECB, LPR, false, 2>(pb)
+                                : grad_kernel<DT, VECB, LPR, false, 4>(pb);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, ref, gout, gacc, recs, cursor, nunits, multi,
+                      gloc, gw, pb, gpb);
     }
 };
 
@@ -329,13 +351,45 @@ struct Accum {
     }
 };
 
+template <int DT, int REF>
+const void* count_kernel(const msda::Problem& pb) {
+    return is_l4p4(pb) ? kfn(&msda::msda_bin_count_kernel<DT, 4, 4, REF>)
+                       : kfn(&msda::msda_bin_count_kernel<DT, 0, 0, REF>);
+}
+
 template <int DT>
-msda_status_t count_launch(const msda::Problem& pb, const void* loc, int32_t* counts, hipStream_t st) {
+msda_status_t count_launch(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
+                           int32_t* counts, hipStream_t st) {
     const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
     const int64_t blocks = int64_t(pb.nplanes) * ((nsamp + msda::kCountChunk - 1) / msda::kCountChunk);
-    const void* k = is_l4p4(pb) ? kfn(&msda::msda_bin_count_kernel<DT, 4, 4>)
-                                : kfn(&msda::msda_bin_count_kernel<DT, 0, 0>);
-    return launch(k, blocks, kBlock, sizeof(int32_t) * pb.nseg, st, loc, counts, pb);
+    const void* k = ref_dims == 0   ? count_kernel<DT, 0>(pb)
+                    : ref_dims == 2 ? count_kernel<DT, 2>(pb)
+                                    : count_kernel<DT, 4>(pb);
+    return launch(k, blocks, kBlock, sizeof(int32_t) * pb.nseg, st, loc, ref, counts, pb);
+}
+
+// Reference points of the fused prologue: ref_dims 0 (none; ref unused), 2
+// or 4, with [batch, num_queries, num_levels, ref_dims] elements.
+msda_status_t check_ref(const msda_problem_t* p, int ref_dims, const void* ref) {
+    if (ref_dims == 0) return MSDA_SUCCESS;
+    if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
+    return check_ptr(ref, int64_t(p->batch) * p->num_queries * p->num_levels * ref_dims);
+}
+
+msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
+                           const void* sampling_locations, const void* attention_weights, void* output,
+                           hipStream_t stream) {
+    MSDA_TRY(check_problem(problem));
+    MSDA_TRY(check_ref(problem, ref_dims, ref));
+    MSDA_TRY(check_ptr(value, value_elems(problem)));
+    MSDA_TRY(check_ptr(sampling_locations, sample_elems(problem)));
+    MSDA_TRY(check_ptr(attention_weights, sample_elems(problem)));
+    MSDA_TRY(check_ptr(output, out_elems(problem)));
+    if (out_elems(problem) == 0) return MSDA_SUCCESS;
+    const msda::Problem pb = pack(problem);
+    const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
+    return by_dtype_split<Fwd>(problem->dtype, s, pb, ref_dims, value, ref, sampling_locations, attention_weights,
+                               output, stream);
 }
 
 msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
@@ -369,9 +423,11 @@ msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
 // float32 and the workspace's float32 buffer for 16-bit dtypes, which then
 // holds only rows the kernels add into (and is rounded into gfinal at the
 // end).
-msda_status_t backward_into(const msda_problem_t* problem, const void* value, const void* loc,
-                            const void* w, const void* gout, float* gacc, void* gfinal, void* gloc, void* gw,
-                            char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
+// ref_dims != 0: the fused prologue (loc and w are the offsets and logits,
+// gloc and gw receive their gradients).
+msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
+                            const void* loc, const void* w, const void* gout, float* gacc, void* gfinal, void* gloc,
+                            void* gw, char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
     const bool narrow16 = !accumulate && problem->dtype != MSDA_F32;
     if (sample_elems(problem) == 0) {
         // no samples (Q = 0): grad_value is zero and nothing else is written
@@ -391,7 +447,7 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
         MSDA_TRY(mark(ev, kStageCount, st));
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
-        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, value, loc, w, gout, gacc,
+        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, ref_dims, value, ref, loc, w, gout, gacc,
                                       static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
                                       static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
                                       gloc, gw, st));
@@ -417,16 +473,16 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
     MSDA_TRY(mark(ev, kStageCount, st));
     switch (problem->dtype) {
-        case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, loc, counts, st)); break;
-        case MSDA_F16: MSDA_TRY(count_launch<kF16>(pb, loc, counts, st)); break;
-        default: MSDA_TRY(count_launch<kBF16>(pb, loc, counts, st)); break;
+        case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, ref_dims, ref, loc, counts, st)); break;
+        case MSDA_F16: MSDA_TRY(count_launch<kF16>(pb, ref_dims, ref, loc, counts, st)); break;
+        default: MSDA_TRY(count_launch<kBF16>(pb, ref_dims, ref, loc, counts, st)); break;
     }
     MSDA_TRY(mark(ev, kStageScan, st));
     MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
                     static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb,
                     static_cast<int>(plane_records(problem)), static_cast<int>(plane_units(problem, pb))));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, value, loc, w, gout, gacc, recs, cursor,
+    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, ref_dims, value, ref, loc, w, gout, gacc, recs, cursor,
                                   nunits, static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
@@ -444,11 +500,13 @@ msda_status_t backward_into(const msda_problem_t* problem, const void* value, co
     return MSDA_SUCCESS;
 }
 
-msda_status_t backward_call(const msda_problem_t* problem, const void* value, const void* sampling_locations,
-                            const void* attention_weights, const void* grad_output, void* grad_value,
-                            void* grad_sampling_locations, void* grad_attention_weights, void* workspace,
-                            size_t workspace_bytes, hipEvent_t* ev, hipStream_t stream) {
+msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
+                            const void* sampling_locations, const void* attention_weights,
+                            const void* grad_output, void* grad_value, void* grad_sampling_locations,
+                            void* grad_attention_weights, void* workspace, size_t workspace_bytes, hipEvent_t* ev,
+                            hipStream_t stream) {
     MSDA_TRY(check_problem(problem));
+    MSDA_TRY(check_ref(problem, ref_dims, ref));
     MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output,
                                  grad_value, grad_sampling_locations, grad_attention_weights));
     const int64_t nv = value_elems(problem);
@@ -462,8 +520,8 @@ msda_status_t backward_call(const msda_problem_t* problem, const void* value, co
     const Layout lay = layout(problem, pack(problem));
     float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
                                              : reinterpret_cast<float*>(ws + lay.acc);
-    MSDA_TRY(backward_into(problem, value, sampling_locations, attention_weights, grad_output, gacc, grad_value,
-                           grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
+    MSDA_TRY(backward_into(problem, ref_dims, value, ref, sampling_locations, attention_weights, grad_output, gacc,
+                           grad_value, grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
     return mark(ev, kStageEnd, stream);
 }
 
@@ -489,16 +547,15 @@ const char* msda_status_string(msda_status_t status) {
 msda_status_t msda_forward(const msda_problem_t* problem, const void* value,
                            const void* sampling_locations, const void* attention_weights,
                            void* output, hipStream_t stream) {
-    MSDA_TRY(check_problem(problem));
-    MSDA_TRY(check_ptr(value, value_elems(problem)));
-    MSDA_TRY(check_ptr(sampling_locations, sample_elems(problem)));
-    MSDA_TRY(check_ptr(attention_weights, sample_elems(problem)));
-    MSDA_TRY(check_ptr(output, out_elems(problem)));
-    if (out_elems(problem) == 0) return MSDA_SUCCESS;
-    const msda::Problem pb = pack(problem);
-    const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    return by_dtype_split<Fwd>(problem->dtype, s, pb, value, sampling_locations, attention_weights, output,
-                                  stream);
+    return forward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, output, stream);
+}
+
+msda_status_t msda_forward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
+                                 const void* reference_points, const void* sampling_offsets,
+                                 const void* attention_logits, void* output, hipStream_t stream) {
+    if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
+    return forward_call(problem, ref_dims, value, reference_points, sampling_offsets, attention_logits, output,
+                        stream);
 }
 
 size_t msda_backward_workspace_bytes(const msda_problem_t* problem) {
@@ -512,9 +569,20 @@ msda_status_t msda_backward(const msda_problem_t* problem, const void* value,
                             const void* grad_output, void* grad_value,
                             void* grad_sampling_locations, void* grad_attention_weights,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return backward_call(problem, value, sampling_locations, attention_weights, grad_output, grad_value,
-                         grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes, nullptr,
-                         stream);
+    return backward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
+                         nullptr, stream);
+}
+
+msda_status_t msda_backward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
+                                  const void* reference_points, const void* sampling_offsets,
+                                  const void* attention_logits, const void* grad_output, void* grad_value,
+                                  void* grad_sampling_offsets, void* grad_attention_logits, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
+    return backward_call(problem, ref_dims, value, reference_points, sampling_offsets, attention_logits,
+                         grad_output, grad_value, grad_sampling_offsets, grad_attention_logits, workspace,
+                         workspace_bytes, nullptr, stream);
 }
 
 msda_status_t msda_backward_profile(const msda_problem_t* problem, const void* value,
@@ -524,8 +592,8 @@ msda_status_t msda_backward_profile(const msda_problem_t* problem, const void* v
                                     void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
                                     hipStream_t stream) {
     if (stage_events == nullptr) return MSDA_ERROR_INVALID_VALUE;
-    return backward_call(problem, value, sampling_locations, attention_weights, grad_output, grad_value,
-                         grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
+    return backward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
                          stage_events, stream);
 }
 
@@ -543,9 +611,9 @@ msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void
         MSDA_TRY(check_ptr(workspace, 1));
     }
     if (value_elems(problem) == 0) return MSDA_SUCCESS;
-    return backward_into(problem, value, sampling_locations, attention_weights, grad_output, grad_value_acc, nullptr,
-                         grad_sampling_locations, grad_attention_weights, static_cast<char*>(workspace), 1,
-                         nullptr, stream);
+    return backward_into(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value_acc, nullptr, grad_sampling_locations, grad_attention_weights,
+                         static_cast<char*>(workspace), 1, nullptr, stream);
 }
 
 }  // extern "C"

@@ -197,10 +197,12 @@ __device__ __forceinline__ void lds_add_f32xN(float* dst, const float* v) {
 // 1. count
 // ---------------------------------------------------------------------------
 // Grid: nplanes * ceil(Q*L*P / kCountChunk) workgroups of kBlock lanes; one
-// lane per sample.  LDS: nseg int32.
-template <int DT, int L_CT, int P_CT>
+// lane per sample.  LDS: nseg int32.  REF as for the gradient kernel (loc
+// holds the offsets and ref the reference points when REF != 0).
+template <int DT, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kBlock)
-msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts, Problem pb) {
+msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref, int32_t* __restrict__ counts,
+                      Problem pb) {
     extern __shared__ int32_t hist[];
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
@@ -223,9 +225,12 @@ msda_bin_count_kernel(const void* __restrict__ loc, int32_t* __restrict__ counts
             const int s = s0 + u * kBlock;
             lx[u] = ly[u] = -2.0f;                       // off the map
             if (s < s_end) {
-                const int q = s / LP, lp = s - q * LP;
+                const int q = s / LP, lp = s - q * LP, l = lp / P;
                 const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
-                const float2 xy = load_pair<DT>(loc, i);
+                const int64_t ri = (static_cast<int64_t>(b) * pb.Q + q) * L + l;
+                const int4 lv = s_lv[l];
+                const float2 xy = sample_location<DT, REF>(loc, ref, i, ri, static_cast<float>(lv.y),
+                                                           static_cast<float>(lv.x), static_cast<float>(P));
                 lx[u] = xy.x;
                 ly[u] = xy.y;
             }
@@ -400,10 +405,10 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 // rows of the plane's multi-unit segments (the accumulation adds into them).
 // LDS: gpb * (8 * L * P + 4) words; when BINNED also 2 * nseg int32 (counts,
 // then cursors, and bases).
-template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED>
+template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
-                     const void* __restrict__ attw, const void* __restrict__ gout,
+                     const void* __restrict__ attw, const void* __restrict__ ref, const void* __restrict__ gout,
                      float* __restrict__ gacc, uint3* __restrict__ recs, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
@@ -419,6 +424,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     uint32_t* srec = sm;
     int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);
     int32_t* lbase = lhist + pb.nseg;
+    // fused prologue: logits (later the weights' gradients) and exponentials
+    float* sv = reinterpret_cast<float*>(lhist + (BINNED ? 2 * pb.nseg : 0));
+    float* se = sv + gpb * LP;
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
@@ -426,17 +434,29 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     stage_levels(pb, s_lv);
     if constexpr (BINNED)
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) lhist[i] = 0;
+    if constexpr (REF != 0) load_logits<DT>(attw, t.G0, pb.M, t.gcount, LP, sv);
     __syncthreads();
+    if constexpr (REF != 0) {
+        exp_logits(t.gcount, LP, sv, se);
+        __syncthreads();
+    }
 
-    // prologue: one lane per sample
+    // prologue: one lane per sample.  With REF != 0 the weight kept is the
+    // softmax weight even for a sample off the map (its gradient reaches the
+    // other logits of the group); nothing reads it there but the softmax
+    // backward.
     for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
         const int4 lv = s_lv[l];
         const int H = lv.x, W = lv.y;
-        const float2 xy = load_pair<DT>(loc, si);
+        const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
+        const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(W), static_cast<float>(H),
+                                                   static_cast<float>(P));
         const Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
-        const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        float aw;
+        if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        else aw = se[i] / group_total(se + g * LP, LP);
         uint32_t* r = srec + g * gstride + lp * 8;
         const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
                                    : kNoCell;
@@ -478,7 +498,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         constexpr int kSB = kC % kSBMax == 0 ? kSBMax : 1;
 #pragma unroll 1
         for (int c0 = 0; c0 < LP; c0 += kC) {
-            float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f;
+            float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f, own_a = 0.0f;
 #pragma unroll
             for (int b0 = 0; b0 < kC; b0 += kSB) {
                 uint4 o[kSB];
@@ -533,16 +553,50 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     if (li == b0 + u) {
                         const int l = lp / P;                // uniform across the wave
                         own_w = off ? 0.0f : sw;
-                        own_x = off ? 0.0f : sx * (static_cast<float>(pb.lv.W[l]) * fr.z);
-                        own_y = off ? 0.0f : sy * (static_cast<float>(pb.lv.H[l]) * fr.z);
+                        if constexpr (REF == 0) {
+                            own_x = off ? 0.0f : sx * (static_cast<float>(pb.lv.W[l]) * fr.z);
+                            own_y = off ? 0.0f : sy * (static_cast<float>(pb.lv.H[l]) * fr.z);
+                        } else {
+                            // d loc / d offset: 1 / (W, H) for 2-d reference
+                            // points, ref_wh * 0.5 / P for 4-d ones
+                            own_x = off ? 0.0f : sx * fr.z;
+                            own_y = off ? 0.0f : sy * fr.z;
+                            own_a = static_cast<float>(l);
+                        }
                     }
                 }
             }
             if (li < kC) {
                 const int64_t s = G * LP + c0 + li;
-                store_scalar<DT>(grad_w, s, own_w);
+                if constexpr (REF == 0) {
+                    store_scalar<DT>(grad_w, s, own_w);
+                } else {
+                    sv[lg * LP + c0 + li] = own_w;       // the softmax backward below
+                    if constexpr (REF == 4) {
+                        const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + lg) * L +
+                                           static_cast<int>(own_a);
+                        const float2 wh = load_pair<DT>(ref, 2 * ri + 1);
+                        const float k = 0.5f / static_cast<float>(P);
+                        own_x = own_x * static_cast<float>(pb.lv.W[static_cast<int>(own_a)]) * (wh.x * k);
+                        own_y = own_y * static_cast<float>(pb.lv.H[static_cast<int>(own_a)]) * (wh.y * k);
+                    }
+                }
                 store_pair<DT>(grad_loc, s, own_x, own_y);
             }
+        }
+    }
+    if constexpr (REF != 0) {
+        // softmax backward: with w the group's weights and g = dL/dw,
+        // dL/dlogit_i = w_i * (g_i - sum_k w_k g_k)
+        __syncthreads();
+        for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+            const int g = i / LP;
+            const uint32_t* r = srec + g * gstride + 6;          // the weights, 8 words apart
+            const float* gg = sv + g * LP;
+            float dot = 0.0f;
+            for (int k = 0; k < LP; ++k) dot += __uint_as_float(r[8 * k]) * gg[k];
+            const float wi = __uint_as_float(r[8 * (i - g * LP)]);
+            store_scalar<DT>(grad_w, (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + (i - g * LP), wi * (sv[i] - dot));
         }
     }
     if constexpr (BINNED) {

@@ -241,6 +241,70 @@ __device__ __forceinline__ bool pixel_coords(float loc_x, float loc_y, float Wf,
     return (x > -1.0f) & (x < Wf) & (y > -1.0f) & (y < Hf);
 }
 
+// ---- sampling locations and weights (plain or fused prologue) --------------
+//
+// REF selects what the kernels are given.  REF = 0: sampling locations
+// [bs,Q,M,L,P,2] and attention weights [bs,Q,M,L,P].  REF = 2 or 4: the step
+// before the core in "Deformable DETR walkthrough" section 2.2.4
+// (MSDeformAttn.forward): reference points [bs,Q,L,REF], sampling offsets
+// laid out like the locations and attention logits laid out like the
+// weights.  The location is ref + offset / (W, H) for 2-d reference points
+// and ref_xy + offset / P * ref_wh * 0.5 for 4-d ones, each operation rounded
+// to float32 in that order; the weights are the softmax of the L*P logits of
+// one (batch, query, head).
+
+// Sample si's location; ri = (b * Q + q) * L + l indexes its reference point.
+template <int DT, int REF>
+__device__ __forceinline__ float2 sample_location(const void* loc_or_off, const void* ref, int64_t si,
+                                                  int64_t ri, float Wf, float Hf, float Pf) {
+#pragma clang fp contract(off)
+    const float2 a = load_pair<DT>(loc_or_off, si);
+    if constexpr (REF == 0) {
+        return a;
+    } else if constexpr (REF == 2) {
+        const float2 r = load_pair<DT>(ref, ri);
+        const float ox = a.x / Wf, oy = a.y / Hf;
+        return make_float2(r.x + ox, r.y + oy);
+    } else {
+        const float2 rxy = load_pair<DT>(ref, 2 * ri), rwh = load_pair<DT>(ref, 2 * ri + 1);
+        float tx = a.x / Pf, ty = a.y / Pf;
+        tx = tx * rwh.x;
+        ty = ty * rwh.y;
+        tx = tx * 0.5f;
+        ty = ty * 0.5f;
+        return make_float2(rxy.x + tx, rxy.y + ty);
+    }
+}
+
+// Softmax of each (batch, query, head)'s L*P logits, staged through LDS for
+// the gcount groups G0, G0 + M, ... of a workgroup (sample i = g * LP + lp):
+// load_logits fills sv; after a barrier exp_logits writes
+// se[i] = exp(sv[i] - max of the group); after another barrier a sample's
+// weight is se[i] / group_total(se + g * LP, LP).  Float32 throughout.
+template <int DT>
+__device__ __forceinline__ void load_logits(const void* logits, int64_t G0, int M, int gcount, int LP,
+                                            float* sv) {
+    for (int i = threadIdx.x; i < gcount * LP; i += blockDim.x) {
+        const int g = i / LP, lp = i - g * LP;
+        sv[i] = load_scalar<DT>(logits, (G0 + static_cast<int64_t>(g) * M) * LP + lp);
+    }
+}
+
+__device__ __forceinline__ void exp_logits(int gcount, int LP, const float* sv, float* se) {
+    for (int i = threadIdx.x; i < gcount * LP; i += blockDim.x) {
+        const float* v = sv + (i / LP) * LP;
+        float mx = v[0];
+        for (int k = 1; k < LP; ++k) mx = fmaxf(mx, v[k]);
+        se[i] = expf(sv[i] - mx);
+    }
+}
+
+__device__ __forceinline__ float group_total(const float* a, int n) {
+    float s = 0.0f;
+    for (int k = 0; k < n; ++k) s += a[k];
+    return s;
+}
+
 // Bilinear cell of a valid sample: the four corners' flat offsets (in
 // elements, relative to the (batch, head) base), their in-map flags and
 // bilinear weights (without the attention weight).

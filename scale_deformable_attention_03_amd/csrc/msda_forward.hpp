@@ -91,11 +91,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value,
 }
 
 // Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes.
-// LDS: gpb * (8 * L * P + 4) words.
-template <int DT, int VECB, int LPR, int L_CT, int P_CT>
+// LDS: gpb * (8 * L * P + 4) words, plus 2 * gpb * L * P when REF != 0.
+// REF = 0: loc and attw are the sampling locations and attention weights;
+// REF = 2 or 4: they are the sampling offsets and attention logits, and ref
+// holds the reference points (see sample_location).
+template <int DT, int VECB, int LPR, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
-                    const void* __restrict__ attw, void* __restrict__ out, Problem pb, int gpb) {
+                    const void* __restrict__ attw, const void* __restrict__ ref, void* __restrict__ out,
+                    Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     const int L = L_CT ? L_CT : pb.L;
@@ -108,16 +112,28 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
     __shared__ int4 s_lv[kMaxLevels];
     stage_levels(pb, s_lv);
+    // fused prologue: the workgroup's logits and their exponentials
+    float* sv = reinterpret_cast<float*>(sm + gpb * gstride);
+    float* se = sv + gpb * LP;
+    if constexpr (REF != 0) load_logits<DT>(attw, t.G0, pb.M, t.gcount, LP, sv);
     __syncthreads();
+    if constexpr (REF != 0) {
+        exp_logits(t.gcount, LP, sv, se);
+        __syncthreads();
+    }
 
     // prologue: one lane per sample
     for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
         const int g = i / LP, lp = i - g * LP, l = lp / P;
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-        const float2 xy = load_pair<DT>(loc, si);
         const int4 lv = s_lv[l];
+        const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
+        const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
+                                                   static_cast<float>(lv.x), static_cast<float>(P));
         const Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
-        const float aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        float aw;
+        if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        else aw = c.ok ? se[i] / group_total(se + g * LP, LP) : 0.0f;
         const float wy0 = aw * c.hy, wy1 = aw * c.ly;
         uint32_t* r = sm + g * gstride + lp * 8;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);

@@ -18,6 +18,19 @@ attention_weights and None for the two integer tensors, as
 MSDeformAttnFunction.backward does on the "DQ-DETR ops directory" CSDN page
 (section 2(3)).
 
+The fused form takes what MSDeformAttn.forward has before it forms the
+locations and weights ("Deformable DETR walkthrough", section 2.2.4):
+
+    ms_deform_attn_fused(value, spatial_shapes, level_start_index,
+                         reference_points, sampling_offsets, attention_logits)
+
+    reference_points    [bs, num_queries, num_levels, 2 or 4]
+    sampling_offsets    like sampling_locations
+    attention_logits    like attention_weights (softmax over levels * points)
+
+and differentiates with respect to value, sampling_offsets and
+attention_logits (reference points get no gradient).
+
 This module only marshals arguments: PyTorch supplies device memory and the
 current stream, the HIP library computes.  The shape tensors are read on the
 host (a device copy is fetched once per call, which synchronises).
@@ -146,3 +159,87 @@ def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_locations,
     """Differentiable MSDeformAttn core (see the module docstring)."""
     return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index,
                                       sampling_locations, attention_weights)
+
+
+def _check_fused(value, reference_points, sampling_offsets, attention_logits):
+    dev, dt = value.device, value.dtype
+    bs, K, M, D = value.shape
+    _, Q, _, L, P, _ = sampling_offsets.shape
+    _check(value, "value", dt, dev)
+    _check(sampling_offsets, "sampling_offsets", dt, dev)
+    _check(attention_logits, "attention_logits", dt, dev, (bs, Q, M, L, P))
+    if reference_points.dim() != 4 or reference_points.shape[-1] not in (2, 4):
+        raise ValueError("reference_points must be [bs, num_queries, num_levels, 2 or 4]")
+    _check(reference_points, "reference_points", dt, dev, (bs, Q, L, reference_points.shape[-1]))
+    return int(reference_points.shape[-1])
+
+
+def forward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                  attention_logits, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One msda_forward_fused call on the current stream; returns output."""
+    prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_offsets)
+    ref_dims = _check_fused(value, reference_points, sampling_offsets, attention_logits)
+    bs, K, M, D = value.shape
+    Q = sampling_offsets.shape[1]
+    if out is None:
+        out = torch.empty((bs, Q, M * D), dtype=value.dtype, device=value.device)
+    _check(out, "output", value.dtype, value.device, (bs, Q, M * D))
+    _lib.forward_fused(prob, ref_dims, value.data_ptr(), reference_points.data_ptr(),
+                       sampling_offsets.data_ptr(), attention_logits.data_ptr(), out.data_ptr(),
+                       _stream(value.device))
+    return out
+
+
+def backward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                   attention_logits, grad_output, grads=None, workspace: torch.Tensor | None = None):
+    """One msda_backward_fused call on the current stream; returns
+    (grad_value, grad_sampling_offsets, grad_attention_logits)."""
+    prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_offsets)
+    ref_dims = _check_fused(value, reference_points, sampling_offsets, attention_logits)
+    dev, dt = value.device, value.dtype
+    bs, K, M, D = value.shape
+    Q = sampling_offsets.shape[1]
+    _check(grad_output, "grad_output", dt, dev, (bs, Q, M * D))
+    if grads is None:
+        grads = (torch.empty_like(value), torch.empty_like(sampling_offsets),
+                 torch.empty_like(attention_logits))
+    gv, go, gl = grads
+    _check(gv, "grad_value", dt, dev, value.shape)
+    _check(go, "grad_sampling_offsets", dt, dev, sampling_offsets.shape)
+    _check(gl, "grad_attention_logits", dt, dev, attention_logits.shape)
+    need = _lib.workspace_bytes(prob)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if (need > 0) else 0
+    _lib.backward_fused(prob, ref_dims, value.data_ptr(), reference_points.data_ptr(),
+                        sampling_offsets.data_ptr(), attention_logits.data_ptr(), grad_output.data_ptr(),
+                        gv.data_ptr(), go.data_ptr(), gl.data_ptr(), ws_ptr, need, _stream(dev))
+    return gv, go, gl
+
+
+class MSDeformAttnFusedFunction(torch.autograd.Function):
+    """Autograd wrapper: forward = msda_forward_fused, backward = msda_backward_fused."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                attention_logits):
+        shapes = _host_int64(spatial_shapes)
+        starts = _host_int64(level_start_index)
+        out = forward_fused(value, shapes, starts, reference_points, sampling_offsets, attention_logits)
+        ctx.save_for_backward(value, reference_points, sampling_offsets, attention_logits)
+        ctx.host_shapes = (shapes, starts)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, ref, off, logits = ctx.saved_tensors
+        shapes, starts = ctx.host_shapes
+        gv, go, gl = backward_fused(value, shapes, starts, ref, off, logits, grad_output.contiguous())
+        return gv, None, None, None, go, gl
+
+
+def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                         attention_logits):
+    """Differentiable MSDeformAttn core with the fused prologue (see the module docstring)."""
+    return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index, reference_points,
+                                           sampling_offsets, attention_logits)

@@ -216,3 +216,100 @@ NAMED = {
     "large_batch_encoder": large_batch_encoder,
     "max_constraint": max_constraint,
 }
+
+
+# --- inputs of the fused prologue ----------------------------------------------
+
+@dataclass
+class FusedWorkload:
+    """Inputs of the fused form: reference points, raw sampling offsets and
+    attention logits instead of locations and weights (host tensors)."""
+
+    name: str
+    dtype: str
+    spatial_shapes: np.ndarray       # int64 [L, 2] = (H, W)
+    level_start_index: np.ndarray    # int64 [L]
+    value: torch.Tensor              # [bs, K, M, D]
+    reference_points: torch.Tensor   # [bs, Q, L, 2 or 4]
+    sampling_offsets: torch.Tensor   # [bs, Q, M, L, P, 2]
+    attention_logits: torch.Tensor   # [bs, Q, M, L, P]
+    grad_output: torch.Tensor        # [bs, Q, M*D]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def ref_dims(self) -> int:
+        return int(self.reference_points.shape[-1])
+
+    def f32(self, name: str) -> np.ndarray:
+        return getattr(self, name).to(torch.float32).numpy()
+
+
+def offset_directions(heads: int, levels: int, points: int) -> np.ndarray:
+    """[M, L, P, 2] pixel offsets of the module's initial sampling pattern
+    (walkthrough section 2.2.4, _reset_parameters): head m looks along the
+    angle 2 pi m / M, its direction scaled so that the larger component is
+    1, and point p goes p + 1 steps along it, on every level."""
+    th = np.arange(heads) * (2.0 * np.pi / heads)
+    d = np.stack([np.cos(th), np.sin(th)], -1)
+    d = d / np.abs(d).max(-1, keepdims=True)
+    steps = np.arange(1, points + 1, dtype=np.float64)
+    return np.broadcast_to(d[:, None, None, :] * steps[None, None, :, None], (heads, levels, points, 2)).copy()
+
+
+def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries: int,
+               dtype: str, seed: int, ref_dims: int = 2, ref_dist: str = "uniform",
+               offset_sigma: float = 1.0, meta: dict | None = None) -> FusedWorkload:
+    """Seeded inputs of the fused form.
+
+    ref_dist:  "encoder" the pixel centre of query q (queries = keys), the
+                         same on every level (valid ratios 1), as the encoder's
+                         get_reference_points gives;
+               "uniform" U[0,1]^2 per query, the same on every level (the
+                         decoder's reference points).
+    ref_dims 4 appends a box size U[0.05, 0.5]^2 per query.
+    Offsets: the initial sampling pattern (offset_directions) plus
+    N(0, offset_sigma) pixels per sample -- the 4-d form reads the same
+    numbers in units of P half box sizes.  Logits: N(0, 1).
+    Draw order: value, reference points, box sizes, offsets, logits,
+    grad_output.
+    """
+    shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
+    L = shapes.shape[0]
+    K = int((shapes[:, 0] * shapes[:, 1]).sum())
+    M, D, P, Q = heads, dims, points, queries
+    rng = np.random.default_rng(seed)
+    value = rng.standard_normal((bs, K, M, D))
+    if ref_dist == "encoder":
+        if Q != K:
+            raise ValueError("encoder reference points need queries == keys")
+        xy = np.broadcast_to(pixel_centre_refs(shapes)[None], (bs, Q, 2))
+    elif ref_dist == "uniform":
+        xy = rng.random((bs, Q, 2))
+    else:
+        raise ValueError(ref_dist)
+    ref = np.broadcast_to(xy[:, :, None, :], (bs, Q, L, 2))
+    if ref_dims == 4:
+        wh = rng.uniform(0.05, 0.5, size=(bs, Q, 2))
+        ref = np.concatenate([ref, np.broadcast_to(wh[:, :, None, :], (bs, Q, L, 2))], -1)
+    elif ref_dims != 2:
+        raise ValueError(ref_dims)
+    off = offset_directions(M, L, P)[None, None] + rng.normal(0.0, offset_sigma, size=(bs, Q, M, L, P, 2))
+    logits = rng.standard_normal((bs, Q, M, L, P))
+    g = rng.standard_normal((bs, Q, M * D))
+    return FusedWorkload(name=name, dtype=dtype, spatial_shapes=shapes, level_start_index=level_starts(shapes),
+                         value=_cast(value, dtype), reference_points=_cast(ref, dtype),
+                         sampling_offsets=_cast(off, dtype), attention_logits=_cast(logits, dtype),
+                         grad_output=_cast(g, dtype), meta=dict(meta or {}, seed=seed))
+
+
+def detr_encoder_fused(bs: int = 2, dtype: str = "f32", seed: int = 1012) -> FusedWorkload:
+    """The DETR encoder shapes in the fused form: pixel-centre reference
+    points (2-d), offsets around the initial pattern, logits."""
+    K = sum(h * w for h, w in DETR_LEVELS)
+    return make_fused("detr_encoder_fused", bs, DETR_LEVELS, 8, 32, 4, K, dtype, seed, 2, "encoder")
+
+
+def detr_decoder_fused(dtype: str = "f32", ref_dims: int = 4, seed: int = 1013) -> FusedWorkload:
+    """The DETR decoder shapes in the fused form (bs 2, 300 queries), with
+    4-d box reference points (two-stage / box refinement) by default."""
+    return make_fused("detr_decoder_fused", 2, DETR_LEVELS, 8, 32, 4, 300, dtype, seed, ref_dims, "uniform")

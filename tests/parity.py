@@ -96,3 +96,52 @@ def check_backward(wl, grads=None):
     assert_close(f"{wl.name}/{wl.dtype}/grad_sampling_locations", f64(gl), rgl, rtol, arms, atol)
     assert_close(f"{wl.name}/{wl.dtype}/grad_value", f64(gv), rgv, rtol, arms, atol)
     return gv, gl, gw
+
+
+# ---- fused prologue ---------------------------------------------------------------
+
+def fused_to_device(wl, device="cuda"):
+    return dict(value=wl.value.to(device), ref=wl.reference_points.to(device),
+                off=wl.sampling_offsets.to(device), logits=wl.attention_logits.to(device),
+                g=wl.grad_output.to(device))
+
+
+def gpu_forward_fused(wl, t=None):
+    from scale_deformable_attention_03_amd import ops
+    t = t or fused_to_device(wl)
+    out = ops.forward_fused(t["value"], wl.spatial_shapes, wl.level_start_index, t["ref"], t["off"], t["logits"])
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_backward_fused(wl, t=None):
+    from scale_deformable_attention_03_amd import ops
+    t = t or fused_to_device(wl)
+    grads = ops.backward_fused(t["value"], wl.spatial_shapes, wl.level_start_index, t["ref"], t["off"],
+                               t["logits"], t["g"])
+    torch.cuda.synchronize()
+    return grads
+
+
+def oracle_fused_args(wl):
+    return (wl.f32("value"), wl.spatial_shapes, wl.level_start_index, wl.f32("reference_points"),
+            wl.f32("sampling_offsets"), wl.f32("attention_logits"))
+
+
+def check_forward_fused(wl, out=None):
+    out = gpu_forward_fused(wl) if out is None else out
+    rtol, arms, atol = TOL[(wl.dtype, "fwd")]
+    assert_close(f"{wl.name}/{wl.dtype}/ref{wl.ref_dims}/output", f64(out),
+                 oracle.forward_fused(*oracle_fused_args(wl)), rtol, arms, atol)
+    return out
+
+
+def check_backward_fused(wl, grads=None):
+    gv, goff, glog = gpu_backward_fused(wl) if grads is None else grads
+    rgv, rgoff, rglog = oracle.backward_fused(*oracle_fused_args(wl), wl.f32("grad_output"))
+    rtol, arms, atol = TOL[(wl.dtype, "bwd")]
+    tag = f"{wl.name}/{wl.dtype}/ref{wl.ref_dims}"
+    assert_close(f"{tag}/grad_attention_logits", f64(glog), rglog, rtol, arms, atol)
+    assert_close(f"{tag}/grad_sampling_offsets", f64(goff), rgoff, rtol, arms, atol)
+    assert_close(f"{tag}/grad_value", f64(gv), rgv, rtol, arms, atol)
+    return gv, goff, glog
