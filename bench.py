@@ -15,7 +15,11 @@ Default workload: Deformable-DETR encoder self-attention, fp32, bs 2, levels
 Prints one JSON line: queries/s (bs * num_queries per step / seconds per
 step), plus the roofline of the dominant kernel (algorithmic bytes per launch
 over its HIP-event-timed average duration against 8 TB/s) and the CPU oracle
-timed on the host cores as a reported baseline.
+timed on the host cores as a reported baseline.  A second object,
+"fused_prologue", times the fused form on the same shapes (reference points,
+offsets and logits in; msda_forward_fused + msda_backward_fused) beside the
+module path it replaces (PyTorch ops for the locations and the softmax and
+their backward around the core).
 """
 from __future__ import annotations
 
@@ -239,6 +243,77 @@ def cpu_baseline(wl, seconds: float) -> dict:
                       f"{dt:.1f} s, float64 scalar C with OpenMP"}
 
 
+def fused_prologue_leg(wl_core, dev, steps: int, warmup: int, nsets: int) -> dict:
+    """The fused form on the same shapes (msda_forward_fused +
+    msda_backward_fused: reference points, offsets and logits in, offset and
+    logit gradients out) against the module path it replaces: PyTorch forms
+    the locations and the softmax, the core runs through the C ABI, and
+    autograd carries the gradients back through PyTorch's ops."""
+    import torch
+    from scale_deformable_attention_03_amd import _lib, ops
+    from scale_deformable_attention_03_amd import workloads as W
+
+    bs, K, M, D = wl_core.value.shape
+    Q, L, P = wl_core.sampling_locations.shape[1], wl_core.sampling_locations.shape[3], \
+        wl_core.sampling_locations.shape[4]
+    ref_dist = "encoder" if Q == K else "uniform"
+    wl = W.make_fused(wl_core.name + "_fused", bs, wl_core.spatial_shapes, M, D, P, Q, wl_core.dtype,
+                      seed=1012, ref_dims=2, ref_dist=ref_dist)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_offsets)
+    need_ws = _lib.workspace_bytes(prob)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    sets = []
+    for _ in range(nsets):
+        s = dict(value=wl.value.to(dev), ref=wl.reference_points.to(dev), off=wl.sampling_offsets.to(dev),
+                 lg=wl.attention_logits.to(dev), g=wl.grad_output.to(dev))
+        s["out"] = torch.empty(bs, Q, M * D, dtype=wl.value.dtype, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["goff"] = torch.empty_like(s["off"])
+        s["glg"] = torch.empty_like(s["lg"])
+        s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
+        s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
+        sets.append(s)
+
+    def fused(s):
+        p = s["ptr"]
+        _lib.forward_fused(prob, 2, p["value"], p["ref"], p["off"], p["lg"], p["out"], sp)
+        _lib.backward_fused(prob, 2, p["value"], p["ref"], p["off"], p["lg"], p["g"], p["gv"], p["goff"],
+                            p["glg"], p["ws"] if need_ws else 0, need_ws, sp)
+
+    shapes = torch.as_tensor(wl.spatial_shapes, device=dev)
+    norm = torch.stack([shapes[:, 1], shapes[:, 0]], -1).to(wl.value.dtype)
+
+    def module_path(s):
+        off = s["off"].detach().requires_grad_()
+        lg = s["lg"].detach().requires_grad_()
+        loc = s["ref"][:, :, None, :, None, :] + off / norm[None, None, None, :, None, :]
+        w = torch.softmax(lg.view(bs, Q, M, L * P), -1).view(bs, Q, M, L, P)
+        out = ops.MSDeformAttnFunction.apply(s["value"], wl.spatial_shapes, wl.level_start_index,
+                                             loc.contiguous(), w.contiguous())
+        out.backward(s["g"])
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(sets[i % nsets])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    fused_ms = timed(fused)
+    module_ms = timed(module_path)
+    log(f"[bench] fused prologue: {fused_ms * 1e3:.1f} us/step; module path {module_ms * 1e3:.1f} us/step")
+    return {"workload": wl.name, "reference_points": "2-d", "fused_ms_per_step": round(fused_ms, 5),
+            "fused_queries_per_s": round(bs * Q / (fused_ms * 1e-3), 1),
+            "module_path_ms_per_step": round(module_ms, 5),
+            "speedup_vs_module_path": round(module_ms / fused_ms, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +324,7 @@ def main() -> int:
                              "tiny_single_level"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
     ap.add_argument("--ingest-profiles", metavar="DIR",
                     help="summarise the rocprofv3 output of the profiling commands under DIR into profiles/ "
                          "(no GPU needed) and exit")
@@ -422,6 +498,9 @@ def main() -> int:
         "kernel_digest": digest,
         "roofline": roofline,
     }
+    if not args.no_fused:
+        result["fused_prologue"] = fused_prologue_leg(wl, dev, max(10, args.steps // 2), max(2, args.warmup // 2),
+                                                      nsets)
     if args.no_cpu_baseline:
         result["cpu_baseline"] = None
     else:
