@@ -277,8 +277,8 @@ def fused_prologue_leg(wl_core, dev, steps: int, warmup: int, nsets: int) -> dic
 
     def fused(s):
         p = s["ptr"]
-        _lib.forward_fused(prob, 2, p["value"], p["ref"], p["off"], p["lg"], p["out"], sp)
-        _lib.backward_fused(prob, 2, p["value"], p["ref"], p["off"], p["lg"], p["g"], p["gv"], p["goff"],
+        _lib.forward_fused(prob, 2, p["value"], 0, p["ref"], p["off"], p["lg"], p["out"], sp)
+        _lib.backward_fused(prob, 2, p["value"], 0, p["ref"], p["off"], p["lg"], p["g"], p["gv"], p["goff"],
                             p["glg"], p["ws"] if need_ws else 0, need_ws, sp)
 
     shapes = torch.as_tensor(wl.spatial_shapes, device=dev)

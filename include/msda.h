@@ -256,12 +256,18 @@ msda_status_t msda_backward_profile(const msda_problem_t *problem,
  *                     (x, y), in pixels of the level (2-d) or in units of
  *                     P half-box sizes (4-d)
  *   attention_logits  [batch, num_queries, num_heads, num_levels, num_points]
+ *   key_padding_mask  NULL (no padding) or device uint8 [batch, num_keys]:
+ *                     nonzero marks a padded key, whose value row the module
+ *                     fills with zeros before the core (section 2.2.4,
+ *                     masked_fill), so the kernels read it as zero; no
+ *                     alignment needed
  * ref_dims must be 2 or 4 (MSDA_ERROR_INVALID_VALUE otherwise).  Pointers,
  * ownership, streams and errors as for msda_forward.
  */
 msda_status_t msda_forward_fused(const msda_problem_t *problem,
                                  int32_t ref_dims,
                                  const void *value,
+                                 const uint8_t *key_padding_mask,
                                  const void *reference_points,
                                  const void *sampling_offsets,
                                  const void *attention_logits,
@@ -282,12 +288,16 @@ msda_status_t msda_forward_fused(const msda_problem_t *problem,
  *                            the gradient of the weights as in msda_backward
  *                            (a sample off the map has g = 0 but still
  *                            receives the second term)
+ * With a key_padding_mask the rows of padded keys read as zero in every
+ * gradient, and their grad_value rows are zero (the gradient of the
+ * zero-fill).
  * Same workspace (msda_backward_workspace_bytes), kernels, ownership and
  * error codes as msda_backward; all three gradients are overwritten.
  */
 msda_status_t msda_backward_fused(const msda_problem_t *problem,
                                   int32_t ref_dims,
                                   const void *value,
+                                  const uint8_t *key_padding_mask,
                                   const void *reference_points,
                                   const void *sampling_offsets,
                                   const void *attention_logits,

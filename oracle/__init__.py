@@ -181,13 +181,26 @@ def softmax_weights(attention_logits) -> np.ndarray:
     return (e / e.sum(axis=-1, keepdims=True)).reshape(bs, Q, M, L, P)
 
 
+def masked_value(value, key_padding_mask) -> np.ndarray:
+    """The module's zero-fill of padded keys (section 2.2.4,
+    value.masked_fill(input_padding_mask[..., None], 0)): rows (b, k, :, :)
+    with a nonzero mask byte become zero."""
+    value = _f32(value)
+    if key_padding_mask is None:
+        return value
+    m = np.asarray(key_padding_mask).astype(bool)
+    if m.shape != value.shape[:2]:
+        raise ValueError("key_padding_mask must be [bs, num_keys]")
+    return np.where(m[:, :, None, None], np.float32(0), value).astype(np.float32)
+
+
 def forward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                  attention_logits, nthreads: int = 0) -> np.ndarray:
-    """Oracle of the fused forward: locations and weights as above, then the
-    core (``forward``)."""
+                  attention_logits, key_padding_mask=None, nthreads: int = 0) -> np.ndarray:
+    """Oracle of the fused forward: padded keys zeroed, locations and weights
+    as above, then the core (``forward``)."""
     loc = sampling_locations_from(reference_points, sampling_offsets, spatial_shapes)
     w = softmax_weights(attention_logits)
-    return forward(value, spatial_shapes, level_start_index, loc, w, nthreads)
+    return forward(masked_value(value, key_padding_mask), spatial_shapes, level_start_index, loc, w, nthreads)
 
 
 def location_jacobian(reference_points, spatial_shapes, num_heads: int, num_points: int) -> np.ndarray:
@@ -205,7 +218,7 @@ def location_jacobian(reference_points, spatial_shapes, num_heads: int, num_poin
 
 
 def backward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                   attention_logits, grad_output, nthreads: int = 0):
+                   attention_logits, grad_output, key_padding_mask=None, nthreads: int = 0):
     """Oracle of the fused backward; returns float64
     ``(grad_value, grad_sampling_offsets, grad_attention_logits)``.
 
@@ -213,11 +226,16 @@ def backward_fused(value, spatial_shapes, level_start_index, reference_points, s
     then the chain rule through the prologue: the location gradient times
     d loc / d offset, and the softmax's backward,
     d L / d logit_i = w_i * (g_i - sum_k w_k g_k) over the head's L*P entries,
-    g being the gradient of the weights.
+    g being the gradient of the weights.  With a key padding mask the core
+    sees the zero-filled value, and the zero-fill passes no gradient to the
+    padded rows.
     """
     loc = sampling_locations_from(reference_points, sampling_offsets, spatial_shapes)
     w = softmax_weights(attention_logits)
-    gv, gl, gw = backward(value, spatial_shapes, level_start_index, loc, w, grad_output, nthreads)
+    gv, gl, gw = backward(masked_value(value, key_padding_mask), spatial_shapes, level_start_index, loc, w,
+                          grad_output, nthreads)
+    if key_padding_mask is not None:
+        gv = np.where(np.asarray(key_padding_mask).astype(bool)[:, :, None, None], 0.0, gv)
     bs, Q, M, L, P, _ = gl.shape
     goff = gl * location_jacobian(reference_points, spatial_shapes, M, P)
     wf, gf = w.reshape(bs, Q, M, L * P), gw.reshape(bs, Q, M, L * P)

@@ -87,9 +87,9 @@ def _load():
     lib.msda_backward_profile.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.msda_backward_profile.restype = ctypes.c_int
     i32 = ctypes.c_int32
-    lib.msda_forward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.msda_forward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.msda_forward_fused.restype = ctypes.c_int
-    lib.msda_backward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msda_backward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward_fused.restype = ctypes.c_int
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
@@ -141,17 +141,18 @@ def backward_profile(problem: Problem, value: int, loc: int, w: int, gout: int, 
         raise MsdaError(st, "msda_backward_profile")
 
 
-def forward_fused(problem: Problem, ref_dims: int, value: int, ref: int, off: int, logits: int, out: int,
-                  stream: int) -> None:
-    st = lib.msda_forward_fused(ctypes.byref(problem), ref_dims, value, ref, off, logits, out, stream)
+def forward_fused(problem: Problem, ref_dims: int, value: int, mask: int, ref: int, off: int, logits: int,
+                  out: int, stream: int) -> None:
+    """mask: device address of the uint8 key padding mask, or 0 for none."""
+    st = lib.msda_forward_fused(ctypes.byref(problem), ref_dims, value, mask, ref, off, logits, out, stream)
     if st != 0:
         raise MsdaError(st, "msda_forward_fused")
 
 
-def backward_fused(problem: Problem, ref_dims: int, value: int, ref: int, off: int, logits: int, gout: int,
-                   gvalue: int, goff: int, glogits: int, workspace: int, workspace_bytes_: int,
+def backward_fused(problem: Problem, ref_dims: int, value: int, mask: int, ref: int, off: int, logits: int,
+                   gout: int, gvalue: int, goff: int, glogits: int, workspace: int, workspace_bytes_: int,
                    stream: int) -> None:
-    st = lib.msda_backward_fused(ctypes.byref(problem), ref_dims, value, ref, off, logits, gout, gvalue,
+    st = lib.msda_backward_fused(ctypes.byref(problem), ref_dims, value, mask, ref, off, logits, gout, gvalue,
                                  goff, glogits, workspace, workspace_bytes_, stream)
     if st != 0:
         raise MsdaError(st, "msda_backward_fused")

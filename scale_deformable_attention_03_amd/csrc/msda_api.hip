@@ -300,21 +300,22 @@ size_t fused_lds(int ref_dims, int gpb, int LP) { return ref_dims ? sizeof(float
 template <int DT, int VECB, int LPR>
 struct Fwd {
     static msda_status_t run(const msda::Problem& pb, int ref_dims, const void* v, const void* ref,
-                             const void* loc, const void* w, void* out, hipStream_t st) {
+                             const uint8_t* kmask, const void* loc, const void* w, void* out, hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, 1024);
         const int LP = pb.L * pb.P;
         const size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
         const void* k = ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
                         : ref_dims == 2 ? fwd_kernel<DT, VECB, LPR, 2>(pb)
                                         : fwd_kernel<DT, VECB, LPR, 4>(pb);
-        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, out, pb, gpb);
+        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, kmask, out, pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
 struct Grad {
     static msda_status_t run(const msda::Problem& pb, bool binned, int ref_dims, const void* v, const void* ref,
-                             const void* loc, const void* w, const void* gout, float* gacc, uint3* recs,
+                             const uint8_t* kmask, const void* loc, const void* w, const void* gout, float* gacc,
+                             uint3* recs,
                              int32_t* cursor, int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
                              hipStream_t st) {
         const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
@@ -331,23 +332,23 @@ struct Grad {
             k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, false, 0>(pb)
                 : ref_dims == 2 ? grad_kernel<DT, VECB, LPR, false, 2>(pb)
                                 : grad_kernel<DT, VECB, LPR, false, 4>(pb);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, ref, gout, gacc, recs, cursor, nunits, multi,
-                      gloc, gw, pb, gpb);
+        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, ref, kmask, gout, gacc, recs, cursor, nunits,
+                      multi, gloc, gw, pb, gpb);
     }
 };
 
 template <int DT, int VECB, int LPR>
 struct Accum {
     static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
-                             const uint3* recs, const int32_t* nunits, const int4* units, float* gacc,
-                             void* gfinal, hipStream_t st) {
+                             const uint3* recs, const int32_t* nunits, const int4* units, const uint8_t* kmask,
+                             float* gacc, void* gfinal, hipStream_t st) {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
                            sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
                            2 * sizeof(int32_t) * msda::kMaxSegKeys;
         return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::acc_block(LPR), lds, st,
-                      gout, recs, nunits, units, gacc, gfinal, pb, plane_units);
+                      gout, recs, nunits, units, kmask, gacc, gfinal, pb, plane_units);
     }
 };
 
@@ -377,8 +378,8 @@ msda_status_t check_ref(const msda_problem_t* p, int ref_dims, const void* ref) 
 }
 
 msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
-                           const void* sampling_locations, const void* attention_weights, void* output,
-                           hipStream_t stream) {
+                           const uint8_t* kmask, const void* sampling_locations, const void* attention_weights,
+                           void* output, hipStream_t stream) {
     MSDA_TRY(check_problem(problem));
     MSDA_TRY(check_ref(problem, ref_dims, ref));
     MSDA_TRY(check_ptr(value, value_elems(problem)));
@@ -388,8 +389,8 @@ msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const vo
     if (out_elems(problem) == 0) return MSDA_SUCCESS;
     const msda::Problem pb = pack(problem);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    return by_dtype_split<Fwd>(problem->dtype, s, pb, ref_dims, value, ref, sampling_locations, attention_weights,
-                               output, stream);
+    return by_dtype_split<Fwd>(problem->dtype, s, pb, ref_dims, value, ref, kmask, sampling_locations,
+                               attention_weights, output, stream);
 }
 
 msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
@@ -426,8 +427,9 @@ msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
 // ref_dims != 0: the fused prologue (loc and w are the offsets and logits,
 // gloc and gw receive their gradients).
 msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
-                            const void* loc, const void* w, const void* gout, float* gacc, void* gfinal, void* gloc,
-                            void* gw, char* ws, int accumulate, hipEvent_t* ev, hipStream_t st) {
+                            const uint8_t* kmask, const void* loc, const void* w, const void* gout, float* gacc,
+                            void* gfinal, void* gloc, void* gw, char* ws, int accumulate, hipEvent_t* ev,
+                            hipStream_t st) {
     const bool narrow16 = !accumulate && problem->dtype != MSDA_F32;
     if (sample_elems(problem) == 0) {
         // no samples (Q = 0): grad_value is zero and nothing else is written
@@ -447,7 +449,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
         MSDA_TRY(mark(ev, kStageCount, st));
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
-        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, ref_dims, value, ref, loc, w, gout, gacc,
+        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, ref_dims, value, ref, kmask, loc, w, gout, gacc,
                                       static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
                                       static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
                                       gloc, gw, st));
@@ -482,13 +484,14 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
                     static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb,
                     static_cast<int>(plane_records(problem)), static_cast<int>(plane_units(problem, pb))));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, ref_dims, value, ref, loc, w, gout, gacc, recs, cursor,
+    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs,
+                                  cursor,
                                   nunits, static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
     MSDA_TRY(by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
                                    gout, static_cast<const uint3*>(recs), static_cast<const int32_t*>(nunits),
-                                   static_cast<const int4*>(units), gacc, narrow16 ? gfinal : nullptr, st));
+                                   static_cast<const int4*>(units), kmask, gacc, narrow16 ? gfinal : nullptr, st));
     MSDA_TRY(mark(ev, kStageNarrow, st));
     if (narrow16) {
         const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_segments_kernel<kF16>)
@@ -501,7 +504,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
 }
 
 msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
-                            const void* sampling_locations, const void* attention_weights,
+                            const uint8_t* kmask, const void* sampling_locations, const void* attention_weights,
                             const void* grad_output, void* grad_value, void* grad_sampling_locations,
                             void* grad_attention_weights, void* workspace, size_t workspace_bytes, hipEvent_t* ev,
                             hipStream_t stream) {
@@ -520,8 +523,8 @@ msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const v
     const Layout lay = layout(problem, pack(problem));
     float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
                                              : reinterpret_cast<float*>(ws + lay.acc);
-    MSDA_TRY(backward_into(problem, ref_dims, value, ref, sampling_locations, attention_weights, grad_output, gacc,
-                           grad_value, grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
+    MSDA_TRY(backward_into(problem, ref_dims, value, ref, kmask, sampling_locations, attention_weights, grad_output,
+                           gacc, grad_value, grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
     return mark(ev, kStageEnd, stream);
 }
 
@@ -547,15 +550,16 @@ const char* msda_status_string(msda_status_t status) {
 msda_status_t msda_forward(const msda_problem_t* problem, const void* value,
                            const void* sampling_locations, const void* attention_weights,
                            void* output, hipStream_t stream) {
-    return forward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, output, stream);
+    return forward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, output, stream);
 }
 
 msda_status_t msda_forward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
-                                 const void* reference_points, const void* sampling_offsets,
-                                 const void* attention_logits, void* output, hipStream_t stream) {
+                                 const uint8_t* key_padding_mask, const void* reference_points,
+                                 const void* sampling_offsets, const void* attention_logits, void* output,
+                                 hipStream_t stream) {
     if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
-    return forward_call(problem, ref_dims, value, reference_points, sampling_offsets, attention_logits, output,
-                        stream);
+    return forward_call(problem, ref_dims, value, reference_points, key_padding_mask, sampling_offsets,
+                        attention_logits, output, stream);
 }
 
 size_t msda_backward_workspace_bytes(const msda_problem_t* problem) {
@@ -569,18 +573,20 @@ msda_status_t msda_backward(const msda_problem_t* problem, const void* value,
                             const void* grad_output, void* grad_value,
                             void* grad_sampling_locations, void* grad_attention_weights,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return backward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+    return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
                          nullptr, stream);
 }
 
 msda_status_t msda_backward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
-                                  const void* reference_points, const void* sampling_offsets,
-                                  const void* attention_logits, const void* grad_output, void* grad_value,
-                                  void* grad_sampling_offsets, void* grad_attention_logits, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+                                  const uint8_t* key_padding_mask, const void* reference_points,
+                                  const void* sampling_offsets, const void* attention_logits,
+                                  const void* grad_output, void* grad_value, void* grad_sampling_offsets,
+                                  void* grad_attention_logits, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
     if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
-    return backward_call(problem, ref_dims, value, reference_points, sampling_offsets, attention_logits,
+    return backward_call(problem, ref_dims, value, reference_points, key_padding_mask, sampling_offsets,
+                         attention_logits,
                          grad_output, grad_value, grad_sampling_offsets, grad_attention_logits, workspace,
                          workspace_bytes, nullptr, stream);
 }
@@ -592,7 +598,7 @@ msda_status_t msda_backward_profile(const msda_problem_t* problem, const void* v
                                     void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
                                     hipStream_t stream) {
     if (stage_events == nullptr) return MSDA_ERROR_INVALID_VALUE;
-    return backward_call(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+    return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
                          stage_events, stream);
 }
@@ -611,7 +617,7 @@ msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void
         MSDA_TRY(check_ptr(workspace, 1));
     }
     if (value_elems(problem) == 0) return MSDA_SUCCESS;
-    return backward_into(problem, 0, value, nullptr, sampling_locations, attention_weights, grad_output,
+    return backward_into(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value_acc, nullptr, grad_sampling_locations, grad_attention_weights,
                          static_cast<char*>(workspace), 1, nullptr, stream);
 }

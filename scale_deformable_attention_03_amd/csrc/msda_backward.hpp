@@ -408,7 +408,8 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
-                     const void* __restrict__ attw, const void* __restrict__ ref, const void* __restrict__ gout,
+                     const void* __restrict__ attw, const void* __restrict__ ref,
+                     const uint8_t* __restrict__ kmask, const void* __restrict__ gout,
                      float* __restrict__ gacc, uint3* __restrict__ recs, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
@@ -453,7 +454,10 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
         const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(W), static_cast<float>(H),
                                                    static_cast<float>(P));
-        const Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
+        Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
+        // padded corners read as zero; their records still go to the
+        // accumulation, which writes padded rows as zero
+        mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, W);
         float aw;
         if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         else aw = se[i] / group_total(se + g * LP, LP);
@@ -681,8 +685,8 @@ __device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 template <int DT, int VECB, int LPR>
 __global__ void __launch_bounds__(acc_block(LPR), DT == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
-                       const int32_t* __restrict__ nunits,
-                       const int4* __restrict__ units, float* __restrict__ gacc, void* __restrict__ gfinal,
+                       const int32_t* __restrict__ nunits, const int4* __restrict__ units,
+                       const uint8_t* __restrict__ kmask, float* __restrict__ gacc, void* __restrict__ gfinal,
                        Problem pb, int plane_units) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
@@ -869,10 +873,19 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     // lane, float32 into gacc, or for 16-bit dtypes 8 elements rounded once
     // straight into grad_value (gfinal).
     const int64_t row0 = (static_cast<int64_t>(b) * pb.K + pb.lv.start[lvl] + k0) * pb.M + m;
+    // rows of padded keys (the module zero-fills them, so their gradient is
+    // zero) are written as zeros
+    const uint8_t* km = kmask ? kmask + static_cast<int64_t>(b) * pb.K + pb.lv.start[lvl] + k0 : nullptr;
+    if (km != nullptr) {                             // uniform: a kernel argument
+        for (int i = threadIdx.x; i < nk * D; i += kAccBlock)
+            if (km[i / D] != 0) tile[i] = 0.0f;
+        __syncthreads();
+    }
     if (unit.w) {
         for (int i = threadIdx.x; i < nk * D; i += kAccBlock) {
             const int k = i / D, d = i - k * D;
-            atomic_add_f32(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + d, tile[i]);
+            if (km == nullptr || km[k] == 0)
+                atomic_add_f32(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + d, tile[i]);
         }
     } else if constexpr (DT == kF32) {
         const int q4 = D / 4;

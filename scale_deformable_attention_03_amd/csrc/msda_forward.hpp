@@ -61,6 +61,20 @@ __device__ __forceinline__ Corners sample_corners(float loc_x, float loc_y, int 
     return c;
 }
 
+// Key padding: the module fills the value rows of padded keys with zeros
+// before the core ("Deformable DETR walkthrough", section 2.2.4,
+// MSDeformAttn.forward), so a corner on a padded key reads as zero, exactly
+// like a corner off the map.  km: the batch's num_keys mask bytes (nonzero =
+// padded), or null for no padding.
+__device__ __forceinline__ void mask_corners(Corners& c, const uint8_t* km, int start, int W) {
+    if (km == nullptr || !c.ok) return;
+    const int row = start + c.y0 * W + c.x0;          // in the map whenever o00 is
+    if (c.o00 != kOffMap && km[row] != 0) c.o00 = kOffMap;
+    if (c.o01 != kOffMap && km[row + 1] != 0) c.o01 = kOffMap;
+    if (c.o10 != kOffMap && km[row + W] != 0) c.o10 = kOffMap;
+    if (c.o11 != kOffMap && km[row + W + 1] != 0) c.o11 = kOffMap;
+}
+
 // Plane-local workgroup: queries q0 .. q0 + gcount - 1 of plane (b, m).
 struct PlaneTile {
     int b, m, q0, gcount, pl;
@@ -94,12 +108,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value,
 // LDS: gpb * (8 * L * P + 4) words, plus 2 * gpb * L * P when REF != 0.
 // REF = 0: loc and attw are the sampling locations and attention weights;
 // REF = 2 or 4: they are the sampling offsets and attention logits, and ref
-// holds the reference points (see sample_location).
+// holds the reference points (see sample_location).  kmask: [bs, K] key
+// padding bytes or null (see mask_corners).
 template <int DT, int VECB, int LPR, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
-                    const void* __restrict__ attw, const void* __restrict__ ref, void* __restrict__ out,
-                    Problem pb, int gpb) {
+                    const void* __restrict__ attw, const void* __restrict__ ref,
+                    const uint8_t* __restrict__ kmask, void* __restrict__ out, Problem pb, int gpb) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     const int L = L_CT ? L_CT : pb.L;
@@ -130,7 +145,8 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
         const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
                                                    static_cast<float>(lv.x), static_cast<float>(P));
-        const Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
+        Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
+        mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
         float aw;
         if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
         else aw = c.ok ? se[i] / group_total(se + g * LP, LP) : 0.0f;

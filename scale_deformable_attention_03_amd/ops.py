@@ -22,14 +22,17 @@ The fused form takes what MSDeformAttn.forward has before it forms the
 locations and weights ("Deformable DETR walkthrough", section 2.2.4):
 
     ms_deform_attn_fused(value, spatial_shapes, level_start_index,
-                         reference_points, sampling_offsets, attention_logits)
+                         reference_points, sampling_offsets, attention_logits,
+                         key_padding_mask=None)
 
     reference_points    [bs, num_queries, num_levels, 2 or 4]
     sampling_offsets    like sampling_locations
     attention_logits    like attention_weights (softmax over levels * points)
+    key_padding_mask    None or bool/uint8 [bs, num_keys], True = padded key
+                        (its value row reads as zero)
 
 and differentiates with respect to value, sampling_offsets and
-attention_logits (reference points get no gradient).
+attention_logits (reference points and the mask get no gradient).
 
 This module only marshals arguments: PyTorch supplies device memory and the
 current stream, the HIP library computes.  The shape tensors are read on the
@@ -161,6 +164,16 @@ def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_locations,
                                       sampling_locations, attention_weights)
 
 
+def _mask_ptr(value, key_padding_mask) -> int:
+    if key_padding_mask is None:
+        return 0
+    bs, K = value.shape[:2]
+    if key_padding_mask.dtype not in (torch.bool, torch.uint8):
+        raise TypeError("key_padding_mask must be bool or uint8")
+    _check(key_padding_mask, "key_padding_mask", key_padding_mask.dtype, value.device, (bs, K))
+    return key_padding_mask.data_ptr()      # bool is stored as one byte, 0 or 1
+
+
 def _check_fused(value, reference_points, sampling_offsets, attention_logits):
     dev, dt = value.device, value.dtype
     bs, K, M, D = value.shape
@@ -175,27 +188,30 @@ def _check_fused(value, reference_points, sampling_offsets, attention_logits):
 
 
 def forward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                  attention_logits, out: torch.Tensor | None = None) -> torch.Tensor:
+                  attention_logits, key_padding_mask=None, out: torch.Tensor | None = None) -> torch.Tensor:
     """One msda_forward_fused call on the current stream; returns output."""
     prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_offsets)
     ref_dims = _check_fused(value, reference_points, sampling_offsets, attention_logits)
+    mask = _mask_ptr(value, key_padding_mask)
     bs, K, M, D = value.shape
     Q = sampling_offsets.shape[1]
     if out is None:
         out = torch.empty((bs, Q, M * D), dtype=value.dtype, device=value.device)
     _check(out, "output", value.dtype, value.device, (bs, Q, M * D))
-    _lib.forward_fused(prob, ref_dims, value.data_ptr(), reference_points.data_ptr(),
+    _lib.forward_fused(prob, ref_dims, value.data_ptr(), mask, reference_points.data_ptr(),
                        sampling_offsets.data_ptr(), attention_logits.data_ptr(), out.data_ptr(),
                        _stream(value.device))
     return out
 
 
 def backward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                   attention_logits, grad_output, grads=None, workspace: torch.Tensor | None = None):
+                   attention_logits, grad_output, key_padding_mask=None, grads=None,
+                   workspace: torch.Tensor | None = None):
     """One msda_backward_fused call on the current stream; returns
     (grad_value, grad_sampling_offsets, grad_attention_logits)."""
     prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_offsets)
     ref_dims = _check_fused(value, reference_points, sampling_offsets, attention_logits)
+    mask = _mask_ptr(value, key_padding_mask)
     dev, dt = value.device, value.dtype
     bs, K, M, D = value.shape
     Q = sampling_offsets.shape[1]
@@ -211,7 +227,7 @@ def backward_fused(value, spatial_shapes, level_start_index, reference_points, s
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if (need > 0) else 0
-    _lib.backward_fused(prob, ref_dims, value.data_ptr(), reference_points.data_ptr(),
+    _lib.backward_fused(prob, ref_dims, value.data_ptr(), mask, reference_points.data_ptr(),
                         sampling_offsets.data_ptr(), attention_logits.data_ptr(), grad_output.data_ptr(),
                         gv.data_ptr(), go.data_ptr(), gl.data_ptr(), ws_ptr, need, _stream(dev))
     return gv, go, gl
@@ -222,24 +238,25 @@ class MSDeformAttnFusedFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                attention_logits):
+                attention_logits, key_padding_mask=None):
         shapes = _host_int64(spatial_shapes)
         starts = _host_int64(level_start_index)
-        out = forward_fused(value, shapes, starts, reference_points, sampling_offsets, attention_logits)
-        ctx.save_for_backward(value, reference_points, sampling_offsets, attention_logits)
+        out = forward_fused(value, shapes, starts, reference_points, sampling_offsets, attention_logits,
+                            key_padding_mask)
+        ctx.save_for_backward(value, reference_points, sampling_offsets, attention_logits, key_padding_mask)
         ctx.host_shapes = (shapes, starts)
         return out
 
     @staticmethod
     def backward(ctx, grad_output):
-        value, ref, off, logits = ctx.saved_tensors
+        value, ref, off, logits, mask = ctx.saved_tensors
         shapes, starts = ctx.host_shapes
-        gv, go, gl = backward_fused(value, shapes, starts, ref, off, logits, grad_output.contiguous())
-        return gv, None, None, None, go, gl
+        gv, go, gl = backward_fused(value, shapes, starts, ref, off, logits, grad_output.contiguous(), mask)
+        return gv, None, None, None, go, gl, None
 
 
 def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                         attention_logits):
+                         attention_logits, key_padding_mask=None):
     """Differentiable MSDeformAttn core with the fused prologue (see the module docstring)."""
     return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index, reference_points,
-                                           sampling_offsets, attention_logits)
+                                           sampling_offsets, attention_logits, key_padding_mask)

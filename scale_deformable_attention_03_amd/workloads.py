@@ -234,6 +234,7 @@ class FusedWorkload:
     sampling_offsets: torch.Tensor   # [bs, Q, M, L, P, 2]
     attention_logits: torch.Tensor   # [bs, Q, M, L, P]
     grad_output: torch.Tensor        # [bs, Q, M*D]
+    key_padding_mask: torch.Tensor | None = None   # bool [bs, K] or None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -256,9 +257,35 @@ def offset_directions(heads: int, levels: int, points: int) -> np.ndarray:
     return np.broadcast_to(d[:, None, None, :] * steps[None, None, :, None], (heads, levels, points, 2)).copy()
 
 
+def padding_masks(shapes, valid) -> tuple[np.ndarray, np.ndarray]:
+    """Key padding of a batch of images padded to one size (walkthrough
+    section 2.1: the backbone downsamples the image mask to every level with
+    F.interpolate, nearest; section 2.2.4: the valid ratios are the unpadded
+    fraction of each level's width and height).
+
+    valid: per batch element, the unpadded fraction (h, w) of the padded
+    image, whose size is 8x the first level's.  Returns the mask
+    [bs, K] (True = padded key) and the valid ratios [bs, L, 2] as (x, y)."""
+    import torch.nn.functional as F
+    shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
+    Hi, Wi = int(shapes[0, 0]) * 8, int(shapes[0, 1]) * 8
+    img = torch.zeros(len(valid), Hi, Wi, dtype=torch.bool)
+    for b, (fh, fw) in enumerate(valid):
+        img[b, int(round(fh * Hi)):, :] = True
+        img[b, :, int(round(fw * Wi)):] = True
+    masks, ratios = [], []
+    for H, W in shapes:
+        m = F.interpolate(img[None].float(), size=(int(H), int(W))).to(torch.bool)[0]     # [bs, H, W]
+        vh = (~m[:, :, 0]).sum(1).double() / float(H)
+        vw = (~m[:, 0, :]).sum(1).double() / float(W)
+        masks.append(m.reshape(len(valid), -1))
+        ratios.append(torch.stack([vw, vh], -1))
+    return torch.cat(masks, 1).numpy(), torch.stack(ratios, 1).numpy()
+
+
 def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries: int,
                dtype: str, seed: int, ref_dims: int = 2, ref_dist: str = "uniform",
-               offset_sigma: float = 1.0, meta: dict | None = None) -> FusedWorkload:
+               offset_sigma: float = 1.0, valid=None, meta: dict | None = None) -> FusedWorkload:
     """Seeded inputs of the fused form.
 
     ref_dist:  "encoder" the pixel centre of query q (queries = keys), the
@@ -267,6 +294,11 @@ def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, q
                "uniform" U[0,1]^2 per query, the same on every level (the
                          decoder's reference points).
     ref_dims 4 appends a box size U[0.05, 0.5]^2 per query.
+    valid (per batch element (h, w) fractions, see padding_masks) adds a key
+    padding mask and scales the reference points by the valid ratios the way
+    the encoder (get_reference_points: pixel centres over the valid extent,
+    times each level's ratio) and the decoder (reference times the ratios;
+    the box by the ratios too) do; None means no padding.
     Offsets: the initial sampling pattern (offset_directions) plus
     N(0, offset_sigma) pixels per sample -- the 4-d form reads the same
     numbers in units of P half box sizes.  Logits: N(0, 1).
@@ -279,18 +311,26 @@ def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, q
     M, D, P, Q = heads, dims, points, queries
     rng = np.random.default_rng(seed)
     value = rng.standard_normal((bs, K, M, D))
+    if valid is not None:
+        if len(valid) != bs:
+            raise ValueError("valid needs one (h, w) pair per batch element")
+        mask, ratios = padding_masks(shapes, valid)
+    else:
+        mask, ratios = None, np.ones((bs, L, 2))
     if ref_dist == "encoder":
         if Q != K:
             raise ValueError("encoder reference points need queries == keys")
-        xy = np.broadcast_to(pixel_centre_refs(shapes)[None], (bs, Q, 2))
+        # pixel centres of each query's own level over that level's valid extent
+        lvl_of_key = np.repeat(np.arange(L), shapes[:, 0] * shapes[:, 1])
+        xy = pixel_centre_refs(shapes)[None] / ratios[:, lvl_of_key, :]          # [bs, K, 2]
     elif ref_dist == "uniform":
         xy = rng.random((bs, Q, 2))
     else:
         raise ValueError(ref_dist)
-    ref = np.broadcast_to(xy[:, :, None, :], (bs, Q, L, 2))
+    ref = xy[:, :, None, :] * ratios[:, None, :, :]
     if ref_dims == 4:
         wh = rng.uniform(0.05, 0.5, size=(bs, Q, 2))
-        ref = np.concatenate([ref, np.broadcast_to(wh[:, :, None, :], (bs, Q, L, 2))], -1)
+        ref = np.concatenate([ref, wh[:, :, None, :] * ratios[:, None, :, :]], -1)
     elif ref_dims != 2:
         raise ValueError(ref_dims)
     off = offset_directions(M, L, P)[None, None] + rng.normal(0.0, offset_sigma, size=(bs, Q, M, L, P, 2))
@@ -299,7 +339,9 @@ def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, q
     return FusedWorkload(name=name, dtype=dtype, spatial_shapes=shapes, level_start_index=level_starts(shapes),
                          value=_cast(value, dtype), reference_points=_cast(ref, dtype),
                          sampling_offsets=_cast(off, dtype), attention_logits=_cast(logits, dtype),
-                         grad_output=_cast(g, dtype), meta=dict(meta or {}, seed=seed))
+                         grad_output=_cast(g, dtype),
+                         key_padding_mask=None if mask is None else torch.from_numpy(mask),
+                         meta=dict(meta or {}, seed=seed))
 
 
 def detr_encoder_fused(bs: int = 2, dtype: str = "f32", seed: int = 1012) -> FusedWorkload:

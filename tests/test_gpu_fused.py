@@ -3,7 +3,9 @@ against the oracle's fused functions, element by element, on seeded inputs:
 reference points (2-d and 4-d), raw offsets and logits in every dtype, on
 problems of several workgroups with a ragged tail, the L = P = 4 kernels and
 the generic ones, samples pushed off the map, the float-atomic fallback, an
-empty problem, the DETR encoder and decoder shapes at full size and the
+empty problem, key padding masks (padded images with valid-ratio-scaled
+reference points, random masks, masks on segments split over several
+accumulation units), the DETR encoder and decoder shapes at full size and the
 autograd wrapper."""
 import numpy as np
 import pytest
@@ -21,7 +23,9 @@ def setup_module(module):
 
 
 def run(wl):
-    print(f"[gpu] fused {wl.name} {wl.dtype} ref{wl.ref_dims} {tuple(wl.sampling_offsets.shape)}", flush=True)
+    masked = "" if wl.key_padding_mask is None else f" masked {int(wl.key_padding_mask.sum())}"
+    print(f"[gpu] fused {wl.name} {wl.dtype} ref{wl.ref_dims} {tuple(wl.sampling_offsets.shape)}{masked}",
+          flush=True)
     t = fused_to_device(wl)
     check_forward_fused(wl, gpu_forward_fused(wl, t))
     check_backward_fused(wl, gpu_backward_fused(wl, t))
@@ -86,6 +90,52 @@ def test_detr_shapes_full_size(make):
     run(make())
 
 
+PADDED = [(1.0, 1.0), (0.7, 0.55)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ref_dims", [2, 4])
+def test_padded_images_encoder(dtype, ref_dims):
+    """Two images padded to one size (the second to 70% x 55%): per-level
+    masks by nearest downsampling, encoder reference points over the valid
+    extent scaled by each level's valid ratio; L = P = 4."""
+    shapes = [(16, 20), (8, 10), (4, 5), (2, 3)]
+    K = sum(h * w for h, w in shapes)
+    run(W.make_fused("padded_enc", 2, shapes, 8, 32, 4, K, dtype, seed=41, ref_dims=ref_dims,
+                     ref_dist="encoder", valid=PADDED))
+
+
+@pytest.mark.parametrize("ref_dims", [2, 4])
+def test_padded_images_decoder(ref_dims):
+    run(W.make_fused("padded_dec", 2, [(15, 21), (8, 11), (4, 6)], 4, 32, 3, 130, "f32", seed=42,
+                     ref_dims=ref_dims, valid=PADDED))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_random_mask(dtype):
+    """A mask with no structure (30% of keys), generic kernels."""
+    wl = W.make_fused("random_mask", 2, [(11, 13), (6, 7), (3, 4)], 4, 32, 3, 150, dtype, seed=43)
+    wl.key_padding_mask = torch.from_numpy(np.random.default_rng(44).random(wl.value.shape[:2]) < 0.3)
+    run(wl)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mask_on_split_segments(dtype):
+    """2000 queries on a 4x4 level: its segments are split over several
+    accumulation units (rows added with atomics), with a random mask."""
+    wl = W.make_fused("split_mask", 2, [(4, 4), (30, 40)], 2, 16, 4, 2000, dtype, seed=45)
+    wl.key_padding_mask = torch.from_numpy(np.random.default_rng(46).random(wl.value.shape[:2]) < 0.3)
+    run(wl)
+
+
+def test_mask_on_fallback_path():
+    wl = W.make_fused("fallback_mask", 1, [(1, 600000)], 1, 8, 1, 64, "f32", seed=47)
+    m = np.zeros(wl.value.shape[:2], dtype=bool)
+    m[:, ::3] = True
+    wl.key_padding_mask = torch.from_numpy(m)
+    run(wl)
+
+
 def test_autograd_function():
     from scale_deformable_attention_03_amd import ms_deform_attn_fused
     wl = W.make_fused("autograd", 2, [(11, 13), (6, 7)], 4, 32, 3, 40, "f32", seed=37, ref_dims=4)
@@ -93,7 +143,9 @@ def test_autograd_function():
     v = t["value"].clone().requires_grad_()
     off = t["off"].clone().requires_grad_()
     lg = t["logits"].clone().requires_grad_()
-    out = ms_deform_attn_fused(v, wl.spatial_shapes, wl.level_start_index, t["ref"], off, lg)
+    mask = torch.from_numpy(np.random.default_rng(38).random(wl.value.shape[:2]) < 0.2).cuda()
+    wl.key_padding_mask = mask.cpu()
+    out = ms_deform_attn_fused(v, wl.spatial_shapes, wl.level_start_index, t["ref"], off, lg, mask)
     out.backward(t["g"])
     torch.cuda.synchronize()
     check_forward_fused(wl, out.detach())

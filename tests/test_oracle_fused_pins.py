@@ -17,7 +17,9 @@ against an independent fact:
   * 4-d boxes of size 2P / (W, H) make the 4-d form equal the 2-d form;
   * torch float64 autograd through the location formula, torch.softmax and
     grid_sample, on dyadic inputs that make every float32 location exact;
-  * central differences in the logits.
+  * central differences in the logits;
+  * key padding: float64 autograd through masked_fill; a mask over every key
+    zeroes everything; a mask over keys no corner reaches changes nothing.
 """
 import numpy as np
 import pytest
@@ -205,20 +207,24 @@ def dyadic_fused_problem(rng, shapes, M, D, P, Q, ref_dims):
     return shapes, value, ref, off, lg, g
 
 
+@pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("ref_dims", [2, 4])
-def test_autograd_cross_check(ref_dims):
-    """torch float64 autograd through the location step, torch.softmax and
-    grid_sample (bilinear, zeros, align_corners=False) gives the oracle's
-    output and all three gradients."""
+def test_autograd_cross_check(ref_dims, masked):
+    """torch float64 autograd through masked_fill of the padded keys, the
+    location step, torch.softmax and grid_sample (bilinear, zeros,
+    align_corners=False) gives the oracle's output and all three
+    gradients."""
     rng = np.random.default_rng(7 + ref_dims)
     shapes, value, ref, off, lg, g = dyadic_fused_problem(rng, [(8, 16), (4, 8), (2, 4)], 3, 8, 4, 11,
                                                           ref_dims)
     starts = starts_of(shapes)
-    out = oracle.forward_fused(value, shapes, starts, ref, off, lg)
-    gv, goff, glog = oracle.backward_fused(value, shapes, starts, ref, off, lg, g)
+    mask = rng.random(value.shape[:2]) < 0.3 if masked else None
+    out = oracle.forward_fused(value, shapes, starts, ref, off, lg, mask)
+    gv, goff, glog = oracle.backward_fused(value, shapes, starts, ref, off, lg, g, mask)
 
     bs, Q, M, L, P, _ = off.shape
     v = torch.tensor(value, dtype=torch.float64, requires_grad=True)
+    vm = v.masked_fill(torch.tensor(mask)[..., None, None], 0.0) if masked else v
     o = torch.tensor(off, dtype=torch.float64, requires_grad=True)
     a = torch.tensor(lg, dtype=torch.float64, requires_grad=True)
     r = torch.tensor(ref, dtype=torch.float64)[:, :, None, :, None, :]
@@ -230,7 +236,7 @@ def test_autograd_cross_check(ref_dims):
     w = torch.softmax(a.reshape(bs, Q, M, L * P), -1).reshape(bs, Q, M, L, P)
     Wd = torch.tensor(shapes[:, 1], dtype=torch.float64)[None, None, None, :, None]
     Hd = torch.tensor(shapes[:, 0], dtype=torch.float64)[None, None, None, :, None]
-    ref_out = grid_sample_core(v, shapes, loc[..., 0] * Wd - 0.5, loc[..., 1] * Hd - 0.5, w)
+    ref_out = grid_sample_core(vm, shapes, loc[..., 0] * Wd - 0.5, loc[..., 1] * Hd - 0.5, w)
     ref_out.backward(torch.tensor(g, dtype=torch.float64))
     np.testing.assert_allclose(out, ref_out.detach().numpy(), rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(gv, v.grad.numpy(), rtol=1e-10, atol=1e-10)
@@ -256,3 +262,41 @@ def test_logit_central_differences():
         fd = ((g64 * oracle.forward_fused(value, shapes, starts, ref, off, up)).sum() -
               (g64 * oracle.forward_fused(value, shapes, starts, ref, off, dn)).sum()) / (2 * h)
         assert fd == pytest.approx(glog[idx], rel=1e-5, abs=1e-8)
+
+
+@pytest.mark.parametrize("ref_dims", [2, 4])
+def test_mask_everything_zeroes_everything(ref_dims):
+    """Every key padded: every sample reads zeros, so the output and all
+    gradients (value, offsets, logits) are zero."""
+    rng = np.random.default_rng(12)
+    shapes, value, ref, off, lg, g = fused_problem(rng, 2, [(6, 9), (3, 4)], 3, 8, 3, 7, ref_dims)
+    starts = starts_of(shapes)
+    mask = np.ones(value.shape[:2], dtype=bool)
+    assert np.all(oracle.forward_fused(value, shapes, starts, ref, off, lg, mask) == 0)
+    for x in oracle.backward_fused(value, shapes, starts, ref, off, lg, g, mask):
+        assert np.all(x == 0)
+
+
+def test_mask_of_unreached_keys_changes_nothing():
+    """Padding keys that no bilinear corner touches leaves output and
+    gradients exactly as without a mask (those rows' value gradient is zero
+    either way)."""
+    rng = np.random.default_rng(13)
+    shapes = np.array([(12, 16), (6, 8)], dtype=np.int64)
+    starts = starts_of(shapes)
+    M, P, Q, D = 2, 2, 5, 8
+    K = int((shapes[:, 0] * shapes[:, 1]).sum())
+    value = rng.standard_normal((1, K, M, D)).astype(np.float32)
+    ref = np.full((1, Q, 2, 2), 0.25, dtype=np.float32)         # top-left quarter of every level
+    off = rng.uniform(-0.4, 0.4, size=(1, Q, M, 2, P, 2)).astype(np.float32)
+    lg = rng.standard_normal((1, Q, M, 2, P)).astype(np.float32)
+    g = rng.standard_normal((1, Q, M * D)).astype(np.float32)
+    mask = np.zeros((1, K), dtype=bool)
+    for (H, W), s0 in zip(shapes, starts):                       # pad the right half of every level
+        yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+        mask[0, s0 + (yy * W + xx)[xx >= W // 2]] = True
+    np.testing.assert_array_equal(oracle.forward_fused(value, shapes, starts, ref, off, lg, mask),
+                                  oracle.forward_fused(value, shapes, starts, ref, off, lg))
+    for a, b in zip(oracle.backward_fused(value, shapes, starts, ref, off, lg, g, mask),
+                    oracle.backward_fused(value, shapes, starts, ref, off, lg, g)):
+        np.testing.assert_array_equal(a, b)
