@@ -163,7 +163,8 @@ size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
  *   (may be NULL when that is 0), 16-byte aligned, owned by the caller; its
  *   contents are scratch on entry and on exit.  Calls that overlap in time
  *   must not share a workspace.
- *   Enqueues on `stream`: a record count, a scan, the gradient kernel (a
+ *   Enqueues on `stream`: a record count and a scan (one kernel when each
+ *   (batch, head) has at most 8192 samples), the gradient kernel (a
  *   gather like the forward, which also writes the records), the
  *   accumulation kernel (one workgroup per key segment writes grad_value
  *   rows once) and, for fp16/bf16, a conversion kernel.  Problems whose
@@ -214,12 +215,14 @@ msda_status_t msda_backward_accumulate(const msda_problem_t *problem,
  *   stage_events: host array of MSDA_BACKWARD_STAGES + 1 events created by
  *   the caller (hipEventCreate); event k is recorded just before stage k,
  *   the last one after the final stage:
- *     0 zero the segment counts      1 count records per segment
- *     2 scan counts into ranges      3 gradient kernel (gather, records)
+ *     0 zero fill (float-atomic fallback only)
+ *     1 count records per segment    2 scan counts into ranges
+ *     3 gradient kernel (gather, records)
  *     4 accumulate grad_value        5 fp16/bf16 conversion
- *   A stage with no kernel for the problem (the conversion for fp32; the
- *   count, scan and accumulation on the float-atomic fallback, whose zero
- *   fill then runs as stage 0) leaves its two events back to back.
+ *   A stage with no kernel for the problem leaves its two events back to
+ *   back: stage 0 on the binned path; the scan when one kernel counts and
+ *   scans (planes of at most 8192 samples); the conversion for fp32; the
+ *   count, scan and accumulation on the float-atomic fallback.
  *   Otherwise identical to msda_backward; stage_events must not be NULL.
  */
 #define MSDA_BACKWARD_STAGES 6

@@ -19,7 +19,7 @@ STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_S
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
            "msda_backward_accumulate", "msda_backward_profile", "msda_forward_fused",
            "msda_backward_fused", "msda_status_string", "msda_abi_version")
-BACKWARD_STAGES = ("zero_counts", "count", "scan", "gradient", "accumulate", "narrow")
+BACKWARD_STAGES = ("zero_fill", "count", "scan", "gradient", "accumulate", "narrow")
 
 
 class MsdaError(RuntimeError):

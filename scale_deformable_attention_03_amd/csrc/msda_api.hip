@@ -148,6 +148,21 @@ int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
     return pb.nseg + (plane_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
 }
 
+// Counting: samples per counting workgroup (one histogram row each) and the
+// number of rows per plane; planes of at most kCountScanSamples samples are
+// counted and scanned by one workgroup instead (no rows).
+int64_t count_chunk(const msda::Problem& pb) {
+    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
+    return std::max<int64_t>(msda::kCountChunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks);
+}
+int64_t count_chunks(const msda::Problem& pb) {
+    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
+    return (nsamp + count_chunk(pb) - 1) / count_chunk(pb);
+}
+bool fused_count_scan(const msda::Problem& pb) {
+    return int64_t(pb.Q) * pb.L * pb.P <= msda::kCountScanSamples;
+}
+
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
     for (int l = 0; l < p->num_levels; ++l)
         if (p->spatial_shapes[2 * l] > msda::kMaxBinnedExtent || p->spatial_shapes[2 * l + 1] > msda::kMaxBinnedExtent)
@@ -174,8 +189,9 @@ Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
     if (w.binned) {
         const int64_t nbins = int64_t(pb.nplanes) * pb.nseg;
         w.max_units = int64_t(pb.nplanes) * plane_units(p, pb);
+        // one histogram row per counting workgroup
         w.counts = off;
-        off += round_up(nbins * 4);
+        if (!fused_count_scan(pb)) off += round_up(nbins * count_chunks(pb) * 4);
         w.cursor = off;
         off += round_up(nbins * 4);
         // [p] units of plane p, [nplanes + p] its multi-unit segments (both
@@ -267,17 +283,22 @@ msda_status_t by_dtype_split(msda_dtype_t dt, const LaneSplit& s, A&&... a) {
 
 bool is_l4p4(const msda::Problem& pb) { return pb.L == 4 && pb.P == 4; }
 
+int64_t plane_blocks(const msda::Problem& pb, int gpb) {
+    return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
+}
+
 // Queries per workgroup: the full 256 lanes unless the per-sample LDS
-// records would exceed `max_samples` samples per workgroup.
-int tile_queries(const msda::Problem& pb, int lpr, int max_samples) {
+// records would exceed `max_samples` samples per workgroup.  With `shrink`,
+// small problems (fewer than two workgroups per compute unit) take smaller
+// workgroups, down to one wave, so that more compute units share the
+// latency-bound work.
+int tile_queries(const msda::Problem& pb, int lpr, int max_samples, bool shrink) {
+    constexpr int64_t kFill = 2 * 256;
     int gpb = kBlock / lpr;
     const int cap = max_samples / (pb.L * pb.P);
     if (gpb > cap) gpb = cap < 1 ? 1 : cap;
+    while (shrink && plane_blocks(pb, gpb) < kFill && gpb * lpr > 64 && gpb % 2 == 0) gpb /= 2;
     return gpb;
-}
-
-int64_t plane_blocks(const msda::Problem& pb, int gpb) {
-    return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
 }
 
 // Reference-point form of a call: 0 (locations and weights given), 2 or 4
@@ -301,7 +322,7 @@ template <int DT, int VECB, int LPR>
 struct Fwd {
     static msda_status_t run(const msda::Problem& pb, int ref_dims, const void* v, const void* ref,
                              const uint8_t* kmask, const void* loc, const void* w, void* out, hipStream_t st) {
-        const int gpb = tile_queries(pb, LPR, 1024);
+        const int gpb = tile_queries(pb, LPR, 1024, true);
         const int LP = pb.L * pb.P;
         const size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
         const void* k = ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
@@ -318,7 +339,9 @@ struct Grad {
                              uint3* recs,
                              int32_t* cursor, int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
                              hipStream_t st) {
-        const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples);
+        // (the gradient kernel keeps full workgroups: measured, its per-workgroup
+        // cursor reservation makes smaller ones slower on small problems)
+        const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples, false);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
         size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
@@ -352,21 +375,54 @@ struct Accum {
     }
 };
 
+// Records events[k] (when events is not NULL) on the stream just before
+// backward stage k; stage kStageEnd marks the end of the last stage.
+enum Stage { kStageZero = 0, kStageCount, kStageScan, kStageGrad, kStageAccum, kStageNarrow, kStageEnd };
+
+msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
+    if (events == nullptr) return MSDA_SUCCESS;
+    return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
+}
+
 template <int DT, int REF>
 const void* count_kernel(const msda::Problem& pb) {
     return is_l4p4(pb) ? kfn(&msda::msda_bin_count_kernel<DT, 4, 4, REF>)
                        : kfn(&msda::msda_bin_count_kernel<DT, 0, 0, REF>);
 }
 
+template <int DT, int REF>
+const void* count_scan_kernel(const msda::Problem& pb) {
+    return is_l4p4(pb) ? kfn(&msda::msda_bin_count_scan_kernel<DT, 4, 4, REF>)
+                       : kfn(&msda::msda_bin_count_scan_kernel<DT, 0, 0, REF>);
+}
+
+// Count records per segment and scan the counts into ranges, cursors and
+// units: one fused launch for small planes, else count (histogram rows) and
+// scan.  Events: the count stage before, the scan stage between.
 template <int DT>
-msda_status_t count_launch(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
-                           int32_t* counts, hipStream_t st) {
-    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
-    const int64_t blocks = int64_t(pb.nplanes) * ((nsamp + msda::kCountChunk - 1) / msda::kCountChunk);
+msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
+                                int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
+                                int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
+    MSDA_TRY(mark(ev, kStageCount, st));
+    if (fused_count_scan(pb)) {
+        const void* k = ref_dims == 0   ? count_scan_kernel<DT, 0>(pb)
+                        : ref_dims == 2 ? count_scan_kernel<DT, 2>(pb)
+                                        : count_scan_kernel<DT, 4>(pb);
+        MSDA_TRY(launch(k, pb.nplanes, msda::kCountScanBlock, 0, st, loc, ref, cursor, nunits, multi, units,
+                        accumulate, pb, plane_recs, plane_us));
+        return mark(ev, kStageScan, st);
+    }
+    const int64_t chunks = count_chunks(pb);
     const void* k = ref_dims == 0   ? count_kernel<DT, 0>(pb)
                     : ref_dims == 2 ? count_kernel<DT, 2>(pb)
                                     : count_kernel<DT, 4>(pb);
-    return launch(k, blocks, kBlock, sizeof(int32_t) * pb.nseg, st, loc, ref, counts, pb);
+    MSDA_TRY(launch(k, int64_t(pb.nplanes) * chunks, msda::kCountBlock, sizeof(int32_t) * pb.nseg, st, loc, ref,
+                    counts, pb,
+                    static_cast<int>(count_chunk(pb))));
+    MSDA_TRY(mark(ev, kStageScan, st));
+    return launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
+                  static_cast<const int32_t*>(counts), static_cast<int>(chunks), cursor, nunits, multi, units,
+                  accumulate, pb, plane_recs, plane_us);
 }
 
 // Reference points of the fused prologue: ref_dims 0 (none; ref unused), 2
@@ -409,14 +465,6 @@ msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* val
     return MSDA_SUCCESS;
 }
 
-// Records events[k] (when events is not NULL) on the stream just before
-// backward stage k; stage kStageEnd marks the end of the last stage.
-enum Stage { kStageZero = 0, kStageCount, kStageScan, kStageGrad, kStageAccum, kStageNarrow, kStageEnd };
-
-msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
-    if (events == nullptr) return MSDA_SUCCESS;
-    return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
-}
 
 // The backward.  accumulate = 1: grad_value is added into the float32
 // buffer gacc (gfinal unused).  accumulate = 0: grad_value is overwritten
@@ -471,18 +519,22 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
     int4* units = reinterpret_cast<int4*>(ws + lay.units);
     uint3* recs = reinterpret_cast<uint3*>(ws + lay.recs);
 
-    MSDA_TRY(mark(ev, kStageZero, st));
-    MSDA_TRY(zero_bytes(counts, round_up(size_t(pb.nplanes) * pb.nseg * 4), st));
-    MSDA_TRY(mark(ev, kStageCount, st));
+    MSDA_TRY(mark(ev, kStageZero, st));             // no zero fill on this path
+    const int prec = static_cast<int>(plane_records(problem)), pun = static_cast<int>(plane_units(problem, pb));
     switch (problem->dtype) {
-        case MSDA_F32: MSDA_TRY(count_launch<kF32>(pb, ref_dims, ref, loc, counts, st)); break;
-        case MSDA_F16: MSDA_TRY(count_launch<kF16>(pb, ref_dims, ref, loc, counts, st)); break;
-        default: MSDA_TRY(count_launch<kBF16>(pb, ref_dims, ref, loc, counts, st)); break;
+        case MSDA_F32:
+            MSDA_TRY(count_scan_launch<kF32>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
+                                             prec, pun, ev, st));
+            break;
+        case MSDA_F16:
+            MSDA_TRY(count_scan_launch<kF16>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
+                                             prec, pun, ev, st));
+            break;
+        default:
+            MSDA_TRY(count_scan_launch<kBF16>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
+                                              accumulate, prec, pun, ev, st));
+            break;
     }
-    MSDA_TRY(mark(ev, kStageScan, st));
-    MSDA_TRY(launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
-                    static_cast<const int32_t*>(counts), cursor, nunits, multi, units, accumulate, pb,
-                    static_cast<int>(plane_records(problem)), static_cast<int>(plane_units(problem, pb))));
     MSDA_TRY(mark(ev, kStageGrad, st));
     MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs,
                                   cursor,

@@ -65,7 +65,9 @@ constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 1024;    // samples one gradient workgroup holds
 constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path (16-bit cell fields)
-constexpr int kCountChunk = 4096;      // samples one counting workgroup bins
+constexpr int kCountBlock = 512;       // lanes of a counting workgroup
+constexpr int kCountChunk = 8192;      // samples one counting workgroup bins (at least)
+constexpr int kMaxCountChunks = 64;    // counting workgroups (histogram rows) per plane
 
 // Corners of one row that a record covers.
 enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
@@ -196,33 +198,23 @@ __device__ __forceinline__ void lds_add_f32xN(float* dst, const float* v) {
 // ---------------------------------------------------------------------------
 // 1. count
 // ---------------------------------------------------------------------------
-// Grid: nplanes * ceil(Q*L*P / kCountChunk) workgroups of kBlock lanes; one
-// lane per sample.  LDS: nseg int32.  REF as for the gradient kernel (loc
-// holds the offsets and ref the reference points when REF != 0).
-template <int DT, int L_CT, int P_CT, int REF>
-__global__ void __launch_bounds__(kBlock)
-msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref, int32_t* __restrict__ counts,
-                      Problem pb) {
-    extern __shared__ int32_t hist[];
+// Samples [s_begin, s_end) of plane (b, m), in the plane's (query, level,
+// point) order, counted into the LDS histogram `hist` (nseg bins), NT lanes.
+// REF as for the gradient kernel (loc holds the offsets and ref the reference
+// points when REF != 0).  s_lv: the staged level table.
+template <int DT, int L_CT, int P_CT, int REF, int NT>
+__device__ __forceinline__ void count_samples(const void* __restrict__ loc, const void* __restrict__ ref,
+                                              int32_t* hist, const int4* s_lv, const Problem& pb, int b, int m,
+                                              int s_begin, int s_end) {
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
     const int LP = L * P;
-    const int nsamp = pb.Q * LP;
-    const int nchunks = (nsamp + kCountChunk - 1) / kCountChunk;
-    const int pl = blockIdx.x / nchunks, chunk = blockIdx.x - pl * nchunks;
-    const int b = pl / pb.M, m = pl - b * pb.M;
-
-    __shared__ int4 s_lv[kMaxLevels];
-    stage_levels(pb, s_lv);
-    for (int i = threadIdx.x; i < pb.nseg; i += kBlock) hist[i] = 0;
-    __syncthreads();
-    const int s_end = min((chunk + 1) * kCountChunk, nsamp);
     constexpr int kU = 4;                            // samples whose loads fly together
-    for (int s0 = chunk * kCountChunk + threadIdx.x; s0 < s_end; s0 += kU * kBlock) {
+    for (int s0 = s_begin + static_cast<int>(threadIdx.x); s0 < s_end; s0 += kU * NT) {
         float lx[kU], ly[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int s = s0 + u * kBlock;
+            const int s = s0 + u * NT;
             lx[u] = ly[u] = -2.0f;                       // off the map
             if (s < s_end) {
                 const int q = s / LP, lp = s - q * LP, l = lp / P;
@@ -237,7 +229,7 @@ msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int s = s0 + u * kBlock;
+            const int s = s0 + u * NT;
             if (s >= s_end) break;
             const int lp = s % LP, l = lp / P;
             const int4 lv = s_lv[l];
@@ -249,9 +241,32 @@ msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref
                             [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
         }
     }
+}
+
+// Grid: nplanes * nchunks workgroups of kCountBlock lanes, chunk samples
+// each (the last chunk of a plane may be short).  Each workgroup writes its
+// own histogram row counts[(plane * nchunks + chunk) * nseg ...] in full, so
+// no buffer needs zeroing first.  LDS: nseg int32.
+template <int DT, int L_CT, int P_CT, int REF>
+__global__ void __launch_bounds__(kCountBlock)
+msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref, int32_t* __restrict__ counts,
+                      Problem pb, int chunk) {
+    extern __shared__ int32_t hist[];
+    const int LP = (L_CT ? L_CT : pb.L) * (P_CT ? P_CT : pb.P);
+    const int nsamp = pb.Q * LP;
+    const int nchunks = (nsamp + chunk - 1) / chunk;
+    const int pl = blockIdx.x / nchunks, c = blockIdx.x - pl * nchunks;
+    const int b = pl / pb.M, m = pl - b * pb.M;
+
+    __shared__ int4 s_lv[kMaxLevels];
+    stage_levels(pb, s_lv);
+    for (int i = threadIdx.x; i < pb.nseg; i += kCountBlock) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < pb.nseg; i += kBlock)
-        if (hist[i] != 0) atomicAdd(&counts[static_cast<int64_t>(pl) * pb.nseg + i], hist[i]);
+    count_samples<DT, L_CT, P_CT, REF, kCountBlock>(loc, ref, hist, s_lv, pb, b, m, c * chunk,
+                                                    min((c + 1) * chunk, nsamp));
+    __syncthreads();
+    int32_t* row = counts + static_cast<int64_t>(blockIdx.x) * pb.nseg;
+    for (int i = threadIdx.x; i < pb.nseg; i += kCountBlock) row[i] = hist[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -312,36 +327,30 @@ msda_narrow_segments_kernel(const float* __restrict__ gacc, void* __restrict__ o
         narrow_segment<DT>(pb, gacc, out, multi[static_cast<int64_t>(pl) * pb.nseg + e], threadIdx.x, kBlock);
 }
 
-// One workgroup per plane (b, m).  Plane p owns a fixed record region
-// [p * plane_records, ...) and a fixed unit region [p * plane_units, ...), so
-// planes need no common prefix.  counts -> cursor (the plane's exclusive
-// prefix plus its region base), the plane's units {segment, first record,
-// end record, flush-with-atomics} and their number (nunits[p]), and the
-// plane's segments split over several units (nunits[nplanes + p] entries of
-// multi[p * nseg ...]), whose rows the gradient kernel zeroes.  With
-// `accumulate` every unit adds into the caller's buffer, which is then left
-// as it is (and no segment is listed).  Every lane scans kScanPer
-// consecutive segments; lanes combine through a wave scan and the wave
-// totals.
-constexpr int kScanPer = kMaxSegments / kBlock;
-
-__global__ void __launch_bounds__(kBlock)
-msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
-                     int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
-                     int accumulate, Problem pb, int plane_records, int plane_units) {
-    __shared__ int32_t s_cnt[kMaxSegments];
-    __shared__ int32_t s_wrec[kBlock / 64], s_wunit[kBlock / 64];
-    __shared__ int32_t s_nmulti;
+// Plane p owns a fixed record region [p * plane_records, ...) and a fixed
+// unit region [p * plane_units, ...), so planes need no common prefix.  From
+// the plane's segment counts (LDS s_cnt), NT lanes write: the cursors (the
+// exclusive prefix plus the region base), the plane's units {segment, first
+// record, end record, flush-with-atomics} and their number (nunits[p]), and
+// the plane's segments split over several units (nunits[nplanes + p]
+// entries of multi[p * nseg ...]), whose rows the gradient kernel zeroes.
+// With `accumulate` every unit adds into the caller's buffer, which is then
+// left as it is (and no segment is listed).  Every lane scans kMaxSegments /
+// NT consecutive segments; lanes combine through a wave scan and the wave
+// totals.  Ends with a barrier; s_nmulti must be zero on entry.
+template <int NT>
+__device__ void scan_plane(const int32_t* s_cnt, int32_t* s_wrec, int32_t* s_wunit, int32_t* s_nmulti,
+                           int32_t* __restrict__ cursor, int32_t* __restrict__ nunits,
+                           int32_t* __restrict__ multi, int4* __restrict__ units, int accumulate,
+                           const Problem& pb, int pl, int plane_records, int plane_units) {
+    constexpr int kPer = kMaxSegments / NT;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int pl = blockIdx.x, n = pb.nseg;
+    const int n = pb.nseg;
     const int64_t cbase = static_cast<int64_t>(pl) * n;
-    if (t == 0) s_nmulti = 0;
-    for (int i = t; i < n; i += kBlock) s_cnt[i] = counts[cbase + i];
-    __syncthreads();
     int rsum = 0, usum = 0;
 #pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-        const int i = t * kScanPer + j;
+    for (int j = 0; j < kPer; ++j) {
+        const int i = t * kPer + j;
         if (i < n) {
             rsum += s_cnt[i];
             usum += units_of(s_cnt[i]);
@@ -369,8 +378,8 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
     rbase += pl * plane_records;
     const int ufirst = pl * plane_units;
 #pragma unroll 1
-    for (int j = 0; j < kScanPer; ++j) {
-        const int i = t * kScanPer + j;
+    for (int j = 0; j < kPer; ++j) {
+        const int i = t * kPer + j;
         if (i >= n) break;
         const int c = s_cnt[i], u = units_of(c);
         const int gi = static_cast<int>(cbase) + i;
@@ -379,15 +388,67 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ c
         for (int k = 0; k < u; ++k)
             units[ufirst + ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
                                                   rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
-        if (u > 1 && !accumulate) multi[cbase + atomicAdd(&s_nmulti, 1)] = gi;
+        if (u > 1 && !accumulate) multi[cbase + atomicAdd(s_nmulti, 1)] = gi;
         rbase += c;
         ubase += u;
     }
     __syncthreads();
-    if (t == kBlock - 1) {
+    if (t == NT - 1) {
         nunits[pl] = ubase;                          // the last lane's running count is the total
-        nunits[pb.nplanes + pl] = s_nmulti;
+        nunits[pb.nplanes + pl] = *s_nmulti;
     }
+}
+
+// One workgroup per plane: sums the plane's nchunks histogram rows, then
+// scan_plane.
+__global__ void __launch_bounds__(kBlock)
+msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* __restrict__ cursor,
+                     int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
+                     int accumulate, Problem pb, int plane_records, int plane_units) {
+    __shared__ int32_t s_cnt[kMaxSegments];
+    __shared__ int32_t s_wrec[kBlock / 64], s_wunit[kBlock / 64];
+    __shared__ int32_t s_nmulti;
+    const int pl = blockIdx.x, n = pb.nseg;
+    if (threadIdx.x == 0) s_nmulti = 0;
+    const int32_t* rows = counts + static_cast<int64_t>(pl) * nchunks * n;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        int sum = 0;
+#pragma unroll 8
+        for (int c = 0; c < nchunks; ++c) sum += rows[static_cast<int64_t>(c) * n + i];
+        s_cnt[i] = sum;
+    }
+    __syncthreads();
+    scan_plane<kBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb, pl,
+                       plane_records, plane_units);
+}
+
+// Count and scan in one launch, one workgroup of kCountScanBlock lanes per
+// plane, for planes of at most kCountScanSamples samples (a latency-bound
+// size: one launch and no histogram rows in memory).
+constexpr int kCountScanBlock = 1024;
+constexpr int kCountScanSamples = 8192;
+
+template <int DT, int L_CT, int P_CT, int REF>
+__global__ void __launch_bounds__(kCountScanBlock)
+msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict__ ref,
+                           int32_t* __restrict__ cursor, int32_t* __restrict__ nunits, int32_t* __restrict__ multi,
+                           int4* __restrict__ units, int accumulate, Problem pb, int plane_records,
+                           int plane_units) {
+    __shared__ int32_t s_cnt[kMaxSegments];
+    __shared__ int32_t s_wrec[kCountScanBlock / 64], s_wunit[kCountScanBlock / 64];
+    __shared__ int32_t s_nmulti;
+    __shared__ int4 s_lv[kMaxLevels];
+    const int pl = blockIdx.x;
+    const int b = pl / pb.M, m = pl - b * pb.M;
+    const int LP = (L_CT ? L_CT : pb.L) * (P_CT ? P_CT : pb.P);
+    stage_levels(pb, s_lv);
+    if (threadIdx.x == 0) s_nmulti = 0;
+    for (int i = threadIdx.x; i < pb.nseg; i += kCountScanBlock) s_cnt[i] = 0;
+    __syncthreads();
+    count_samples<DT, L_CT, P_CT, REF, kCountScanBlock>(loc, ref, s_cnt, s_lv, pb, b, m, 0, pb.Q * LP);
+    __syncthreads();
+    scan_plane<kCountScanBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb,
+                                pl, plane_records, plane_units);
 }
 
 // ---------------------------------------------------------------------------
