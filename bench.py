@@ -41,7 +41,9 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak
 MALL_BYTES = 256 << 20       # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_03_amd", "csrc", f)
-                  for f in ("msda_api.hip", "msda_forward.hpp", "msda_backward.hpp", "msda_device.hpp")]
+                  for f in ("msda_api.hip", "msda_forward.hpp", "msda_backward.hpp", "msda_device.hpp",
+                            "msda_launch.hpp", "msda_launch_impl.hpp", "msda_kernels_f32.hip",
+                            "msda_kernels_f16.hip", "msda_kernels_bf16.hip")]
 
 
 def log(*a):

@@ -13,15 +13,18 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsda.so")
-SOURCES = [os.path.join(CSRC, "msda_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp")] + \
-          [os.path.join(INCLUDE, "msda.h")]
+# the C ABI and one translation unit of kernel instantiations per dtype,
+# compiled in parallel and linked into one library
+SOURCES = [os.path.join(CSRC, f) for f in ("msda_api.hip", "msda_kernels_f32.hip", "msda_kernels_f16.hip",
+                                            "msda_kernels_bf16.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp",
+                                           "msda_launch.hpp", "msda_launch_impl.hpp")] + [os.path.join(INCLUDE, "msda.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     "-Wall", "-Wno-unused-result", "-Wno-pass-failed",
     # float32 atomics compile to the hardware global_atomic_add_f32
     "-munsafe-fp-atomics",
@@ -31,12 +34,26 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into ``libmsda.so`` (always recompiles)."""
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", LIB + ".tmp", *SOURCES]
+    """Compile every source into ``libmsda.so`` (always recompiles): one
+    hipcc process per source, in parallel, then one link."""
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, os.path.basename(src)[:-4] + ".o")
+        cmd = [HIPCC, *FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), cmd))
+        objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(LIB + ".tmp", LIB)
+    for obj in objs:
+        os.remove(obj)
     return LIB
 
 

@@ -12,8 +12,7 @@
 #include <algorithm>
 
 #include "msda.h"
-#include "msda_backward.hpp"
-#include "msda_forward.hpp"
+#include "msda_launch.hpp"
 
 namespace {
 
@@ -21,18 +20,26 @@ using msda::kBF16;
 using msda::kBlock;
 using msda::kF16;
 using msda::kF32;
+using msda_host::count_chunks;
+using msda_host::fused_count_scan;
+using msda_host::kfn;
+using msda_host::LaneSplit;
+using msda_host::launch;
+using msda_host::Launch;
+using msda_host::mark;
+using msda_host::kStageZero;
+using msda_host::kStageCount;
+using msda_host::kStageScan;
+using msda_host::kStageGrad;
+using msda_host::kStageAccum;
+using msda_host::kStageNarrow;
+using msda_host::kStageEnd;
 
 constexpr int64_t kIndexLimit = int64_t(1) << 31;
 
 int elem_bytes(msda_dtype_t dt) { return dt == MSDA_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Lane split of one group: VECB bytes per lane, LPR lanes (a power of two,
-// at least 4) of which `active` own channels.
-struct LaneSplit {
-    int vecb, lpr, active;
-};
 
 LaneSplit lane_split(int embed_dims, msda_dtype_t dt) {
     const int row = embed_dims * elem_bytes(dt);   // a multiple of 16 bytes
@@ -148,21 +155,6 @@ int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
     return pb.nseg + (plane_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
 }
 
-// Counting: samples per counting workgroup (one histogram row each) and the
-// number of rows per plane; planes of at most kCountScanSamples samples are
-// counted and scanned by one workgroup instead (no rows).
-int64_t count_chunk(const msda::Problem& pb) {
-    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
-    return std::max<int64_t>(msda::kCountChunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks);
-}
-int64_t count_chunks(const msda::Problem& pb) {
-    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
-    return (nsamp + count_chunk(pb) - 1) / count_chunk(pb);
-}
-bool fused_count_scan(const msda::Problem& pb) {
-    return int64_t(pb.Q) * pb.L * pb.P <= msda::kCountScanSamples;
-}
-
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
     for (int l = 0; l < p->num_levels; ++l)
         if (p->spatial_shapes[2 * l] > msda::kMaxBinnedExtent || p->spatial_shapes[2 * l + 1] > msda::kMaxBinnedExtent)
@@ -220,29 +212,6 @@ msda_status_t check_ptr(const void* ptr, int64_t elems) {
     return MSDA_SUCCESS;
 }
 
-#define MSDA_TRY(expr)                                  \
-    do {                                                \
-        msda_status_t s_ = (expr);                      \
-        if (s_ != MSDA_SUCCESS) return s_;              \
-    } while (0)
-
-// Launch through hipLaunchKernel, whose return code belongs to this launch
-// alone (no sticky error of an earlier, unrelated call is read or cleared).
-template <typename... Args>
-msda_status_t launch(const void* kernel, int64_t blocks, int threads, size_t lds_bytes, hipStream_t stream,
-                     Args... args) {
-    if (blocks <= 0) return MSDA_SUCCESS;
-    if (blocks > 0x7fffffff) return MSDA_ERROR_NOT_SUPPORTED;
-    void* argv[] = {static_cast<void*>(&args)...};
-    return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), argv, lds_bytes,
-                           stream) == hipSuccess
-               ? MSDA_SUCCESS
-               : MSDA_ERROR_HIP;
-}
-
-template <typename K>
-const void* kfn(K* k) { return reinterpret_cast<const void*>(k); }
-
 int64_t fill_blocks(int64_t n) {
     const int64_t want = (n + kBlock - 1) / kBlock;
     return want < 8192 ? (want > 0 ? want : 1) : 8192;
@@ -251,178 +220,6 @@ int64_t fill_blocks(int64_t n) {
 msda_status_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
     const int64_t n16 = static_cast<int64_t>(bytes / 16);
     return launch(kfn(&msda::msda_zero_kernel), fill_blocks(n16), kBlock, 0, st, static_cast<uint4*>(p), n16);
-}
-
-// ---- kernel selection ----------------------------------------------------------
-
-// Calls F<DT, VECB, LPR>::run(args...) for the problem's lane split.
-template <int DT, template <int, int, int> class F, typename... A>
-msda_status_t by_split(const LaneSplit& s, A&&... a) {
-    if (s.vecb == 4) return F<DT, 4, 4>::run(a...);
-    if (s.vecb == 8) {
-        if (s.lpr == 4) return F<DT, 8, 4>::run(a...);
-        return F<DT, 8, 8>::run(a...);
-    }
-    switch (s.lpr) {
-        case 4: return F<DT, 16, 4>::run(a...);
-        case 8: return F<DT, 16, 8>::run(a...);
-        case 16: return F<DT, 16, 16>::run(a...);
-        case 32: return F<DT, 16, 32>::run(a...);
-        default: return F<DT, 16, 64>::run(a...);
-    }
-}
-
-template <template <int, int, int> class F, typename... A>
-msda_status_t by_dtype_split(msda_dtype_t dt, const LaneSplit& s, A&&... a) {
-    switch (dt) {
-        case MSDA_F32: return by_split<kF32, F>(s, a...);
-        case MSDA_F16: return by_split<kF16, F>(s, a...);
-        default: return by_split<kBF16, F>(s, a...);
-    }
-}
-
-bool is_l4p4(const msda::Problem& pb) { return pb.L == 4 && pb.P == 4; }
-
-int64_t plane_blocks(const msda::Problem& pb, int gpb) {
-    return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
-}
-
-// Queries per workgroup: the full 256 lanes unless the per-sample LDS
-// records would exceed `max_samples` samples per workgroup.  With `shrink`,
-// small problems (fewer than two workgroups per compute unit) take smaller
-// workgroups, down to one wave, so that more compute units share the
-// latency-bound work.
-int tile_queries(const msda::Problem& pb, int lpr, int max_samples, bool shrink) {
-    constexpr int64_t kFill = 2 * 256;
-    int gpb = kBlock / lpr;
-    const int cap = max_samples / (pb.L * pb.P);
-    if (gpb > cap) gpb = cap < 1 ? 1 : cap;
-    while (shrink && plane_blocks(pb, gpb) < kFill && gpb * lpr > 64 && gpb % 2 == 0) gpb /= 2;
-    return gpb;
-}
-
-// Reference-point form of a call: 0 (locations and weights given), 2 or 4
-// (reference points, offsets and logits given; the fused prologue).
-template <int DT, int VECB, int LPR, int REF>
-const void* fwd_kernel(const msda::Problem& pb) {
-    return is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4, REF>)
-                       : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0, REF>);
-}
-
-template <int DT, int VECB, int LPR, bool BINNED, int REF>
-const void* grad_kernel(const msda::Problem& pb) {
-    return is_l4p4(pb) ? kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 4, 4, BINNED, REF>)
-                       : kfn(&msda::msda_backward_kernel<DT, VECB, LPR, 0, 0, BINNED, REF>);
-}
-
-// LDS of the fused prologue: logits and their exponentials.
-size_t fused_lds(int ref_dims, int gpb, int LP) { return ref_dims ? sizeof(float) * 2 * size_t(gpb) * LP : 0; }
-
-template <int DT, int VECB, int LPR>
-struct Fwd {
-    static msda_status_t run(const msda::Problem& pb, int ref_dims, const void* v, const void* ref,
-                             const uint8_t* kmask, const void* loc, const void* w, void* out, hipStream_t st) {
-        const int gpb = tile_queries(pb, LPR, 1024, true);
-        const int LP = pb.L * pb.P;
-        const size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
-        const void* k = ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
-                        : ref_dims == 2 ? fwd_kernel<DT, VECB, LPR, 2>(pb)
-                                        : fwd_kernel<DT, VECB, LPR, 4>(pb);
-        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, kmask, out, pb, gpb);
-    }
-};
-
-template <int DT, int VECB, int LPR>
-struct Grad {
-    static msda_status_t run(const msda::Problem& pb, bool binned, int ref_dims, const void* v, const void* ref,
-                             const uint8_t* kmask, const void* loc, const void* w, const void* gout, float* gacc,
-                             uint3* recs,
-                             int32_t* cursor, int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
-                             hipStream_t st) {
-        // (the gradient kernel keeps full workgroups: measured, its per-workgroup
-        // cursor reservation makes smaller ones slower on small problems)
-        const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples, false);
-        const int LP = pb.L * pb.P;
-        const int64_t blocks = plane_blocks(pb, gpb);
-        size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
-        if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg);
-        const void* k;
-        if (binned)
-            k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, true, 0>(pb)
-                : ref_dims == 2 ? grad_kernel<DT, VECB, LPR, true, 2>(pb)
-                                : grad_kernel<DT, VECB, LPR, true, 4>(pb);
-        else
-            k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, false, 0>(pb)
-                : ref_dims == 2 ? grad_kernel<DT, VECB, LPR, false, 2>(pb)
-                                : grad_kernel<DT, VECB, LPR, false, 4>(pb);
-        return launch(k, blocks, gpb * LPR, lds, st, v, loc, w, ref, kmask, gout, gacc, recs, cursor, nunits,
-                      multi, gloc, gw, pb, gpb);
-    }
-};
-
-template <int DT, int VECB, int LPR>
-struct Accum {
-    static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
-                             const uint3* recs, const int32_t* nunits, const int4* units, const uint8_t* kmask,
-                             float* gacc, void* gfinal, hipStream_t st) {
-        int max_shift = 0;
-        for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
-        const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
-                           sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
-                           2 * sizeof(int32_t) * msda::kMaxSegKeys;
-        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::acc_block(LPR), lds, st,
-                      gout, recs, nunits, units, kmask, gacc, gfinal, pb, plane_units);
-    }
-};
-
-// Records events[k] (when events is not NULL) on the stream just before
-// backward stage k; stage kStageEnd marks the end of the last stage.
-enum Stage { kStageZero = 0, kStageCount, kStageScan, kStageGrad, kStageAccum, kStageNarrow, kStageEnd };
-
-msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
-    if (events == nullptr) return MSDA_SUCCESS;
-    return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
-}
-
-template <int DT, int REF>
-const void* count_kernel(const msda::Problem& pb) {
-    return is_l4p4(pb) ? kfn(&msda::msda_bin_count_kernel<DT, 4, 4, REF>)
-                       : kfn(&msda::msda_bin_count_kernel<DT, 0, 0, REF>);
-}
-
-template <int DT, int REF>
-const void* count_scan_kernel(const msda::Problem& pb) {
-    return is_l4p4(pb) ? kfn(&msda::msda_bin_count_scan_kernel<DT, 4, 4, REF>)
-                       : kfn(&msda::msda_bin_count_scan_kernel<DT, 0, 0, REF>);
-}
-
-// Count records per segment and scan the counts into ranges, cursors and
-// units: one fused launch for small planes, else count (histogram rows) and
-// scan.  Events: the count stage before, the scan stage between.
-template <int DT>
-msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
-                                int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
-                                int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
-    MSDA_TRY(mark(ev, kStageCount, st));
-    if (fused_count_scan(pb)) {
-        const void* k = ref_dims == 0   ? count_scan_kernel<DT, 0>(pb)
-                        : ref_dims == 2 ? count_scan_kernel<DT, 2>(pb)
-                                        : count_scan_kernel<DT, 4>(pb);
-        MSDA_TRY(launch(k, pb.nplanes, msda::kCountScanBlock, 0, st, loc, ref, cursor, nunits, multi, units,
-                        accumulate, pb, plane_recs, plane_us));
-        return mark(ev, kStageScan, st);
-    }
-    const int64_t chunks = count_chunks(pb);
-    const void* k = ref_dims == 0   ? count_kernel<DT, 0>(pb)
-                    : ref_dims == 2 ? count_kernel<DT, 2>(pb)
-                                    : count_kernel<DT, 4>(pb);
-    MSDA_TRY(launch(k, int64_t(pb.nplanes) * chunks, msda::kCountBlock, sizeof(int32_t) * pb.nseg, st, loc, ref,
-                    counts, pb,
-                    static_cast<int>(count_chunk(pb))));
-    MSDA_TRY(mark(ev, kStageScan, st));
-    return launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kBlock, 0, st,
-                  static_cast<const int32_t*>(counts), static_cast<int>(chunks), cursor, nunits, multi, units,
-                  accumulate, pb, plane_recs, plane_us);
 }
 
 // Reference points of the fused prologue: ref_dims 0 (none; ref unused), 2
@@ -445,8 +242,17 @@ msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const vo
     if (out_elems(problem) == 0) return MSDA_SUCCESS;
     const msda::Problem pb = pack(problem);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    return by_dtype_split<Fwd>(problem->dtype, s, pb, ref_dims, value, ref, kmask, sampling_locations,
-                               attention_weights, output, stream);
+    switch (problem->dtype) {
+        case MSDA_F32:
+            return Launch<kF32>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
+                                         output, stream);
+        case MSDA_F16:
+            return Launch<kF16>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
+                                         output, stream);
+        default:
+            return Launch<kBF16>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
+                                          output, stream);
+    }
 }
 
 msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
@@ -465,6 +271,56 @@ msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* val
     return MSDA_SUCCESS;
 }
 
+
+// Dtype dispatch of the backward's launches.
+msda_status_t gradient(msda_dtype_t dt, const LaneSplit& s, const msda::Problem& pb, bool binned, int ref_dims,
+                       const void* v, const void* ref, const uint8_t* kmask, const void* loc, const void* w,
+                       const void* gout, float* gacc, uint3* recs, int32_t* cursor, int32_t* nunits,
+                       const int32_t* multi, void* gloc, void* gw, hipStream_t st) {
+    switch (dt) {
+        case MSDA_F32:
+            return Launch<kF32>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
+                                          nunits, multi, gloc, gw, st);
+        case MSDA_F16:
+            return Launch<kF16>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
+                                          nunits, multi, gloc, gw, st);
+        default:
+            return Launch<kBF16>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
+                                           nunits, multi, gloc, gw, st);
+    }
+}
+
+msda_status_t accumulate_rows(msda_dtype_t dt, const LaneSplit& s, const msda::Problem& pb, int64_t max_units,
+                              int plane_units, const void* gout, const uint3* recs, const int32_t* nunits,
+                              const int4* units, const uint8_t* kmask, float* gacc, void* gfinal, hipStream_t st) {
+    switch (dt) {
+        case MSDA_F32:
+            return Launch<kF32>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
+                                            gfinal, st);
+        case MSDA_F16:
+            return Launch<kF16>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
+                                            gfinal, st);
+        default:
+            return Launch<kBF16>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
+                                             gfinal, st);
+    }
+}
+
+msda_status_t count_scan(msda_dtype_t dt, const msda::Problem& pb, int ref_dims, const void* ref,
+                         const void* loc, int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi,
+                         int4* units, int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
+    switch (dt) {
+        case MSDA_F32:
+            return Launch<kF32>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
+                                            plane_recs, plane_us, ev, st);
+        case MSDA_F16:
+            return Launch<kF16>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
+                                            plane_recs, plane_us, ev, st);
+        default:
+            return Launch<kBF16>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
+                                             accumulate, plane_recs, plane_us, ev, st);
+    }
+}
 
 // The backward.  accumulate = 1: grad_value is added into the float32
 // buffer gacc (gfinal unused).  accumulate = 0: grad_value is overwritten
@@ -497,7 +353,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
         MSDA_TRY(mark(ev, kStageCount, st));
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
-        MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, false, ref_dims, value, ref, kmask, loc, w, gout, gacc,
+        MSDA_TRY(gradient(problem->dtype, s, pb, false, ref_dims, value, ref, kmask, loc, w, gout, gacc,
                                       static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
                                       static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
                                       gloc, gw, st));
@@ -521,27 +377,15 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
 
     MSDA_TRY(mark(ev, kStageZero, st));             // no zero fill on this path
     const int prec = static_cast<int>(plane_records(problem)), pun = static_cast<int>(plane_units(problem, pb));
-    switch (problem->dtype) {
-        case MSDA_F32:
-            MSDA_TRY(count_scan_launch<kF32>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                                             prec, pun, ev, st));
-            break;
-        case MSDA_F16:
-            MSDA_TRY(count_scan_launch<kF16>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                                             prec, pun, ev, st));
-            break;
-        default:
-            MSDA_TRY(count_scan_launch<kBF16>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
-                                              accumulate, prec, pun, ev, st));
-            break;
-    }
+    MSDA_TRY(count_scan(problem->dtype, pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
+                        prec, pun, ev, st));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(by_dtype_split<Grad>(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs,
+    MSDA_TRY(gradient(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs,
                                   cursor,
                                   nunits, static_cast<const int32_t*>(multi), gloc, gw,
                                   st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    MSDA_TRY(by_dtype_split<Accum>(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
+    MSDA_TRY(accumulate_rows(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
                                    gout, static_cast<const uint3*>(recs), static_cast<const int32_t*>(nunits),
                                    static_cast<const int4*>(units), kmask, gacc, narrow16 ? gfinal : nullptr, st));
     MSDA_TRY(mark(ev, kStageNarrow, st));

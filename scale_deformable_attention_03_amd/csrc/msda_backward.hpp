@@ -116,7 +116,7 @@ __device__ __forceinline__ int level_of_segment(const Problem& pb, int seg) {
 
 // Zero n16 16-byte words (a kernel, not a memset node, so that the backward
 // stays correct inside a captured HIP graph).
-__global__ void __launch_bounds__(kBlock) msda_zero_kernel(uint4* __restrict__ p, int64_t n16) {
+[[maybe_unused]] static __global__ void __launch_bounds__(kBlock) msda_zero_kernel(uint4* __restrict__ p, int64_t n16) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride)
         p[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -400,8 +400,9 @@ __device__ void scan_plane(const int32_t* s_cnt, int32_t* s_wrec, int32_t* s_wun
 }
 
 // One workgroup per plane: sums the plane's nchunks histogram rows, then
-// scan_plane.
-__global__ void __launch_bounds__(kBlock)
+// scan_plane.  (static: every translation unit that launches it has its own
+// copy, as for the other non-template kernels.)
+[[maybe_unused]] static __global__ void __launch_bounds__(kBlock)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
                      int accumulate, Problem pb, int plane_records, int plane_units) {

@@ -1,0 +1,103 @@
+// Host-side launch interface of the MSDeformAttn kernels, shared by the
+// C-ABI translation unit and the translation units that instantiate the
+// kernels (one per dtype, compiled in parallel): launch helpers, stage
+// events, counting plan, and the per-dtype launch functions.  Internal to
+// the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "msda.h"
+#include "msda_backward.hpp"
+#include "msda_forward.hpp"
+
+namespace msda_host {
+
+using msda::kBF16;
+using msda::kBlock;
+using msda::kF16;
+using msda::kF32;
+
+// Lane split of one group: VECB bytes per lane, LPR lanes (a power of two,
+// at least 4) of which `active` own channels.
+struct LaneSplit {
+    int vecb, lpr, active;
+};
+
+#define MSDA_TRY(expr)                                  \
+    do {                                                \
+        msda_status_t s_ = (expr);                      \
+        if (s_ != MSDA_SUCCESS) return s_;              \
+    } while (0)
+
+// Launch through hipLaunchKernel, whose return code belongs to this launch
+// alone (no sticky error of an earlier, unrelated call is read or cleared).
+template <typename... Args>
+msda_status_t launch(const void* kernel, int64_t blocks, int threads, size_t lds_bytes, hipStream_t stream,
+                     Args... args) {
+    if (blocks <= 0) return MSDA_SUCCESS;
+    if (blocks > 0x7fffffff) return MSDA_ERROR_NOT_SUPPORTED;
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), argv, lds_bytes,
+                           stream) == hipSuccess
+               ? MSDA_SUCCESS
+               : MSDA_ERROR_HIP;
+}
+
+template <typename K>
+const void* kfn(K* k) { return reinterpret_cast<const void*>(k); }
+
+// Counting: samples per counting workgroup (one histogram row each) and the
+// number of rows per plane; planes of at most kCountScanSamples samples are
+// counted and scanned by one workgroup instead (no rows).
+inline int64_t count_chunk(const msda::Problem& pb) {
+    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
+    return std::max<int64_t>(msda::kCountChunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks);
+}
+inline int64_t count_chunks(const msda::Problem& pb) {
+    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
+    return (nsamp + count_chunk(pb) - 1) / count_chunk(pb);
+}
+inline bool fused_count_scan(const msda::Problem& pb) {
+    return int64_t(pb.Q) * pb.L * pb.P <= msda::kCountScanSamples;
+}
+
+// Records events[k] (when events is not NULL) on the stream just before
+// backward stage k; stage kStageEnd marks the end of the last stage.
+enum Stage { kStageZero = 0, kStageCount, kStageScan, kStageGrad, kStageAccum, kStageNarrow, kStageEnd };
+
+inline msda_status_t mark(hipEvent_t* events, int stage, hipStream_t st) {
+    if (events == nullptr) return MSDA_SUCCESS;
+    return hipEventRecord(events[stage], st) == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_HIP;
+}
+
+// The launches of one dtype.  Declared here; defined in
+// msda_launch_impl.hpp and instantiated once per dtype, each in a
+// translation unit of its own (msda_kernels_<dtype>.hip), so that the C-ABI
+// translation unit compiles no kernel.
+template <int DT>
+struct Launch {
+    static msda_status_t forward(const LaneSplit& s, const msda::Problem& pb, int ref_dims, const void* v,
+                                 const void* ref, const uint8_t* kmask, const void* loc, const void* w, void* out,
+                                 hipStream_t st);
+    static msda_status_t gradient(const LaneSplit& s, const msda::Problem& pb, bool binned, int ref_dims,
+                                  const void* v, const void* ref, const uint8_t* kmask, const void* loc,
+                                  const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor,
+                                  int32_t* nunits, const int32_t* multi, void* gloc, void* gw, hipStream_t st);
+    static msda_status_t accumulate(const LaneSplit& s, const msda::Problem& pb, int64_t max_units, int plane_units,
+                                    const void* gout, const uint3* recs, const int32_t* nunits, const int4* units,
+                                    const uint8_t* kmask, float* gacc, void* gfinal, hipStream_t st);
+    static msda_status_t count_scan(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
+                                    int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
+                                    int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st);
+};
+
+extern template struct Launch<kF32>;
+extern template struct Launch<kF16>;
+extern template struct Launch<kBF16>;
+
+}  // namespace msda_host
