@@ -19,7 +19,8 @@ timed on the host cores as a reported baseline.  A second object,
 "fused_prologue", times the fused form on the same shapes (reference points,
 offsets and logits in; msda_forward_fused + msda_backward_fused) beside the
 module path it replaces (PyTorch ops for the locations and the softmax and
-their backward around the core).
+their backward around the core).  A third, "mixed_precision", times the
+encoder step with bf16 value-side tensors and float32 per-sample tensors.
 """
 from __future__ import annotations
 
@@ -43,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_03_amd", "csrc", f)
                   for f in ("msda_api.hip", "msda_forward.hpp", "msda_backward.hpp", "msda_device.hpp",
                             "msda_launch.hpp", "msda_launch_impl.hpp", "msda_kernels_f32.hip",
-                            "msda_kernels_f16.hip", "msda_kernels_bf16.hip")]
+                            "msda_kernels_f16.hip", "msda_kernels_bf16.hip", "msda_kernels_f16_f32.hip",
+                            "msda_kernels_bf16_f32.hip")]
 
 
 def log(*a):
@@ -316,6 +318,54 @@ def fused_prologue_leg(wl_core, dev, steps: int, warmup: int, nsets: int) -> dic
             "speedup_vs_module_path": round(module_ms / fused_ms, 3)}
 
 
+def mixed_precision_leg(dev, steps: int, warmup: int, nsets: int) -> dict:
+    """The encoder step with bf16 value, output and value gradient and
+    float32 locations, weights and their gradients (MSDA_BF16_F32), same
+    shapes and draws as the float32 headline workload."""
+    import torch
+    from scale_deformable_attention_03_amd import _lib, ops
+    from scale_deformable_attention_03_amd import workloads as W
+
+    wl = W.detr_encoder(dtype="bf16", sample_dtype="f32")
+    bs, K, M, D = wl.value.shape
+    Q = wl.sampling_locations.shape[1]
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+    need_ws = _lib.workspace_bytes(prob)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    sets = []
+    for _ in range(nsets):
+        s = dict(value=wl.value.to(dev), loc=wl.sampling_locations.to(dev), w=wl.attention_weights.to(dev),
+                 g=wl.grad_output.to(dev))
+        s["out"] = torch.empty(bs, Q, M * D, dtype=wl.value.dtype, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["gl"] = torch.empty_like(s["loc"])
+        s["gw"] = torch.empty_like(s["w"])
+        s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
+        s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
+        sets.append(s)
+
+    def step(s):
+        p = s["ptr"]
+        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
+        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                      p["ws"] if need_ws else 0, need_ws, sp)
+
+    for i in range(warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        step(sets[i % nsets])
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    log(f"[bench] mixed precision (bf16 value, f32 samples): {ms * 1e3:.1f} us/step")
+    return {"workload": "detr_encoder", "dtype": "bf16 value/output/grad_value, f32 locations/weights/grads",
+            "ms_per_step": round(ms, 5), "queries_per_s": round(bs * Q / (ms * 1e-3), 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +377,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision leg")
     ap.add_argument("--ingest-profiles", metavar="DIR",
                     help="summarise the rocprofv3 output of the profiling commands under DIR into profiles/ "
                          "(no GPU needed) and exit")
@@ -503,6 +554,9 @@ def main() -> int:
     if not args.no_fused:
         result["fused_prologue"] = fused_prologue_leg(wl, dev, max(10, args.steps // 2), max(2, args.warmup // 2),
                                                       nsets)
+    if not args.no_mixed and args.workload == "detr_encoder":
+        result["mixed_precision"] = mixed_precision_leg(dev, max(10, args.steps // 2), max(2, args.warmup // 2),
+                                                        nsets)
     if args.no_cpu_baseline:
         result["cpu_baseline"] = None
     else:

@@ -23,7 +23,7 @@
  *     rounded to float32 separately (no fused multiply-add).  A sample takes
  *     part only when -1 < x < W and -1 < y < H (NaN and +-Inf fail); a corner
  *     outside the map reads as zero (per-corner zero padding).
- *   - Layouts (all row-major, contiguous, one dtype for every float tensor):
+ *   - Layouts (all row-major, contiguous; float types per msda_dtype_t):
  *       value                   [batch, num_keys, num_heads, embed_dims]
  *       sampling_locations      [batch, num_queries, num_heads, num_levels, num_points, 2]  (x, y)
  *       attention_weights       [batch, num_queries, num_heads, num_levels, num_points]
@@ -62,12 +62,21 @@ extern "C" {
 
 #define MSDA_ABI_VERSION 1
 
-/* Float type of every float tensor of one call (fp32 and fp16 per the
- * Ascend API page's dtype list; bf16 in addition). */
+/* Float types of one call.  MSDA_F32, MSDA_F16, MSDA_BF16: every float
+ * tensor in that type (fp32 and fp16 per the Ascend API page's dtype list;
+ * bf16 in addition).  Mixed precision: MSDA_F16_F32 and MSDA_BF16_F32 keep
+ * the value-side tensors (value, output, grad_output, grad_value) in fp16 /
+ * bf16 and the per-sample tensors (sampling_locations, attention_weights,
+ * their gradients; for the fused entry points reference_points,
+ * sampling_offsets, attention_logits and their gradients) in float32, so
+ * that locations and weights keep float32 resolution while the gathered
+ * rows are half as wide. */
 typedef enum {
     MSDA_F32 = 0,
     MSDA_F16 = 1,
-    MSDA_BF16 = 2
+    MSDA_BF16 = 2,
+    MSDA_F16_F32 = 3,
+    MSDA_BF16_F32 = 4
 } msda_dtype_t;
 
 typedef enum {
@@ -190,7 +199,7 @@ msda_status_t msda_backward(const msda_problem_t *problem,
  *   grad_value_acc (device, float32, laid out like value whatever the
  *   problem's dtype) is ACCUMULATED into: grad_value_acc[corner row] +=
  *   w * (bilinear weight) * grad_output; the caller zeroes or pre-fills it.
- *   grad_sampling_locations and grad_attention_weights (problem dtype) are
+ *   grad_sampling_locations and grad_attention_weights (per-sample type) are
  *   overwritten, as in msda_backward.  Same kernels as msda_backward except
  *   that the accumulation kernel adds its rows with float atomics (and no
  *   conversion kernel runs).  For callers that sum the value gradient of
@@ -254,7 +263,7 @@ msda_status_t msda_backward_profile(const msda_problem_t *problem,
  * one operation at a time in the order written (no fused multiply-add); the
  * softmax subtracts the group's maximum, sums exp in float32 and divides.
  *   reference_points  [batch, num_queries, num_levels, ref_dims] (x, y) or
- *                     (x, y, w, h), normalised, problem dtype
+ *                     (x, y, w, h), normalised, per-sample type
  *   sampling_offsets  [batch, num_queries, num_heads, num_levels, num_points, 2]
  *                     (x, y), in pixels of the level (2-d) or in units of
  *                     P half-box sizes (4-d)

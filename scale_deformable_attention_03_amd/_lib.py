@@ -14,6 +14,8 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
 
 MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
+# mixed precision: fp16 / bf16 value side, float32 per-sample tensors
+MSDA_F16_F32, MSDA_BF16_F32 = 3, 4
 STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
           3: "MSDA_ERROR_MISALIGNED", 4: "MSDA_ERROR_HIP"}
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",

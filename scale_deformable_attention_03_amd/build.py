@@ -13,10 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsda.so")
-# the C ABI and one translation unit of kernel instantiations per dtype,
+# the C ABI and one translation unit of kernel instantiations per dtype code,
 # compiled in parallel and linked into one library
 SOURCES = [os.path.join(CSRC, f) for f in ("msda_api.hip", "msda_kernels_f32.hip", "msda_kernels_f16.hip",
-                                            "msda_kernels_bf16.hip")]
+                                            "msda_kernels_bf16.hip", "msda_kernels_f16_f32.hip",
+                                            "msda_kernels_bf16_f32.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp",
                                            "msda_launch.hpp", "msda_launch_impl.hpp")] + [os.path.join(INCLUDE, "msda.h")]
 

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "msda.h"
 #include "msda_launch.hpp"
@@ -37,7 +38,25 @@ using msda_host::kStageEnd;
 
 constexpr int64_t kIndexLimit = int64_t(1) << 31;
 
+// Bytes of a value-side element (value, output and their gradients): 2
+// for fp16, bf16 and the mixed codes, whose per-sample tensors are float32.
 int elem_bytes(msda_dtype_t dt) { return dt == MSDA_F32 ? 4 : 2; }
+
+msda_dtype_t value_dtype(msda_dtype_t dt) {
+    return dt == MSDA_F16_F32 ? MSDA_F16 : dt == MSDA_BF16_F32 ? MSDA_BF16 : dt;
+}
+
+// Calls f(std::integral_constant<int, code>) for the kernels' dtype code.
+template <typename F>
+msda_status_t by_code(msda_dtype_t dt, F&& f) {
+    switch (dt) {
+        case MSDA_F32: return f(std::integral_constant<int, kF32>{});
+        case MSDA_F16: return f(std::integral_constant<int, kF16>{});
+        case MSDA_BF16: return f(std::integral_constant<int, kBF16>{});
+        case MSDA_F16_F32: return f(std::integral_constant<int, msda::kF16M>{});
+        default: return f(std::integral_constant<int, msda::kBF16M>{});
+    }
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,7 +72,8 @@ LaneSplit lane_split(int embed_dims, msda_dtype_t dt) {
 
 msda_status_t check_problem(const msda_problem_t* p) {
     if (p == nullptr) return MSDA_ERROR_INVALID_VALUE;
-    if (p->dtype != MSDA_F32 && p->dtype != MSDA_F16 && p->dtype != MSDA_BF16)
+    if (p->dtype != MSDA_F32 && p->dtype != MSDA_F16 && p->dtype != MSDA_BF16 && p->dtype != MSDA_F16_F32 &&
+        p->dtype != MSDA_BF16_F32)
         return MSDA_ERROR_INVALID_VALUE;
     if (p->batch < 0 || p->num_queries < 0 || p->num_keys < 1 || p->num_heads < 1 ||
         p->embed_dims < 1 || p->num_levels < 1 || p->num_points < 1)
@@ -242,17 +262,10 @@ msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const vo
     if (out_elems(problem) == 0) return MSDA_SUCCESS;
     const msda::Problem pb = pack(problem);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    switch (problem->dtype) {
-        case MSDA_F32:
-            return Launch<kF32>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
-                                         output, stream);
-        case MSDA_F16:
-            return Launch<kF16>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
-                                         output, stream);
-        default:
-            return Launch<kBF16>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations, attention_weights,
-                                          output, stream);
-    }
+    return by_code(problem->dtype, [&](auto c) {
+        return Launch<decltype(c)::value>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations,
+                                                   attention_weights, output, stream);
+    });
 }
 
 msda_status_t check_backward_ptrs(const msda_problem_t* problem, const void* value,
@@ -277,49 +290,28 @@ msda_status_t gradient(msda_dtype_t dt, const LaneSplit& s, const msda::Problem&
                        const void* v, const void* ref, const uint8_t* kmask, const void* loc, const void* w,
                        const void* gout, float* gacc, uint3* recs, int32_t* cursor, int32_t* nunits,
                        const int32_t* multi, void* gloc, void* gw, hipStream_t st) {
-    switch (dt) {
-        case MSDA_F32:
-            return Launch<kF32>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
-                                          nunits, multi, gloc, gw, st);
-        case MSDA_F16:
-            return Launch<kF16>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
-                                          nunits, multi, gloc, gw, st);
-        default:
-            return Launch<kBF16>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs, cursor,
-                                           nunits, multi, gloc, gw, st);
-    }
+    return by_code(dt, [&](auto c) {
+        return Launch<decltype(c)::value>::gradient(s, pb, binned, ref_dims, v, ref, kmask, loc, w, gout, gacc, recs,
+                                                    cursor, nunits, multi, gloc, gw, st);
+    });
 }
 
 msda_status_t accumulate_rows(msda_dtype_t dt, const LaneSplit& s, const msda::Problem& pb, int64_t max_units,
                               int plane_units, const void* gout, const uint3* recs, const int32_t* nunits,
                               const int4* units, const uint8_t* kmask, float* gacc, void* gfinal, hipStream_t st) {
-    switch (dt) {
-        case MSDA_F32:
-            return Launch<kF32>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
-                                            gfinal, st);
-        case MSDA_F16:
-            return Launch<kF16>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
-                                            gfinal, st);
-        default:
-            return Launch<kBF16>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
-                                             gfinal, st);
-    }
+    return by_code(dt, [&](auto c) {
+        return Launch<decltype(c)::value>::accumulate(s, pb, max_units, plane_units, gout, recs, nunits, units,
+                                                      kmask, gacc, gfinal, st);
+    });
 }
 
 msda_status_t count_scan(msda_dtype_t dt, const msda::Problem& pb, int ref_dims, const void* ref,
                          const void* loc, int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi,
                          int4* units, int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
-    switch (dt) {
-        case MSDA_F32:
-            return Launch<kF32>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                                            plane_recs, plane_us, ev, st);
-        case MSDA_F16:
-            return Launch<kF16>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                                            plane_recs, plane_us, ev, st);
-        default:
-            return Launch<kBF16>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
-                                             accumulate, plane_recs, plane_us, ev, st);
-    }
+    return by_code(dt, [&](auto c) {
+        return Launch<decltype(c)::value>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
+                                                      accumulate, plane_recs, plane_us, ev, st);
+    });
 }
 
 // The backward.  accumulate = 1: grad_value is added into the float32
@@ -361,7 +353,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
         MSDA_TRY(mark(ev, kStageNarrow, st));
         if (narrow16) {
             const int64_t n8 = value_elems(problem) / 8;
-            const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
+            const void* k = value_dtype(problem->dtype) == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
                                                        : kfn(&msda::msda_narrow_kernel<kBF16>);
             MSDA_TRY(launch(k, fill_blocks(n8), kBlock, 0, st, reinterpret_cast<const float4*>(gacc),
                             static_cast<uint4*>(gfinal), n8));
@@ -390,7 +382,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
                                    static_cast<const int4*>(units), kmask, gacc, narrow16 ? gfinal : nullptr, st));
     MSDA_TRY(mark(ev, kStageNarrow, st));
     if (narrow16) {
-        const void* k = problem->dtype == MSDA_F16 ? kfn(&msda::msda_narrow_segments_kernel<kF16>)
+        const void* k = value_dtype(problem->dtype) == MSDA_F16 ? kfn(&msda::msda_narrow_segments_kernel<kF16>)
                                                    : kfn(&msda::msda_narrow_segments_kernel<kBF16>);
         MSDA_TRY(launch(k, int64_t(pb.nplanes) * msda::kNarrowPerPlane, kBlock, 0, st,
                         static_cast<const float*>(gacc), gfinal, static_cast<const int32_t*>(nunits),

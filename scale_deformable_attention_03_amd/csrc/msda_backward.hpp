@@ -221,7 +221,7 @@ __device__ __forceinline__ void count_samples(const void* __restrict__ loc, cons
                 const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
                 const int64_t ri = (static_cast<int64_t>(b) * pb.Q + q) * L + l;
                 const int4 lv = s_lv[l];
-                const float2 xy = sample_location<DT, REF>(loc, ref, i, ri, static_cast<float>(lv.y),
+                const float2 xy = sample_location<sample_dt(DT), REF>(loc, ref, i, ri, static_cast<float>(lv.y),
                                                            static_cast<float>(lv.x), static_cast<float>(P));
                 lx[u] = xy.x;
                 ly[u] = xy.y;
@@ -247,7 +247,7 @@ __device__ __forceinline__ void count_samples(const void* __restrict__ loc, cons
 // each (the last chunk of a plane may be short).  Each workgroup writes its
 // own histogram row counts[(plane * nchunks + chunk) * nseg ...] in full, so
 // no buffer needs zeroing first.  LDS: nseg int32.
-template <int DT, int L_CT, int P_CT, int REF>
+template <int DTK, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kCountBlock)
 msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref, int32_t* __restrict__ counts,
                       Problem pb, int chunk) {
@@ -262,7 +262,7 @@ msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref
     stage_levels(pb, s_lv);
     for (int i = threadIdx.x; i < pb.nseg; i += kCountBlock) hist[i] = 0;
     __syncthreads();
-    count_samples<DT, L_CT, P_CT, REF, kCountBlock>(loc, ref, hist, s_lv, pb, b, m, c * chunk,
+    count_samples<DTK, L_CT, P_CT, REF, kCountBlock>(loc, ref, hist, s_lv, pb, b, m, c * chunk,
                                                     min((c + 1) * chunk, nsamp));
     __syncthreads();
     int32_t* row = counts + static_cast<int64_t>(blockIdx.x) * pb.nseg;
@@ -429,7 +429,7 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* _
 constexpr int kCountScanBlock = 1024;
 constexpr int kCountScanSamples = 8192;
 
-template <int DT, int L_CT, int P_CT, int REF>
+template <int DTK, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kCountScanBlock)
 msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict__ ref,
                            int32_t* __restrict__ cursor, int32_t* __restrict__ nunits, int32_t* __restrict__ multi,
@@ -446,7 +446,7 @@ msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict_
     if (threadIdx.x == 0) s_nmulti = 0;
     for (int i = threadIdx.x; i < pb.nseg; i += kCountScanBlock) s_cnt[i] = 0;
     __syncthreads();
-    count_samples<DT, L_CT, P_CT, REF, kCountScanBlock>(loc, ref, s_cnt, s_lv, pb, b, m, 0, pb.Q * LP);
+    count_samples<DTK, L_CT, P_CT, REF, kCountScanBlock>(loc, ref, s_cnt, s_lv, pb, b, m, 0, pb.Q * LP);
     __syncthreads();
     scan_plane<kCountScanBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb,
                                 pl, plane_records, plane_units);
@@ -467,7 +467,7 @@ msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict_
 // rows of the plane's multi-unit segments (the accumulation adds into them).
 // LDS: gpb * (8 * L * P + 4) words; when BINNED also 2 * nseg int32 (counts,
 // then cursors, and bases).
-template <int DT, int VECB, int LPR, int L_CT, int P_CT, bool BINNED, int REF>
+template <int DTK, int VECB, int LPR, int L_CT, int P_CT, bool BINNED, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                      const void* __restrict__ attw, const void* __restrict__ ref,
@@ -475,6 +475,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                      float* __restrict__ gacc, uint3* __restrict__ recs, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, const int32_t* __restrict__ multi,
                      void* __restrict__ grad_loc, void* __restrict__ grad_w, Problem pb, int gpb) {
+    constexpr int DT = value_dt(DTK), ST = sample_dt(DTK);
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr bool kFixedLP = L_CT != 0 && P_CT != 0;
@@ -497,7 +498,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     stage_levels(pb, s_lv);
     if constexpr (BINNED)
         for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) lhist[i] = 0;
-    if constexpr (REF != 0) load_logits<DT>(attw, t.G0, pb.M, t.gcount, LP, sv);
+    if constexpr (REF != 0) load_logits<ST>(attw, t.G0, pb.M, t.gcount, LP, sv);
     __syncthreads();
     if constexpr (REF != 0) {
         exp_logits(t.gcount, LP, sv, se);
@@ -514,14 +515,14 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const int4 lv = s_lv[l];
         const int H = lv.x, W = lv.y;
         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
-        const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(W), static_cast<float>(H),
+        const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(W), static_cast<float>(H),
                                                    static_cast<float>(P));
         Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
         // padded corners read as zero; their records still go to the
         // accumulation, which writes padded rows as zero
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, W);
         float aw;
-        if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        if constexpr (REF == 0) aw = c.ok ? load_scalar<ST>(attw, si) : 0.0f;
         else aw = se[i] / group_total(se + g * LP, LP);
         uint32_t* r = srec + g * gstride + lp * 8;
         const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
@@ -635,19 +636,19 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             if (li < kC) {
                 const int64_t s = G * LP + c0 + li;
                 if constexpr (REF == 0) {
-                    store_scalar<DT>(grad_w, s, own_w);
+                    store_scalar<ST>(grad_w, s, own_w);
                 } else {
                     sv[lg * LP + c0 + li] = own_w;       // the softmax backward below
                     if constexpr (REF == 4) {
                         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + lg) * L +
                                            static_cast<int>(own_a);
-                        const float2 wh = load_pair<DT>(ref, 2 * ri + 1);
+                        const float2 wh = load_pair<ST>(ref, 2 * ri + 1);
                         const float k = 0.5f / static_cast<float>(P);
                         own_x = own_x * static_cast<float>(pb.lv.W[static_cast<int>(own_a)]) * (wh.x * k);
                         own_y = own_y * static_cast<float>(pb.lv.H[static_cast<int>(own_a)]) * (wh.y * k);
                     }
                 }
-                store_pair<DT>(grad_loc, s, own_x, own_y);
+                store_pair<ST>(grad_loc, s, own_x, own_y);
             }
         }
     }
@@ -662,7 +663,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             float dot = 0.0f;
             for (int k = 0; k < LP; ++k) dot += __uint_as_float(r[8 * k]) * gg[k];
             const float wi = __uint_as_float(r[8 * (i - g * LP)]);
-            store_scalar<DT>(grad_w, (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + (i - g * LP), wi * (sv[i] - dot));
+            store_scalar<ST>(grad_w, (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + (i - g * LP), wi * (sv[i] - dot));
         }
     }
     if constexpr (BINNED) {
@@ -744,12 +745,13 @@ constexpr int kSortedPairSlots = kUnitRecords + kUnitRecords / 16 + 8;
 __device__ __forceinline__ int key_slot(int i) { return i + 4 * (i >> 5); }
 __device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 
-template <int DT, int VECB, int LPR>
-__global__ void __launch_bounds__(acc_block(LPR), DT == kF32 ? 6 : 5)
+template <int DTK, int VECB, int LPR>
+__global__ void __launch_bounds__(acc_block(LPR), value_dt(DTK) == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits, const int4* __restrict__ units,
                        const uint8_t* __restrict__ kmask, float* __restrict__ gacc, void* __restrict__ gfinal,
                        Problem pb, int plane_units) {
+    constexpr int DT = value_dt(DTK);                 // the accumulation touches no per-sample tensor
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     constexpr int kAccBlock = acc_block(LPR);

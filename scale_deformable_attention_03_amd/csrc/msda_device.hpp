@@ -16,6 +16,15 @@ namespace msda {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// Kernel dtype codes: kF32, kF16, kBF16 (every float tensor in that type),
+// or mixed precision: kF16M / kBF16M keep value, output and their gradients
+// in fp16 / bf16 and the per-sample tensors (locations or offsets, weights
+// or logits, reference points, and their gradients) in float32.
+constexpr int kF16M = 3, kBF16M = 4;
+// type of the value-side tensors, and of the per-sample tensors
+constexpr int value_dt(int code) { return code == kF16M ? kF16 : code == kBF16M ? kBF16 : code; }
+constexpr int sample_dt(int code) { return code >= kF16M ? kF32 : code; }
+
 template <int DT> struct Elem;
 template <> struct Elem<kF32> { static constexpr int bytes = 4; };
 template <> struct Elem<kF16> { static constexpr int bytes = 2; };

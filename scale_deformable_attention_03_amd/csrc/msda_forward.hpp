@@ -110,11 +110,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value,
 // REF = 2 or 4: they are the sampling offsets and attention logits, and ref
 // holds the reference points (see sample_location).  kmask: [bs, K] key
 // padding bytes or null (see mask_corners).
-template <int DT, int VECB, int LPR, int L_CT, int P_CT, int REF>
+template <int DTK, int VECB, int LPR, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                     const void* __restrict__ attw, const void* __restrict__ ref,
                     const uint8_t* __restrict__ kmask, void* __restrict__ out, Problem pb, int gpb) {
+    constexpr int DT = value_dt(DTK), ST = sample_dt(DTK);
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
     const int L = L_CT ? L_CT : pb.L;
@@ -130,7 +131,7 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     // fused prologue: the workgroup's logits and their exponentials
     float* sv = reinterpret_cast<float*>(sm + gpb * gstride);
     float* se = sv + gpb * LP;
-    if constexpr (REF != 0) load_logits<DT>(attw, t.G0, pb.M, t.gcount, LP, sv);
+    if constexpr (REF != 0) load_logits<ST>(attw, t.G0, pb.M, t.gcount, LP, sv);
     __syncthreads();
     if constexpr (REF != 0) {
         exp_logits(t.gcount, LP, sv, se);
@@ -143,12 +144,12 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
         const int4 lv = s_lv[l];
         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
-        const float2 xy = sample_location<DT, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
+        const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
                                                    static_cast<float>(lv.x), static_cast<float>(P));
         Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
         float aw;
-        if constexpr (REF == 0) aw = c.ok ? load_scalar<DT>(attw, si) : 0.0f;
+        if constexpr (REF == 0) aw = c.ok ? load_scalar<ST>(attw, si) : 0.0f;
         else aw = c.ok ? se[i] / group_total(se + g * LP, LP) : 0.0f;
         const float wy0 = aw * c.hy, wy1 = aw * c.ly;
         uint32_t* r = sm + g * gstride + lp * 8;

@@ -99,5 +99,7 @@ struct Launch {
 extern template struct Launch<kF32>;
 extern template struct Launch<kF16>;
 extern template struct Launch<kBF16>;
+extern template struct Launch<msda::kF16M>;
+extern template struct Launch<msda::kBF16M>;
 
 }  // namespace msda_host

@@ -34,6 +34,11 @@ locations and weights ("Deformable DETR walkthrough", section 2.2.4):
 and differentiates with respect to value, sampling_offsets and
 attention_logits (reference points and the mask get no gradient).
 
+Float types: every float tensor in one of float32, float16, bfloat16; or
+mixed precision, with value, output and their gradients in float16 or
+bfloat16 and the per-sample tensors (locations or offsets, weights or
+logits, reference points and their gradients) in float32.
+
 This module only marshals arguments: PyTorch supplies device memory and the
 current stream, the HIP library computes.  The shape tensors are read on the
 host (a device copy is fetched once per call, which synchronises).
@@ -47,6 +52,19 @@ from . import _lib
 
 DTYPE_CODE = {torch.float32: _lib.MSDA_F32, torch.float16: _lib.MSDA_F16,
               torch.bfloat16: _lib.MSDA_BF16}
+
+
+MIXED_CODE = {torch.float16: _lib.MSDA_F16_F32, torch.bfloat16: _lib.MSDA_BF16_F32}
+
+
+def dtype_code(value_dtype, sample_dtype) -> int:
+    """The library's dtype code for value-side and per-sample float types."""
+    if value_dtype == sample_dtype and value_dtype in DTYPE_CODE:
+        return DTYPE_CODE[value_dtype]
+    if sample_dtype == torch.float32 and value_dtype in MIXED_CODE:
+        return MIXED_CODE[value_dtype]
+    raise TypeError(f"unsupported float types: value {value_dtype}, per-sample tensors {sample_dtype} "
+                    "(one type for all, or float16/bfloat16 values with float32 per-sample tensors)")
 
 
 def _host_int64(x) -> np.ndarray:
@@ -74,8 +92,7 @@ def problem_for(value: torch.Tensor, spatial_shapes, level_start_index,
     """(Problem, keepalive) for tensors laid out as in the module docstring."""
     if value.dim() != 4 or sampling_locations.dim() != 6 or sampling_locations.shape[-1] != 2:
         raise ValueError("value must be [bs, K, M, D] and sampling_locations [bs, Q, M, L, P, 2]")
-    if value.dtype not in DTYPE_CODE:
-        raise TypeError(f"unsupported dtype {value.dtype}")
+    code = dtype_code(value.dtype, sampling_locations.dtype)
     bs, K, M, D = value.shape
     bs2, Q, M2, L, P, _ = sampling_locations.shape
     if bs2 != bs or M2 != M:
@@ -84,7 +101,7 @@ def problem_for(value: torch.Tensor, spatial_shapes, level_start_index,
     starts = _host_int64(level_start_index).reshape(-1)
     if shapes.shape[0] != L or starts.shape[0] != L:
         raise ValueError("spatial_shapes / level_start_index do not match num_levels")
-    return _lib.make_problem(bs, K, M, D, L, P, Q, DTYPE_CODE[value.dtype], shapes, starts)
+    return _lib.make_problem(bs, K, M, D, L, P, Q, code, shapes, starts)
 
 
 def _stream(device: torch.device) -> int:
@@ -95,12 +112,12 @@ def forward(value, spatial_shapes, level_start_index, sampling_locations, attent
             out: torch.Tensor | None = None) -> torch.Tensor:
     """One msda_forward call on the current stream; returns output."""
     prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
-    dev, dt = value.device, value.dtype
+    dev, dt, st = value.device, value.dtype, sampling_locations.dtype
     bs, K, M, D = value.shape
     _, Q, _, L, P, _ = sampling_locations.shape
     _check(value, "value", dt, dev)
-    _check(sampling_locations, "sampling_locations", dt, dev)
-    _check(attention_weights, "attention_weights", dt, dev, (bs, Q, M, L, P))
+    _check(sampling_locations, "sampling_locations", st, dev)
+    _check(attention_weights, "attention_weights", st, dev, (bs, Q, M, L, P))
     if out is None:
         out = torch.empty((bs, Q, M * D), dtype=dt, device=dev)
     _check(out, "output", dt, dev, (bs, Q, M * D))
@@ -114,20 +131,20 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations, atten
     """One msda_backward call on the current stream; returns
     (grad_value, grad_sampling_locations, grad_attention_weights)."""
     prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
-    dev, dt = value.device, value.dtype
+    dev, dt, st = value.device, value.dtype, sampling_locations.dtype
     bs, K, M, D = value.shape
     _, Q, _, L, P, _ = sampling_locations.shape
     _check(value, "value", dt, dev)
-    _check(sampling_locations, "sampling_locations", dt, dev)
-    _check(attention_weights, "attention_weights", dt, dev, (bs, Q, M, L, P))
+    _check(sampling_locations, "sampling_locations", st, dev)
+    _check(attention_weights, "attention_weights", st, dev, (bs, Q, M, L, P))
     _check(grad_output, "grad_output", dt, dev, (bs, Q, M * D))
     if grads is None:
         grads = (torch.empty_like(value), torch.empty_like(sampling_locations),
                  torch.empty_like(attention_weights))
     gv, gl, gw = grads
     _check(gv, "grad_value", dt, dev, value.shape)
-    _check(gl, "grad_sampling_locations", dt, dev, sampling_locations.shape)
-    _check(gw, "grad_attention_weights", dt, dev, attention_weights.shape)
+    _check(gl, "grad_sampling_locations", st, dev, sampling_locations.shape)
+    _check(gw, "grad_attention_weights", st, dev, attention_weights.shape)
     need = _lib.workspace_bytes(prob)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -175,15 +192,15 @@ def _mask_ptr(value, key_padding_mask) -> int:
 
 
 def _check_fused(value, reference_points, sampling_offsets, attention_logits):
-    dev, dt = value.device, value.dtype
+    dev, dt, st = value.device, value.dtype, sampling_offsets.dtype
     bs, K, M, D = value.shape
     _, Q, _, L, P, _ = sampling_offsets.shape
     _check(value, "value", dt, dev)
-    _check(sampling_offsets, "sampling_offsets", dt, dev)
-    _check(attention_logits, "attention_logits", dt, dev, (bs, Q, M, L, P))
+    _check(sampling_offsets, "sampling_offsets", st, dev)
+    _check(attention_logits, "attention_logits", st, dev, (bs, Q, M, L, P))
     if reference_points.dim() != 4 or reference_points.shape[-1] not in (2, 4):
         raise ValueError("reference_points must be [bs, num_queries, num_levels, 2 or 4]")
-    _check(reference_points, "reference_points", dt, dev, (bs, Q, L, reference_points.shape[-1]))
+    _check(reference_points, "reference_points", st, dev, (bs, Q, L, reference_points.shape[-1]))
     return int(reference_points.shape[-1])
 
 
@@ -221,8 +238,8 @@ def backward_fused(value, spatial_shapes, level_start_index, reference_points, s
                  torch.empty_like(attention_logits))
     gv, go, gl = grads
     _check(gv, "grad_value", dt, dev, value.shape)
-    _check(go, "grad_sampling_offsets", dt, dev, sampling_offsets.shape)
-    _check(gl, "grad_attention_logits", dt, dev, attention_logits.shape)
+    _check(go, "grad_sampling_offsets", sampling_offsets.dtype, dev, sampling_offsets.shape)
+    _check(gl, "grad_attention_logits", sampling_offsets.dtype, dev, attention_logits.shape)
     need = _lib.workspace_bytes(prob)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

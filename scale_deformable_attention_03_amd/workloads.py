@@ -49,6 +49,7 @@ class Workload:
     attention_weights: torch.Tensor  # [bs, Q, M, L, P]
     grad_output: torch.Tensor        # [bs, Q, M*D]
     meta: dict = field(default_factory=dict)
+    sample_dtype: str | None = None  # per-sample tensors' type when it differs (mixed precision)
 
     @property
     def dims(self):
@@ -92,8 +93,12 @@ def pixel_centre_refs(shapes) -> np.ndarray:
 def make(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries: int,
          dtype: str, seed: int, value_dist: str = "normal", loc_dist: str = "uniform",
          loc_args: tuple = (0.0, 1.0), weight_dist: str = "softmax", grad_dist: str = "normal",
-         meta: dict | None = None) -> Workload:
+         meta: dict | None = None, sample_dtype: str | None = None) -> Workload:
     """General seeded generator.
+
+    dtype is the value-side type (value, grad_output); sample_dtype, when
+    given, the per-sample tensors' type (mixed precision: "f32"), else dtype.
+    The draws are the same either way.
 
     value_dist:  "normal" N(0,1) | "u001" U[0,1)*0.01
     loc_dist:    "uniform" U[lo,hi]^2 i.i.d. per sample (loc_args = (lo, hi))
@@ -153,11 +158,13 @@ def make(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries
     else:
         raise ValueError(grad_dist)
 
+    sdt = sample_dtype or dtype
     return Workload(name=name, dtype=dtype, spatial_shapes=shapes,
                     level_start_index=level_starts(shapes),
-                    value=_cast(value, dtype), sampling_locations=_cast(loc, dtype),
-                    attention_weights=_cast(w, dtype), grad_output=_cast(g, dtype),
-                    meta=dict(meta or {}, seed=seed))
+                    value=_cast(value, dtype), sampling_locations=_cast(loc, sdt),
+                    attention_weights=_cast(w, sdt), grad_output=_cast(g, dtype),
+                    meta=dict(meta or {}, seed=seed),
+                    sample_dtype=None if sdt == dtype else sdt)
 
 
 # --- the five named workloads -------------------------------------------------
@@ -178,19 +185,20 @@ def tiny_single_level(kink: bool = False) -> Workload:
                 weight_dist="u+1e-5", grad_dist="ones")
 
 
-def detr_encoder(bs: int = 2, dtype: str = "f32", sigma: float = 0.02, seed: int = 1002) -> Workload:
+def detr_encoder(bs: int = 2, dtype: str = "f32", sigma: float = 0.02, seed: int = 1002,
+                 sample_dtype: str | None = None) -> Workload:
     """Deformable-DETR encoder self-attention: 4 levels (100,134) (50,67)
     (25,34) (13,17), K = Q = 17821, 8 heads x 32 dims, 4 points."""
     K = sum(h * w for h, w in DETR_LEVELS)
     return make("detr_encoder", bs, DETR_LEVELS, 8, 32, 4, K, dtype, seed,
-                loc_dist="encoder", loc_args=(sigma, -0.05, 1.05))
+                loc_dist="encoder", loc_args=(sigma, -0.05, 1.05), sample_dtype=sample_dtype)
 
 
-def detr_decoder(dtype: str = "f32") -> Workload:
+def detr_decoder(dtype: str = "f32", sample_dtype: str | None = None) -> Workload:
     """Deformable-DETR decoder cross-attention: the encoder's 4-level value,
     bs 2, 300 queries, 4 points; refs U[0,1]^2 + N(0, 0.05) offsets."""
     return make("detr_decoder", 2, DETR_LEVELS, 8, 32, 4, 300, dtype, 1003,
-                loc_dist="decoder", loc_args=(0.05,))
+                loc_dist="decoder", loc_args=(0.05,), sample_dtype=sample_dtype)
 
 
 def large_batch_encoder(bs: int = 8, dtype: str = "bf16") -> Workload:
@@ -236,6 +244,7 @@ class FusedWorkload:
     grad_output: torch.Tensor        # [bs, Q, M*D]
     key_padding_mask: torch.Tensor | None = None   # bool [bs, K] or None
     meta: dict = field(default_factory=dict)
+    sample_dtype: str | None = None  # per-sample tensors' type when it differs (mixed precision)
 
     @property
     def ref_dims(self) -> int:
@@ -285,7 +294,8 @@ def padding_masks(shapes, valid) -> tuple[np.ndarray, np.ndarray]:
 
 def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, queries: int,
                dtype: str, seed: int, ref_dims: int = 2, ref_dist: str = "uniform",
-               offset_sigma: float = 1.0, valid=None, meta: dict | None = None) -> FusedWorkload:
+               offset_sigma: float = 1.0, valid=None, meta: dict | None = None,
+               sample_dtype: str | None = None) -> FusedWorkload:
     """Seeded inputs of the fused form.
 
     ref_dist:  "encoder" the pixel centre of query q (queries = keys), the
@@ -303,7 +313,7 @@ def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, q
     N(0, offset_sigma) pixels per sample -- the 4-d form reads the same
     numbers in units of P half box sizes.  Logits: N(0, 1).
     Draw order: value, reference points, box sizes, offsets, logits,
-    grad_output.
+    grad_output.  sample_dtype as for make.
     """
     shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
     L = shapes.shape[0]
@@ -336,12 +346,13 @@ def make_fused(name: str, bs: int, shapes, heads: int, dims: int, points: int, q
     off = offset_directions(M, L, P)[None, None] + rng.normal(0.0, offset_sigma, size=(bs, Q, M, L, P, 2))
     logits = rng.standard_normal((bs, Q, M, L, P))
     g = rng.standard_normal((bs, Q, M * D))
+    sdt = sample_dtype or dtype
     return FusedWorkload(name=name, dtype=dtype, spatial_shapes=shapes, level_start_index=level_starts(shapes),
-                         value=_cast(value, dtype), reference_points=_cast(ref, dtype),
-                         sampling_offsets=_cast(off, dtype), attention_logits=_cast(logits, dtype),
+                         value=_cast(value, dtype), reference_points=_cast(ref, sdt),
+                         sampling_offsets=_cast(off, sdt), attention_logits=_cast(logits, sdt),
                          grad_output=_cast(g, dtype),
                          key_padding_mask=None if mask is None else torch.from_numpy(mask),
-                         meta=dict(meta or {}, seed=seed))
+                         meta=dict(meta or {}, seed=seed), sample_dtype=None if sdt == dtype else sdt)
 
 
 def detr_encoder_fused(bs: int = 2, dtype: str = "f32", seed: int = 1012) -> FusedWorkload:

@@ -81,20 +81,32 @@ def oracle_backward(wl, nthreads=0):
                            wl.f32("grad_output"), nthreads)
 
 
+def sample_tol(wl, kind):
+    """Tolerance of the per-sample gradients: their own type's (float32 in
+    mixed precision: computed in float32 from the same widened 16-bit rows
+    as the oracle's, and stored as float32)."""
+    return TOL[(wl.sample_dtype or wl.dtype, kind)]
+
+
+def tag(wl):
+    return f"{wl.name}/{wl.dtype}" + (f"+{wl.sample_dtype}" if wl.sample_dtype else "")
+
+
 def check_forward(wl, out=None):
     out = gpu_forward(wl) if out is None else out
     rtol, arms, atol = TOL[(wl.dtype, "fwd")]
-    assert_close(f"{wl.name}/{wl.dtype}/output", f64(out), oracle_forward(wl), rtol, arms, atol)
+    assert_close(f"{tag(wl)}/output", f64(out), oracle_forward(wl), rtol, arms, atol)
     return out
 
 
 def check_backward(wl, grads=None):
     gv, gl, gw = gpu_backward(wl) if grads is None else grads
     rgv, rgl, rgw = oracle_backward(wl)
+    rtol, arms, atol = sample_tol(wl, "bwd")
+    assert_close(f"{tag(wl)}/grad_attention_weights", f64(gw), rgw, rtol, arms, atol)
+    assert_close(f"{tag(wl)}/grad_sampling_locations", f64(gl), rgl, rtol, arms, atol)
     rtol, arms, atol = TOL[(wl.dtype, "bwd")]
-    assert_close(f"{wl.name}/{wl.dtype}/grad_attention_weights", f64(gw), rgw, rtol, arms, atol)
-    assert_close(f"{wl.name}/{wl.dtype}/grad_sampling_locations", f64(gl), rgl, rtol, arms, atol)
-    assert_close(f"{wl.name}/{wl.dtype}/grad_value", f64(gv), rgv, rtol, arms, atol)
+    assert_close(f"{tag(wl)}/grad_value", f64(gv), rgv, rtol, arms, atol)
     return gv, gl, gw
 
 
@@ -137,7 +149,7 @@ def oracle_mask(wl):
 def check_forward_fused(wl, out=None):
     out = gpu_forward_fused(wl) if out is None else out
     rtol, arms, atol = TOL[(wl.dtype, "fwd")]
-    assert_close(f"{wl.name}/{wl.dtype}/ref{wl.ref_dims}/output", f64(out),
+    assert_close(f"{tag(wl)}/ref{wl.ref_dims}/output", f64(out),
                  oracle.forward_fused(*oracle_fused_args(wl), oracle_mask(wl)), rtol, arms, atol)
     return out
 
@@ -145,9 +157,10 @@ def check_forward_fused(wl, out=None):
 def check_backward_fused(wl, grads=None):
     gv, goff, glog = gpu_backward_fused(wl) if grads is None else grads
     rgv, rgoff, rglog = oracle.backward_fused(*oracle_fused_args(wl), wl.f32("grad_output"), oracle_mask(wl))
+    t = f"{tag(wl)}/ref{wl.ref_dims}"
+    rtol, arms, atol = sample_tol(wl, "bwd")
+    assert_close(f"{t}/grad_attention_logits", f64(glog), rglog, rtol, arms, atol)
+    assert_close(f"{t}/grad_sampling_offsets", f64(goff), rgoff, rtol, arms, atol)
     rtol, arms, atol = TOL[(wl.dtype, "bwd")]
-    tag = f"{wl.name}/{wl.dtype}/ref{wl.ref_dims}"
-    assert_close(f"{tag}/grad_attention_logits", f64(glog), rglog, rtol, arms, atol)
-    assert_close(f"{tag}/grad_sampling_offsets", f64(goff), rgoff, rtol, arms, atol)
-    assert_close(f"{tag}/grad_value", f64(gv), rgv, rtol, arms, atol)
+    assert_close(f"{t}/grad_value", f64(gv), rgv, rtol, arms, atol)
     return gv, goff, glog

@@ -53,7 +53,8 @@ def test_status_strings():
     assert _lib.lib.msda_status_string(99).decode() == "MSDA_UNKNOWN_STATUS"
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(dtype=1), dict(dtype=2), dict(D=8), dict(D=256),
+@pytest.mark.parametrize("kw", [dict(), dict(dtype=1), dict(dtype=2), dict(dtype=3), dict(dtype=4), dict(D=8),
+                                dict(D=256),
                                 dict(M=1), dict(M=8), dict(P=16), dict(shapes=[(1, 1)], P=64),
                                 dict(bs=0), dict(Q=0), dict(shapes=[(3, 1)] * 64, P=1)])
 def test_valid_descriptors(kw):
@@ -72,6 +73,7 @@ def test_valid_descriptors(kw):
     (dict(bs=-1), INVALID),
     (dict(Q=-3), INVALID),
     (dict(dtype=7), INVALID),
+    (dict(dtype=5), INVALID),
     (dict(K=17820), INVALID),             # sum of H*W differs from num_keys
     (dict(st=[0, 13400, 16750, 17601]), INVALID),   # not the exclusive prefix sum
     (dict(st=[1, 13401, 16751, 17601]), INVALID),
@@ -111,7 +113,7 @@ def test_workspace_bytes():
     f32 = _lib.workspace_bytes(p)
     samples = 2 * 300 * 8 * 4 * 4
     assert 48 * samples <= f32 < 48 * samples + (8 << 20)
-    for dt in (1, 2):
+    for dt in (1, 2, 3, 4):          # fp16, bf16 and the mixed codes (16-bit values)
         p, keep = prob(dtype=dt)
         assert _lib.workspace_bytes(p) == f32 + 2 * 17821 * 8 * 32 * 4
     p, keep = prob(dtype=1, D=12)

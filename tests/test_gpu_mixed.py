@@ -1,0 +1,117 @@
+"""GPU parity of the mixed-precision dtype codes (MSDA_F16_F32,
+MSDA_BF16_F32): value, output, grad_output and grad_value in fp16 / bf16,
+the per-sample tensors and their gradients in float32.  Checked against the
+oracle fed the same (exactly widened) inputs: the value-side outputs at the
+16-bit bar, the float32 per-sample gradients at the float32 bar.  Covers the
+DETR encoder and decoder shapes at full size, every lane split of 16-bit
+rows, the generic kernels with off-map samples, the fused prologue with a
+padding mask, the accumulate entry point and the autograd wrapper."""
+import numpy as np
+import pytest
+import torch
+
+from scale_deformable_attention_03_amd import workloads as W
+from tests.parity import (TOL, assert_close, check_backward, check_backward_fused, check_forward,
+                          check_forward_fused, f64, fused_to_device, gpu_backward, gpu_backward_fused, gpu_forward,
+                          gpu_forward_fused, oracle_backward, tag, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+def run(wl):
+    print(f"[gpu] mixed {tag(wl)} {tuple(wl.sampling_locations.shape)}", flush=True)
+    t = to_device(wl)
+    out = gpu_forward(wl, t)
+    assert out.dtype == wl.value.dtype
+    check_forward(wl, out)
+    gv, gl, gw = gpu_backward(wl, t)
+    assert gv.dtype == wl.value.dtype and gl.dtype == torch.float32 and gw.dtype == torch.float32
+    check_backward(wl, (gv, gl, gw))
+
+
+@pytest.mark.parametrize("make", [lambda: W.detr_encoder(dtype="bf16", sample_dtype="f32"),
+                                  lambda: W.detr_decoder("f16", sample_dtype="f32"),
+                                  lambda: W.detr_decoder("bf16", sample_dtype="f32")],
+                         ids=["encoder_bf16_f32", "decoder_f16_f32", "decoder_bf16_f32"])
+def test_detr_shapes_full_size(make):
+    run(make())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [8, 16, 32, 64, 128, 256])
+def test_lane_splits(dtype, D):
+    """Every lane split of 16-bit rows (embed_dims 8 .. 256)."""
+    run(W.make(f"split{D}", 1, [(9, 10), (5, 5)], 2, D, 2, 77, dtype, seed=50 + D, sample_dtype="f32"))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_generic_off_map(dtype):
+    """L = P = 3 (generic kernels), locations U[-0.2, 1.2]^2 (many samples
+    partly or fully off the map), ragged last workgroup."""
+    run(W.make("generic_offmap", 2, [(11, 13), (6, 7), (3, 4)], 4, 32, 3, 150, dtype, seed=51,
+               loc_args=(-0.2, 1.2), sample_dtype="f32"))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("ref_dims", [2, 4])
+def test_fused_masked(dtype, ref_dims):
+    wl = W.make_fused("fused_mixed", 2, [(16, 20), (8, 10), (4, 5), (2, 3)], 8, 32, 4, 203, dtype, seed=52,
+                      ref_dims=ref_dims, valid=[(1.0, 1.0), (0.7, 0.55)], sample_dtype="f32")
+    print(f"[gpu] mixed fused {tag(wl)} ref{ref_dims}", flush=True)
+    t = fused_to_device(wl)
+    check_forward_fused(wl, gpu_forward_fused(wl, t))
+    gv, goff, glog = gpu_backward_fused(wl, t)
+    assert goff.dtype == torch.float32 and glog.dtype == torch.float32 and gv.dtype == wl.value.dtype
+    check_backward_fused(wl, (gv, goff, glog))
+
+
+def test_backward_accumulate_mixed():
+    """msda_backward_accumulate with bf16 values and float32 per-sample
+    tensors adds into the float32 buffer."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    wl = W.make("accumulate_mixed", 2, [(20, 30), (10, 15)], 4, 32, 4, 90, "bf16", seed=53, sample_dtype="f32")
+    t = to_device(wl)
+    prob, keep = ops.problem_for(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"])
+    need = _lib.workspace_bytes(prob)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    acc = torch.full(t["value"].shape, 0.25, dtype=torch.float32, device="cuda")
+    gl = torch.empty_like(t["loc"])
+    gw = torch.empty_like(t["w"])
+    _lib.backward_accumulate(prob, t["value"].data_ptr(), t["loc"].data_ptr(), t["w"].data_ptr(),
+                             t["g"].data_ptr(), acc.data_ptr(), gl.data_ptr(), gw.data_ptr(), ws.data_ptr(), need,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rgv, rgl, rgw = oracle_backward(wl)
+    assert_close("accumulate_mixed/grad_value", f64(acc), 0.25 + rgv, *TOL[("f32", "bwd")])
+    assert_close("accumulate_mixed/grad_w", f64(gw), rgw, *TOL[("f32", "bwd")])
+    assert_close("accumulate_mixed/grad_loc", f64(gl), rgl, *TOL[("f32", "bwd")])
+
+
+def test_autograd_mixed():
+    from scale_deformable_attention_03_amd import ms_deform_attn
+    wl = W.make("autograd_mixed", 2, [(11, 13), (6, 7)], 4, 32, 3, 40, "bf16", seed=54, sample_dtype="f32")
+    t = to_device(wl)
+    v = t["value"].clone().requires_grad_()
+    loc = t["loc"].clone().requires_grad_()
+    w = t["w"].clone().requires_grad_()
+    out = ms_deform_attn(v, wl.spatial_shapes, wl.level_start_index, loc, w)
+    out.backward(t["g"])
+    torch.cuda.synchronize()
+    check_forward(wl, out.detach())
+    check_backward(wl, (v.grad, loc.grad, w.grad))
+
+
+def test_rejects_other_mixes():
+    """Only 16-bit values with float32 per-sample tensors mix."""
+    from scale_deformable_attention_03_amd import ops
+    wl = W.make("reject", 1, [(5, 6)], 2, 16, 2, 10, "f32", seed=55)
+    t = to_device(wl)
+    with pytest.raises(TypeError):
+        ops.forward(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"].half(), t["w"].half())
+    with pytest.raises(TypeError):
+        ops.forward(t["value"].half(), wl.spatial_shapes, wl.level_start_index, t["loc"].bfloat16(),
+                    t["w"].bfloat16())
