@@ -122,11 +122,11 @@ def load_traffic(digest: str, kernel: str, workload: str):
 # from /tmp with TMPDIR=/tmp).
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline",
+             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- "
