@@ -241,3 +241,70 @@ def backward_fused(value, spatial_shapes, level_start_index, reference_points, s
     wf, gf = w.reshape(bs, Q, M, L * P), gw.reshape(bs, Q, M, L * P)
     glog = wf * (gf - (wf * gf).sum(axis=-1, keepdims=True))
     return gv, goff, glog.reshape(bs, Q, M, L, P)
+
+
+# ---- the module step around the fused core --------------------------------------
+# MSDeformAttn in the walkthrough (section 2.2.4): value_proj, sampling_offsets
+# and attention_weights Linears before the core, output_proj after it.  The
+# Linears are written out with numpy matmul in float64 (y = x W^T + b, the
+# nn.Linear definition); the module's intermediate tensors value, offsets,
+# logits and the core's input gradient are float32 tensors there, so they are
+# rounded to float32 once before the core's oracle sees them.
+
+
+def _linear64(x, w, b):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T + np.asarray(b, dtype=np.float64)
+
+
+def module_forward(params, query, reference_points, input_flatten, spatial_shapes, level_start_index,
+                   n_heads: int, n_levels: int, n_points: int, key_padding_mask=None, nthreads: int = 0):
+    """Oracle of the module's forward; returns (output float64 [N, Q, C],
+    cache for module_backward).  params: name -> array as nn.Linear stores
+    them (weight [out, in], bias [out])."""
+    q, x = _f32(query), _f32(input_flatten)
+    N, Q, C = q.shape
+    K = x.shape[1]
+    M, L, P = n_heads, n_levels, n_points
+    value = _linear64(x, params["value_proj.weight"], params["value_proj.bias"]).astype(np.float32)
+    off = _linear64(q, params["sampling_offsets.weight"], params["sampling_offsets.bias"]).astype(np.float32)
+    logits = _linear64(q, params["attention_weights.weight"], params["attention_weights.bias"]).astype(np.float32)
+    value = value.reshape(N, K, M, C // M)
+    off = off.reshape(N, Q, M, L, P, 2)
+    logits = logits.reshape(N, Q, M, L, P)
+    core = forward_fused(value, spatial_shapes, level_start_index, reference_points, off, logits,
+                         key_padding_mask, nthreads)
+    out = _linear64(core, params["output_proj.weight"], params["output_proj.bias"])
+    cache = dict(value=value, off=off, logits=logits, core=core, q=q, x=x)
+    return out, cache
+
+
+def module_backward(params, query, reference_points, input_flatten, spatial_shapes, level_start_index,
+                    grad_output, n_heads: int, n_levels: int, n_points: int, key_padding_mask=None,
+                    nthreads: int = 0) -> dict:
+    """Oracle of the module's backward: gradients (float64) of sum(G * output)
+    for every parameter ("<name>.weight" / "<name>.bias"), "query" and
+    "input_flatten" (not the reference points, whose gradient the
+    walkthrough stops, nor the mask).  Linear y = x W^T + b: dx = dy W,
+    dW = dy^T x, db = sum of dy over rows."""
+    _, cache = module_forward(params, query, reference_points, input_flatten, spatial_shapes,
+                              level_start_index, n_heads, n_levels, n_points, key_padding_mask, nthreads)
+    g = np.asarray(_f32(grad_output), dtype=np.float64)
+    N, Q, C = g.shape
+    K = cache["x"].shape[1]
+    grads = {}
+
+    def lin_back(dy, x, name):
+        dy2, x2 = dy.reshape(-1, dy.shape[-1]), np.asarray(x, dtype=np.float64).reshape(-1, x.shape[-1])
+        grads[name + ".weight"] = dy2.T @ x2
+        grads[name + ".bias"] = dy2.sum(axis=0)
+        return dy2 @ np.asarray(params[name + ".weight"], dtype=np.float64)
+
+    d_core = lin_back(g, cache["core"], "output_proj").reshape(N, Q, C)
+    gv, goff, glog = backward_fused(cache["value"], spatial_shapes, level_start_index, reference_points,
+                                    cache["off"], cache["logits"], d_core.astype(np.float32), key_padding_mask,
+                                    nthreads)
+    dq = lin_back(goff.reshape(N, Q, -1), cache["q"], "sampling_offsets")
+    dq = dq + lin_back(glog.reshape(N, Q, -1), cache["q"], "attention_weights")
+    grads["query"] = dq.reshape(N, Q, C)
+    grads["input_flatten"] = lin_back(gv.reshape(N, K, C), cache["x"], "value_proj").reshape(N, K, C)
+    return grads

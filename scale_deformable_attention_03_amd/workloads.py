@@ -366,3 +366,93 @@ def detr_decoder_fused(dtype: str = "f32", ref_dims: int = 4, seed: int = 1013) 
     """The DETR decoder shapes in the fused form (bs 2, 300 queries), with
     4-d box reference points (two-stage / box refinement) by default."""
     return make_fused("detr_decoder_fused", 2, DETR_LEVELS, 8, 32, 4, 300, dtype, seed, ref_dims, "uniform")
+
+
+# --- inputs of the whole module step ------------------------------------------
+
+@dataclass
+class ModuleWorkload:
+    """Inputs and parameters of one MSDeformAttn module step (host, float32)."""
+
+    name: str
+    spatial_shapes: np.ndarray
+    level_start_index: np.ndarray
+    d_model: int
+    n_heads: int
+    n_levels: int
+    n_points: int
+    params: dict                     # name -> float32 array, nn.Linear layouts
+    query: torch.Tensor              # [bs, Q, C]
+    input_flatten: torch.Tensor      # [bs, K, C]
+    reference_points: torch.Tensor   # [bs, Q, L, 2 or 4]
+    grad_output: torch.Tensor        # [bs, Q, C]
+    key_padding_mask: torch.Tensor | None = None
+    meta: dict = field(default_factory=dict)
+
+
+def make_module(name: str, bs: int, shapes, d_model: int, n_heads: int, n_points: int, queries: int,
+                seed: int, ref_dims: int = 2, ref_dist: str = "uniform", valid=None,
+                dyadic: bool = False) -> ModuleWorkload:
+    """Seeded module inputs.  Parameters: ``module.module_parameters``, or with
+    ``dyadic`` every weight a multiple of 1/64 in [-1/4, 1/4] and the offset
+    bias rounded to 1/64, with query and input_flatten multiples of 1/8 in
+    [-2, 2]: then value, offsets and logits (sums of 256 products) are exact
+    in float32 whatever the summation order, so every consumer forms the same
+    sampling locations.  Otherwise query and input_flatten are N(0, 1).
+    Reference points and padding as in make_fused (queries = keys for
+    ref_dist "encoder").  grad_output N(0, 1).
+    Draw order: parameters (own seed), query, input_flatten, reference points,
+    box sizes, grad_output."""
+    from .module import module_parameters
+    shapes = np.asarray(shapes, dtype=np.int64).reshape(-1, 2)
+    L = shapes.shape[0]
+    K = int((shapes[:, 0] * shapes[:, 1]).sum())
+    C, Q = d_model, queries
+    rng = np.random.default_rng(seed)
+    if dyadic:
+        M, P = n_heads, n_points
+        params = {
+            "value_proj.weight": rng.integers(-16, 17, size=(C, C)) / 64, "value_proj.bias": np.zeros(C),
+            "sampling_offsets.weight": rng.integers(-16, 17, size=(M * L * P * 2, C)) / 64,
+            "sampling_offsets.bias": np.round(offset_directions(M, L, P).reshape(-1) * 64) / 64,
+            "attention_weights.weight": rng.integers(-16, 17, size=(M * L * P, C)) / 64,
+            "attention_weights.bias": np.zeros(M * L * P),
+            "output_proj.weight": rng.integers(-16, 17, size=(C, C)) / 64, "output_proj.bias": np.zeros(C),
+        }
+        query = rng.integers(-16, 17, size=(bs, Q, C)) / 8
+        inp = rng.integers(-16, 17, size=(bs, K, C)) / 8
+    else:
+        params = module_parameters(C, L, n_heads, n_points, seed + 1)
+        query = rng.standard_normal((bs, Q, C))
+        inp = rng.standard_normal((bs, K, C))
+    params = {k: np.asarray(v, dtype=np.float32) for k, v in params.items()}
+    if valid is not None:
+        mask, ratios = padding_masks(shapes, valid)
+    else:
+        mask, ratios = None, np.ones((bs, L, 2))
+    if ref_dist == "encoder":
+        if Q != K:
+            raise ValueError("encoder reference points need queries == keys")
+        lvl_of_key = np.repeat(np.arange(L), shapes[:, 0] * shapes[:, 1])
+        xy = pixel_centre_refs(shapes)[None] / ratios[:, lvl_of_key, :]
+    else:
+        xy = rng.random((bs, Q, 2))
+    ref = xy[:, :, None, :] * ratios[:, None, :, :]
+    if ref_dims == 4:
+        wh = rng.uniform(0.05, 0.5, size=(bs, Q, 2))
+        ref = np.concatenate([ref, wh[:, :, None, :] * ratios[:, None, :, :]], -1)
+    g = rng.standard_normal((bs, Q, C))
+    return ModuleWorkload(name=name, spatial_shapes=shapes, level_start_index=level_starts(shapes), d_model=C,
+                          n_heads=n_heads, n_levels=L, n_points=n_points, params=params,
+                          query=_cast(query, "f32"), input_flatten=_cast(inp, "f32"),
+                          reference_points=_cast(ref, "f32"), grad_output=_cast(g, "f32"),
+                          key_padding_mask=None if mask is None else torch.from_numpy(mask),
+                          meta=dict(seed=seed, dyadic=dyadic))
+
+
+def detr_encoder_module(bs: int = 2, seed: int = 1022) -> ModuleWorkload:
+    """One encoder layer's MSDeformAttn step at the DETR encoder shapes:
+    d_model 256 (8 heads x 32), 4 levels, 4 points, K = Q = 17821,
+    pixel-centre reference points."""
+    K = sum(h * w for h, w in DETR_LEVELS)
+    return make_module("detr_encoder_module", bs, DETR_LEVELS, 256, 8, 4, K, seed, 2, "encoder")
