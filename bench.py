@@ -20,7 +20,9 @@ timed on the host cores as a reported baseline.  A second object,
 offsets and logits in; msda_forward_fused + msda_backward_fused) beside the
 module path it replaces (PyTorch ops for the locations and the softmax and
 their backward around the core).  A third, "mixed_precision", times the
-encoder step with bf16 value-side tensors and float32 per-sample tensors.
+encoder step with bf16 value-side tensors and float32 per-sample tensors; a
+fourth, "module_step", the whole MSDeformAttn module (Linears through
+PyTorch's hipBLASLt GEMMs around the fused core) forward and backward.
 """
 from __future__ import annotations
 
@@ -122,11 +124,11 @@ def load_traffic(digest: str, kernel: str, workload: str):
 # from /tmp with TMPDIR=/tmp).
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed",
+             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed --no-module",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- "
@@ -366,6 +368,51 @@ def mixed_precision_leg(dev, steps: int, warmup: int, nsets: int) -> dict:
             "ms_per_step": round(ms, 5), "queries_per_s": round(bs * Q / (ms * 1e-3), 1)}
 
 
+def module_step_leg(dev, steps: int, warmup: int) -> dict:
+    """One MSDeformAttn module step (value_proj, sampling_offsets,
+    attention_weights Linears through PyTorch's hipBLASLt GEMMs, the fused
+    core through the C ABI, output_proj; forward and backward with autograd)
+    at the DETR encoder shapes, float32, random weights."""
+    import torch
+    from scale_deformable_attention_03_amd import workloads as W
+    from scale_deformable_attention_03_amd.module import MSDeformAttnModule
+
+    wl = W.detr_encoder_module()
+    m = MSDeformAttnModule(wl.d_model, wl.n_levels, wl.n_heads, wl.n_points, device=dev, params=wl.params)
+    q = wl.query.to(dev).requires_grad_()
+    x = wl.input_flatten.to(dev).requires_grad_()
+    ref = wl.reference_points.to(dev)
+    g = wl.grad_output.to(dev)
+    shapes, starts = wl.spatial_shapes, wl.level_start_index
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        for p in m.parameters():
+            p.grad = None
+        q.grad = x.grad = None
+        m(q, ref, x, shapes, starts).backward(g)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    bs, Q = wl.query.shape[:2]
+    K = wl.input_flatten.shape[1]
+    C, M, L, P = wl.d_model, wl.n_heads, wl.n_levels, wl.n_points
+    rows_q, rows_k = bs * Q, bs * K
+    # fwd: 4 GEMMs; bwd: 2 per Linear (input and weight gradients), 2 * rows * in * out flops each
+    linear_flops = 2 * (rows_k * C * C + rows_q * C * (M * L * P * 2) + rows_q * C * (M * L * P) + rows_q * C * C)
+    log(f"[bench] module step (Linears + fused core, fwd+bwd): {ms * 1e3:.1f} us/step")
+    return {"workload": wl.name, "dtype": "f32", "ms_per_step": round(ms, 5),
+            "queries_per_s": round(rows_q / (ms * 1e-3), 1), "linear_gflop_per_step": round(3 * linear_flops / 1e9, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,6 +425,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision leg")
+    ap.add_argument("--no-module", action="store_true", help="skip the module-step leg")
     ap.add_argument("--ingest-profiles", metavar="DIR",
                     help="summarise the rocprofv3 output of the profiling commands under DIR into profiles/ "
                          "(no GPU needed) and exit")
@@ -557,6 +605,8 @@ def main() -> int:
     if not args.no_mixed and args.workload == "detr_encoder":
         result["mixed_precision"] = mixed_precision_leg(dev, max(10, args.steps // 2), max(2, args.warmup // 2),
                                                         nsets)
+    if not args.no_module and args.workload == "detr_encoder":
+        result["module_step"] = module_step_leg(dev, max(10, args.steps // 4), max(2, args.warmup // 2))
     if args.no_cpu_baseline:
         result["cpu_baseline"] = None
     else:
