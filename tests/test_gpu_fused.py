@@ -150,3 +150,22 @@ def test_autograd_function():
     torch.cuda.synchronize()
     check_forward_fused(wl, out.detach())
     check_backward_fused(wl, (v.grad, off.grad, lg.grad))
+
+
+@pytest.mark.parametrize("ref_dims", [2, 4])
+def test_max_envelope_fused(ref_dims):
+    """The envelope's corner: L * P = 64 (4 levels x 16 points), 8 heads x 64
+    dims, fp16, large offsets (many samples off the map)."""
+    run(W.make_fused("max_fused", 1, [(40, 40), (20, 20), (10, 10), (5, 5)], 8, 64, 16, 120, "f16", seed=71,
+                     ref_dims=ref_dims, offset_sigma=6.0))
+
+
+def test_fallback_path_box_refs_mixed():
+    """The float-atomic fallback with 4-d reference points, bf16 values and
+    float32 per-sample tensors, and a padding mask."""
+    wl = W.make_fused("fallback_mixed", 1, [(1, 600000)], 1, 8, 2, 64, "bf16", seed=72, ref_dims=4,
+                      sample_dtype="f32")
+    m = np.zeros(wl.value.shape[:2], dtype=bool)
+    m[:, 1::4] = True
+    wl.key_padding_mask = torch.from_numpy(m)
+    run(wl)

@@ -115,3 +115,14 @@ def test_rejects_other_mixes():
     with pytest.raises(TypeError):
         ops.forward(t["value"].half(), wl.spatial_shapes, wl.level_start_index, t["loc"].bfloat16(),
                     t["w"].bfloat16())
+
+
+def test_max_constraint_mixed():
+    """L * P = 64, 8 heads x 64 dims, fp16 values with float32 locations and
+    weights, locations U[-0.1, 1.1]^2 (off-map samples)."""
+    run(W.make("max_mixed", 2, [(60, 60), (30, 30), (15, 15), (8, 8)], 8, 64, 16, 200, "f16", seed=56,
+               loc_args=(-0.1, 1.1), sample_dtype="f32"))
+
+
+def test_fallback_path_mixed():
+    run(W.make("fallback_mixed", 1, [(1, 600000)], 1, 8, 1, 64, "bf16", seed=57, sample_dtype="f32"))
