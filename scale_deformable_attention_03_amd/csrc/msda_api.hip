@@ -121,12 +121,12 @@ int floor_log2(int64_t v) {
 
 // Problem descriptor for the kernels, including the key segments of the
 // binned backward: level l gets segments of 2^shift keys, sized so that a
-// segment receives about 3/4 kUnitRecords records when the samples spread
+// segment receives about 3/4 of a unit's records when the samples spread
 // evenly over the level (two records per sample and level, Q*P samples per
 // level and plane), but never fewer than 32 keys: a denser level spreads a
 // segment over several units (merged with atomics) rather than letting
 // many workers of one unit fold into the same few rows.  A tile of
-// 2^shift keys * D floats stays within 32 KB.
+// 2^shift keys * D floats stays within 32 KB (16 KB for sparse problems).
 msda::Problem pack(const msda_problem_t* p) {
     msda::Problem pb;
     memset(&pb, 0, sizeof(pb));
@@ -140,7 +140,13 @@ msda::Problem pack(const msda_problem_t* p) {
     pb.lpr_active = lane_split(p->embed_dims, p->dtype).active;
     pb.ngroups = int64_t(p->batch) * p->num_queries * p->num_heads;
     pb.nplanes = p->batch * p->num_heads;
-    const int max_shift = floor_log2(std::min<int64_t>(msda::kMaxSegKeys, 8192 / p->embed_dims));
+    // Sparse problems (fewer than one record per key on average: two per
+    // sample, Q * L * P samples per plane) have many short units; they take
+    // smaller units and tiles (16 KB instead of 32 KB), so that more units
+    // run per CU.
+    const bool sparse = 2.0 * double(p->num_queries) * p->num_levels * p->num_points < double(p->num_keys);
+    pb.unit_records = sparse ? msda::kSparseUnitRecords : msda::kUnitRecords;
+    const int max_shift = floor_log2(std::min<int64_t>(msda::kMaxSegKeys, (sparse ? 4096 : 8192) / p->embed_dims));
     int64_t nseg = 0;
     for (int l = 0; l < p->num_levels; ++l) {
         const int64_t H = p->spatial_shapes[2 * l], W = p->spatial_shapes[2 * l + 1];
@@ -148,7 +154,7 @@ msda::Problem pack(const msda_problem_t* p) {
         pb.lv.W[l] = static_cast<int32_t>(W);
         pb.lv.start[l] = static_cast<int32_t>(p->level_start_index[l]);
         const double per_key = 2.0 * double(p->num_queries) * p->num_points / double(H * W);
-        const double keys = per_key > 0 ? (3 * msda::kUnitRecords / 4) / per_key : double(msda::kMaxSegKeys);
+        const double keys = per_key > 0 ? (3 * pb.unit_records / 4) / per_key : double(msda::kMaxSegKeys);
         int shift = keys >= 1.0 ? floor_log2(static_cast<int64_t>(keys)) : 0;
         if (shift < 5) shift = 5;
         if (shift > max_shift) shift = max_shift;
@@ -167,12 +173,12 @@ msda::Problem pack(const msda_problem_t* p) {
 int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
 
 // Per plane: at most 4 records per sample, so a fixed region of
-// plane_records; at most one unit per segment plus one per kUnitRecords.
+// plane_records; at most one unit per segment plus one per unit_records.
 int64_t plane_records(const msda_problem_t* p) {
     return 4 * int64_t(p->num_queries) * p->num_levels * p->num_points;
 }
 int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
-    return pb.nseg + (plane_records(p) + msda::kUnitRecords - 1) / msda::kUnitRecords;
+    return pb.nseg + (plane_records(p) + pb.unit_records - 1) / pb.unit_records;
 }
 
 bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {

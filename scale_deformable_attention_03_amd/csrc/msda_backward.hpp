@@ -29,7 +29,8 @@
 //                global add per non-empty bin).
 //   2. scan      exclusive prefix over the counts gives each segment a record
 //                range and a cursor; segments are split into units of at most
-//                kUnitRecords records.
+//                unit_records (kUnitRecords, or kSparseUnitRecords for sparse
+//                problems) records.
 //   3. gradient  the gather kernel (grad_w, grad_loc) also writes its records
 //                at positions reserved per workgroup and segment: the query
 //                and key (4 bytes) and the two corner weights (8 bytes).
@@ -62,6 +63,7 @@ constexpr int kQueryBits = 24;         // queries per plane for the binned path
 constexpr int kMaxSegKeys = 256;       // keys per segment (8-bit key field)
 constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the map
 constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
+constexpr int kSparseUnitRecords = 512; // the same for sparse problems (fewer than one record per key)
 constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 1024;    // samples one gradient workgroup holds
 constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path (16-bit cell fields)
@@ -273,8 +275,8 @@ msda_bin_count_kernel(const void* __restrict__ loc, const void* __restrict__ ref
 // 2. scan
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int units_of(int count) {
-    return count <= kUnitRecords ? 1 : (count + kUnitRecords - 1) / kUnitRecords;
+__device__ __forceinline__ int units_of(int count, int unit) {
+    return count <= unit ? 1 : (count + unit - 1) / unit;
 }
 
 // Zero the float32 rows of plane-global segment `gs`, lanes t, t+nt, ...
@@ -353,7 +355,7 @@ __device__ void scan_plane(const int32_t* s_cnt, int32_t* s_wrec, int32_t* s_wun
         const int i = t * kPer + j;
         if (i < n) {
             rsum += s_cnt[i];
-            usum += units_of(s_cnt[i]);
+            usum += units_of(s_cnt[i], pb.unit_records);
         }
     }
     int rinc = rsum, uinc = usum;                    // inclusive scan within the wave
@@ -381,13 +383,13 @@ __device__ void scan_plane(const int32_t* s_cnt, int32_t* s_wrec, int32_t* s_wun
     for (int j = 0; j < kPer; ++j) {
         const int i = t * kPer + j;
         if (i >= n) break;
-        const int c = s_cnt[i], u = units_of(c);
+        const int c = s_cnt[i], u = units_of(c, pb.unit_records);
         const int gi = static_cast<int>(cbase) + i;
         cursor[gi] = rbase;
         const int atomic_flush = (u > 1 || accumulate) ? 1 : 0;
         for (int k = 0; k < u; ++k)
-            units[ufirst + ubase + k] = make_int4(gi, rbase + k * kUnitRecords,
-                                                  rbase + min(c, (k + 1) * kUnitRecords), atomic_flush);
+            units[ufirst + ubase + k] = make_int4(gi, rbase + k * pb.unit_records,
+                                                  rbase + min(c, (k + 1) * pb.unit_records), atomic_flush);
         if (u > 1 && !accumulate) multi[cbase + atomicAdd(s_nmulti, 1)] = gi;
         rbase += c;
         ubase += u;
@@ -725,28 +727,33 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 // ---------------------------------------------------------------------------
 // 4. accumulate
 // ---------------------------------------------------------------------------
-// Grid: nplanes * plane_units (the bound), acc_block(LPR) lanes; workgroups past
-// the total unit count exit, and the others take the units of all planes in
-// plane order (nunits[2 nplanes + p]: units before plane p, written by the
-// gradient kernel; nunits[3 nplanes]: all units), remapped so that each XCD
-// gets a contiguous run.  LDS: the segment tile (keys * D floats), the unit's records
-// sorted by key (kUnitRecords weight pairs and keys, padded), 2 * kMaxSegKeys
-// int32.
-// 64 workers of LPR lanes (at most 1024 lanes): the number of slice
-// boundaries per unit, and so the LDS compare-and-swap work, stays the same
-// for every row width.
-constexpr int acc_block(int lpr) { return 64 * lpr < 1024 ? 64 * lpr : 1024; }
+// Grid: nplanes * plane_units (the bound), acc_block(LPR, UNIT) lanes;
+// workgroups past the total unit count exit, and the others take the units
+// of all planes in plane order (nunits[2 nplanes + p]: units before plane p,
+// written by the gradient kernel; nunits[3 nplanes]: all units), remapped so
+// that each XCD gets a contiguous run.  LDS: the segment tile (keys * D
+// floats), the unit's records sorted by key (UNIT weight pairs and keys,
+// padded), 2 * kMaxSegKeys int32.
+// UNIT / 32 workers of LPR lanes (at most 1024 lanes, at most one lane per
+// record slot): the number of slice boundaries per record, and so the LDS
+// compare-and-swap work, stays the same for every row width.  UNIT is
+// kUnitRecords, or kSparseUnitRecords for sparse problems, whose units are
+// many and short: smaller units and tiles let more of them run per CU.
+constexpr int acc_block(int lpr, int unit) {
+    return (unit / 32) * lpr < 1024 ? ((unit / 32) * lpr < unit ? (unit / 32) * lpr : unit)
+                                    : (1024 < unit ? 1024 : unit);
+}
 // Sorted record i: key at word i + 4 * (i / 32), weight pair at pair slot
 // i + 2 * (i / 32).  Workers start 8-aligned batches about 32 records apart
 // and read them with 16-byte vector reads; the padding keeps those reads
 // aligned and puts the eight workers of a wave in different LDS banks.
-constexpr int kSortedKeySlots = kUnitRecords + kUnitRecords / 8 + 8;
-constexpr int kSortedPairSlots = kUnitRecords + kUnitRecords / 16 + 8;
+constexpr int sorted_key_slots(int unit) { return unit + unit / 8 + 8; }
+constexpr int sorted_pair_slots(int unit) { return unit + unit / 16 + 8; }
 __device__ __forceinline__ int key_slot(int i) { return i + 4 * (i >> 5); }
 __device__ __forceinline__ int pair_slot(int i) { return i + 2 * (i >> 5); }
 
-template <int DTK, int VECB, int LPR>
-__global__ void __launch_bounds__(acc_block(LPR), value_dt(DTK) == kF32 ? 6 : 5)
+template <int DTK, int VECB, int LPR, int UNIT>
+__global__ void __launch_bounds__(acc_block(LPR, UNIT), value_dt(DTK) == kF32 ? 6 : 5)
 msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ recs,
                        const int32_t* __restrict__ nunits, const int4* __restrict__ units,
                        const uint8_t* __restrict__ kmask, float* __restrict__ gacc, void* __restrict__ gfinal,
@@ -754,8 +761,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     constexpr int DT = value_dt(DTK);                 // the accumulation touches no per-sample tensor
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
-    constexpr int kAccBlock = acc_block(LPR);
-    constexpr int kAccPerLane = kUnitRecords / kAccBlock;
+    constexpr int kAccBlock = acc_block(LPR, UNIT);
+    constexpr int kAccPerLane = UNIT / kAccBlock;
+    static_assert(kAccPerLane * kAccBlock == UNIT, "the unit's records split evenly over the lanes");
     constexpr int NW = kAccBlock / LPR;              // workers
     // consecutive units (neighbouring segments of one plane) run on one XCD,
     // so the plane's grad_output rows they gather stay in that XCD's L2
@@ -786,8 +794,8 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     extern __shared__ float smem[];
     float* tile = smem;                                                  // nk * D
     float2* sw = reinterpret_cast<float2*>(smem + (1 << shift) * D);     // sorted weights
-    uint32_t* skey = reinterpret_cast<uint32_t*>(sw + kSortedPairSlots); // sorted keys
-    int32_t* hist = reinterpret_cast<int32_t*>(skey + kSortedKeySlots);
+    uint32_t* skey = reinterpret_cast<uint32_t*>(sw + sorted_pair_slots(UNIT)); // sorted keys
+    int32_t* hist = reinterpret_cast<int32_t*>(skey + sorted_key_slots(UNIT));
     int32_t* cur = hist + kMaxSegKeys;
 
     for (int i = threadIdx.x; i < nk * D; i += kAccBlock) tile[i] = 0.0f;

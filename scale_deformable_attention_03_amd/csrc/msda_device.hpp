@@ -50,6 +50,7 @@ struct Problem {
     // seg_base[l] within a (batch, head) plane; seg_base[L] = nseg.
     int32_t nseg;
     int32_t nplanes;         // bs * M
+    int32_t unit_records;    // records per accumulation unit (kUnitRecords or kSparseUnitRecords)
     int32_t seg_shift[kMaxLevels];
     int32_t seg_base[kMaxLevels + 1];
 };

@@ -107,16 +107,26 @@ struct Grad {
 
 template <int DT, int VECB, int LPR>
 struct Accum {
-    static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
-                             const uint3* recs, const int32_t* nunits, const int4* units, const uint8_t* kmask,
-                             float* gacc, void* gfinal, hipStream_t st) {
+    template <int UNIT>
+    static msda_status_t go(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
+                            const uint3* recs, const int32_t* nunits, const int4* units, const uint8_t* kmask,
+                            float* gacc, void* gfinal, hipStream_t st) {
         int max_shift = 0;
         for (int l = 0; l < pb.L; ++l) max_shift = pb.seg_shift[l] > max_shift ? pb.seg_shift[l] : max_shift;
         const size_t lds = sizeof(float) * (size_t(1) << max_shift) * pb.D +
-                           sizeof(float2) * msda::kSortedPairSlots + sizeof(uint32_t) * msda::kSortedKeySlots +
-                           2 * sizeof(int32_t) * msda::kMaxSegKeys;
-        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR>), max_units, msda::acc_block(LPR), lds, st,
-                      gout, recs, nunits, units, kmask, gacc, gfinal, pb, plane_units);
+                           sizeof(float2) * msda::sorted_pair_slots(UNIT) +
+                           sizeof(uint32_t) * msda::sorted_key_slots(UNIT) + 2 * sizeof(int32_t) * msda::kMaxSegKeys;
+        return launch(kfn(&msda::msda_accumulate_kernel<DT, VECB, LPR, UNIT>), max_units, msda::acc_block(LPR, UNIT),
+                      lds, st, gout, recs, nunits, units, kmask, gacc, gfinal, pb, plane_units);
+    }
+    static msda_status_t run(const msda::Problem& pb, int64_t max_units, int plane_units, const void* gout,
+                             const uint3* recs, const int32_t* nunits, const int4* units, const uint8_t* kmask,
+                             float* gacc, void* gfinal, hipStream_t st) {
+        return pb.unit_records == msda::kSparseUnitRecords
+                   ? go<msda::kSparseUnitRecords>(pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
+                                                  gfinal, st)
+                   : go<msda::kUnitRecords>(pb, max_units, plane_units, gout, recs, nunits, units, kmask, gacc,
+                                            gfinal, st);
     }
 };
 
