@@ -145,11 +145,12 @@ msda_status_t msda_forward(const msda_problem_t *problem,
 /*
  * msda_backward_workspace_bytes: device workspace msda_backward and
  * msda_backward_accumulate need for this problem.  It holds the binned
- * transpose of the sampling pattern (per-segment counts and cursors, the
- * unit list and up to four 4-byte records per sample) and, for fp16 and
- * bf16, a float32 grad_value accumulator (batch*num_keys*num_heads*
- * embed_dims*4 bytes).  Returns 0 for an empty problem and for an invalid
- * descriptor; the backward then reports the error.
+ * transpose of the sampling pattern (per-segment histogram rows and
+ * cursors, the unit list and up to four 12-byte records per sample) and,
+ * when grad_value is 16-bit, a float32 grad_value accumulator
+ * (batch*num_keys*num_heads*embed_dims*4 bytes).  Returns 0 for an empty
+ * problem and for an invalid descriptor; the backward then reports the
+ * error.
  */
 size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
 
@@ -175,11 +176,12 @@ size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
  *   Enqueues on `stream`: a record count and a scan (one kernel when each
  *   (batch, head) has at most 8192 samples), the gradient kernel (a
  *   gather like the forward, which also writes the records), the
- *   accumulation kernel (one workgroup per key segment writes grad_value
- *   rows once) and, for fp16/bf16, a conversion kernel.  Problems whose
- *   sampling pattern does not fit the record format (more than 2^21 samples
- *   per (batch, head) or more than 2048 key segments) fall back to a zero
- *   fill and float atomics.
+ *   accumulation kernel (one workgroup per unit of a key segment; rows of
+ *   a segment that fits one unit are written once) and, for a 16-bit
+ *   grad_value, a kernel that rounds the rows of segments split over several
+ *   units.  Problems outside the record format (2^24 or more queries, a
+ *   level side above 65,534, more than 2048 key segments per (batch, head),
+ *   2^30 or more records) fall back to a zero fill and float atomics.
  */
 msda_status_t msda_backward(const msda_problem_t *problem,
                             const void *value,

@@ -567,7 +567,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         constexpr int kSB = kC % kSBMax == 0 ? kSBMax : 1;
 #pragma unroll 1
         for (int c0 = 0; c0 < LP; c0 += kC) {
-            float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f, own_a = 0.0f;
+            float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f;
+            int own_l = 0;                                   // level of the owned sample
 #pragma unroll
             for (int b0 = 0; b0 < kC; b0 += kSB) {
                 uint4 o[kSB];
@@ -630,7 +631,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                             // points, ref_wh * 0.5 / P for 4-d ones
                             own_x = off ? 0.0f : sx * fr.z;
                             own_y = off ? 0.0f : sy * fr.z;
-                            own_a = static_cast<float>(l);
+                            own_l = l;
                         }
                     }
                 }
@@ -643,11 +644,11 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     sv[lg * LP + c0 + li] = own_w;       // the softmax backward below
                     if constexpr (REF == 4) {
                         const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + lg) * L +
-                                           static_cast<int>(own_a);
+                                           own_l;
                         const float2 wh = load_pair<ST>(ref, 2 * ri + 1);
                         const float k = 0.5f / static_cast<float>(P);
-                        own_x = own_x * static_cast<float>(pb.lv.W[static_cast<int>(own_a)]) * (wh.x * k);
-                        own_y = own_y * static_cast<float>(pb.lv.H[static_cast<int>(own_a)]) * (wh.y * k);
+                        own_x = own_x * static_cast<float>(pb.lv.W[own_l]) * (wh.x * k);
+                        own_y = own_y * static_cast<float>(pb.lv.H[own_l]) * (wh.y * k);
                     }
                 }
                 store_pair<ST>(grad_loc, s, own_x, own_y);
