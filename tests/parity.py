@@ -36,9 +36,11 @@ def assert_close(name, gpu, ref, rtol, atol_rms=None, atol=None):
     err = np.abs(gpu - ref)
     bound = rtol * np.abs(ref) + atol
     bad = ~(err <= bound)            # NaN in gpu counts as bad
+    norm = float(np.linalg.norm((gpu - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+    # the normwise relative error, reported beside the elementwise bar (shown with pytest -s)
+    print(f"[parity] {name}: normwise rel err {norm:.3g}, max abs err {float(np.nanmax(err)):.3g}", flush=True)
     if bad.any():
         i = np.unravel_index(int(np.argmax(np.where(bad, err - bound, -np.inf))), ref.shape)
-        norm = float(np.linalg.norm((gpu - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
         raise AssertionError(
             f"{name}: {int(bad.sum())}/{ref.size} elements out of tolerance "
             f"(rtol {rtol:g}, atol {atol:.3g}); worst at {i}: gpu {gpu[i]!r} ref {ref[i]!r}; "
