@@ -120,6 +120,11 @@ EDGE = [
     ("L64_P1", 1, [(2 + i % 3, 3 + i % 4) for i in range(64)], 2, 8, 1, 19, "f32", "uniform", (-0.1, 1.1)),
     ("ragged_tail_L4P4", 1, [(17, 23), (9, 12), (5, 6), (3, 3)], 8, 32, 4, 33, "f32", "uniform", (-0.1, 1.1)),
     ("ragged_tail_bf16", 3, [(17, 23), (9, 12), (5, 6), (3, 3)], 7, 32, 4, 13, "bf16", "uniform", (-0.1, 1.1)),
+    # more than 64 (batch, head) planes: the accumulation's plane lookup reads
+    # a second chunk of unit prefixes; sparse (few records per key) and dense
+    ("planes72_sparse", 9, [(20, 27), (10, 14)], 8, 16, 2, 40, "f32", "uniform", (-0.1, 1.1)),
+    ("planes130_dense", 26, [(6, 7), (3, 4)], 5, 8, 4, 300, "f32", "uniform", (-0.1, 1.1)),
+    ("planes72_dense_bf16", 9, [(8, 9), (4, 5)], 8, 16, 4, 150, "bf16", "uniform", (-0.1, 1.1)),
 ]
 
 
