@@ -19,7 +19,8 @@ timed on the host cores as a reported baseline.  A second object,
 "fused_prologue", times the fused form on the same shapes (reference points,
 offsets and logits in; msda_forward_fused + msda_backward_fused) beside the
 module path it replaces (PyTorch ops for the locations and the softmax and
-their backward around the core).  A third, "mixed_precision", times the
+their backward around the core).  "graph_replay_ms_per_step" is the same step
+captured as HIP graphs and replayed (no host launch cost).  A third, "mixed_precision", times the
 encoder step with bf16 value-side tensors and float32 per-sample tensors; a
 fourth, "module_step", the whole MSDeformAttn module (Linears through
 PyTorch's hipBLASLt GEMMs around the fused core) forward and backward.
@@ -87,13 +88,14 @@ def touched_rows(wl) -> int:
 
 
 def algorithmic_bytes(wl, rows: int) -> dict:
-    e = wl.value.element_size()
+    e = wl.value.element_size()                      # value side
+    es = wl.sampling_locations.element_size()        # per-sample tensors (float32 in mixed precision)
     bs, K, M, D = wl.value.shape
     Q = wl.sampling_locations.shape[1]
     L, P = wl.sampling_locations.shape[3:5]
     value_rows = rows * D * e
-    loc = bs * Q * M * L * P * 2 * e
-    w = bs * Q * M * L * P * e
+    loc = bs * Q * M * L * P * 2 * es
+    w = bs * Q * M * L * P * es
     out = bs * Q * M * D * e
     full_value = bs * K * M * D * e
     fwd = value_rows + loc + w + out
@@ -420,7 +422,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="detr_encoder",
                     choices=["detr_encoder", "large_batch_encoder", "max_constraint", "detr_decoder",
-                             "tiny_single_level"])
+                             "tiny_single_level", "detr_encoder_bf16_f32"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
@@ -524,6 +526,38 @@ def main() -> int:
     log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
         f"bwd {bwd_ms * 1e3:.1f} us")
 
+    # The same steps captured as HIP graphs (one per buffer set) and replayed:
+    # the launches cost no host time, which matters for the small problems.
+    graphs = []
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for s_ in sets:
+            fwd(s_)
+            bwd(s_)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for s_ in sets:
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            gsp = torch.cuda.current_stream(dev).cuda_stream
+            p_ = s_["ptr"]
+            _lib.forward(prob, p_["value"], p_["loc"], p_["w"], p_["out"], gsp)
+            _lib.backward(prob, p_["value"], p_["loc"], p_["w"], p_["g"], p_["gv"], p_["gl"], p_["gw"],
+                          p_["ws"] if need_ws else 0, need_ws, gsp)
+        graphs.append(g_)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % nsets].replay()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record(stream)
+    for i in range(args.steps):
+        graphs[i % nsets].replay()
+    gb.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gb) / args.steps
+    log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
+
     # Per-stage times of msda_backward (HIP events recorded by the library
     # between its kernels, msda_backward_profile), live, same rotation.
     hip = ctypes.CDLL("libamdhip64.so.7")     # PyTorch's runtime, already loaded
@@ -581,7 +615,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype + ("+" + wl.sample_dtype if wl.sample_dtype else ""),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": bs, "num_queries": Q, "num_keys": K,
                    "num_heads": M, "embed_dims": D, "num_levels": L, "num_points": P,
@@ -589,6 +623,7 @@ def main() -> int:
                    "buffer_sets": nsets, "parallelism": "single GPU"},
         "effective_gbps": round(eff_gbps, 1),
         "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "graph_replay_ms_per_step": round(graph_ms, 5),
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
         "bwd_stages_us": stages_us,

@@ -223,6 +223,8 @@ NAMED = {
     "detr_decoder": detr_decoder,
     "large_batch_encoder": large_batch_encoder,
     "max_constraint": max_constraint,
+    # mixed precision: bf16 value side, float32 locations and weights
+    "detr_encoder_bf16_f32": lambda: detr_encoder(dtype="bf16", sample_dtype="f32"),
 }
 
 
