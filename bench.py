@@ -126,16 +126,27 @@ def load_traffic(digest: str, kernel: str, workload: str):
 # from /tmp with TMPDIR=/tmp).
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed --no-module",
+             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
+    "cache": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TA_TA_BUSY_sum TD_TD_BUSY_sum TCP_TOTAL_CACHE_ACCESSES_sum "
+             "TCP_TCC_READ_REQ_sum GRBM_GUI_ACTIVE --output-format csv -d DIR/cache -o run -- "
+             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+    "micro_trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/micro_trace -o run -- "
+                   "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
+    "sq": "rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE "
+          "SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d DIR/sq -o run -- "
+          "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
 }
+# MI355X: 256 compute units in 8 XCDs, 4 SIMDs per CU (GRBM_GUI_ACTIVE is
+# summed over the XCDs; TA/TD/TCP counters over the CUs).
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
 COPY_BYTES = 512 << 20           # one --calibrate-copy dispatch reads and writes this much
 
 
@@ -158,6 +169,75 @@ def _counter_csv(d: str, counter: str) -> dict:
             if r["Counter_Name"] == counter:
                 out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return out
+
+
+def _counters_by_kernel(d: str) -> dict:
+    """{short kernel name: {counter: mean per dispatch}} of one --pmc run
+    (msda kernels only)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "msda" not in r["Kernel_Name"]:
+                continue
+            acc.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters_summary(d: str, workload: str, digest: str) -> list:
+    """Markdown lines: cache hit rates, texture-path, VALU and LDS activity
+    per msda kernel, from the "cache" and "sq" --pmc runs under d.  Busy
+    shares are relative to the kernel's own GPU cycles per XCD
+    (GRBM_GUI_ACTIVE / 8, taken in the same run)."""
+    cache = _counters_by_kernel(os.path.join(d, "cache"))
+    sq = _counters_by_kernel(os.path.join(d, "sq"))
+    if not cache or not sq:
+        return []
+
+    def pct(num, den):
+        """Share num / den as a percentage; a dash when a counter is missing."""
+        if num is None or den is None or den <= 0:
+            return "—"
+        return f"{100.0 * num / den:.0f}%"
+
+    md = [f"# Cache, texture-path, VALU and LDS counters per launch, msda kernels, workload {workload}", "",
+          f"Kernel sources digest {digest}. Means over the dispatches of two rocprofv3 --pmc runs;",
+          f"cycles = GRBM_GUI_ACTIVE / {N_XCD} (GPU cycles of the launch per XCD, same run).",
+          "- L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS); L1 hit = 1 - TCP_TCC_READ_REQ / TCP_TOTAL_CACHE_ACCESSES;",
+          f"- TA busy, TD busy = TA_TA_BUSY_sum, TD_TD_BUSY_sum / {N_CU} / cycles;",
+          f"- VALU issue = SQ_INSTS_VALU * 4 / {N_SIMD} / cycles (a wave64 VALU instruction holds its",
+          "  16-lane SIMD for 4 cycles);",
+          f"- LDS active = SQ_LDS_IDX_ACTIVE / {N_CU} / cycles; bank and address conflicts as shares of",
+          "  the LDS-active cycles (SQ_LDS_BANK_CONFLICT, SQ_LDS_ADDR_CONFLICT: same-address atomics);",
+          "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of wave lifetime spent waiting).", "",
+          "Commands (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
+          f"    {PROFILE_COMMANDS['cache']}", f"    {PROFILE_COMMANDS['sq']}", "",
+          "| kernel | waves | cycles | L2 hit | L1 hit | TA busy | TD busy | VALU issue | LDS active | "
+          "LDS bank conflict | LDS address conflict | waiting |",
+          "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(set(cache) & set(sq)):
+        c, q = cache[k], sq[k]
+        cyc_c = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        cyc_q = q.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        if cyc_c <= 0 or cyc_q <= 0:
+            continue
+        hit, miss = c.get("TCC_HIT_sum"), c.get("TCC_MISS_sum")
+        l1_acc, l1_miss = c.get("TCP_TOTAL_CACHE_ACCESSES_sum"), c.get("TCP_TCC_READ_REQ_sum")
+        l1_hits = None if l1_acc is None or l1_miss is None else l1_acc - l1_miss
+        valu = q.get("SQ_INSTS_VALU")
+        lds = q.get("SQ_LDS_IDX_ACTIVE")
+        waves = q.get("SQ_WAVES")
+        md.append(
+            f"| {k} | {'—' if waves is None else f'{waves:.0f}'} | {cyc_q:.0f} | "
+            f"{pct(hit, None if hit is None or miss is None else hit + miss)} | {pct(l1_hits, l1_acc)} | "
+            f"{pct(c.get('TA_TA_BUSY_sum'), N_CU * cyc_c)} | {pct(c.get('TD_TD_BUSY_sum'), N_CU * cyc_c)} | "
+            f"{pct(None if valu is None else valu * 4, N_SIMD * cyc_q)} | {pct(lds, N_CU * cyc_q)} | "
+            f"{pct(q.get('SQ_LDS_BANK_CONFLICT'), lds)} | {pct(q.get('SQ_LDS_ADDR_CONFLICT'), lds)} | "
+            f"{pct(q.get('SQ_WAIT_ANY'), q.get('SQ_WAVE_CYCLES'))} |")
+    return md
 
 
 def ingest_profiles(d: str, workload: str) -> None:
@@ -228,7 +308,104 @@ def ingest_profiles(d: str, workload: str) -> None:
                       f"{ns['MinNs'] / 1e3:.2f} | {ns['MaxNs'] / 1e3:.2f} | {ns['Percentage']:.1f}% |")
         with open(os.path.join(ROOT, "profiles", f"msda_kernels_{workload}_kernel_trace.md"), "w") as fh:
             fh.write("\n".join(md) + "\n")
+    stats = glob.glob(os.path.join(d, "micro_trace", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        md = [f"# Measurement kernels (gather only, atomic scatter), workload {workload}", "",
+              "rocprofv3 --stats of a short bench run with its ceilings leg: the gather and scatter kernels of",
+              "libmsda_micro.so on the workload's own corner rows (gather: loads only, then with FMAs;",
+              "scatter: lanes on adjacent addresses, then 16 bytes apart), beside the core's kernels.", "",
+              "Command (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
+              f"    {PROFILE_COMMANDS['micro_trace']}", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for r in csv.DictReader(open(stats[0])):
+            name = r.get("Name", "?")
+            if not any(t in name for t in ("gather_kernel", "scatter_kernel", "msda_forward_kernel",
+                                           "msda_backward_kernel", "msda_accumulate_kernel")):
+                continue
+            ns = {k: float(r.get(k) or "nan") for k in ("AverageNs", "MinNs", "MaxNs")}
+            md.append(f"| {name[:110]} | {r.get('Calls', '?')} | {ns['AverageNs'] / 1e3:.2f} | "
+                      f"{ns['MinNs'] / 1e3:.2f} | {ns['MaxNs'] / 1e3:.2f} |")
+        with open(os.path.join(ROOT, "profiles", f"micro_gather_scatter_{workload}_kernel_trace.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+    if os.path.isdir(os.path.join(d, "cache")) and os.path.isdir(os.path.join(d, "sq")):
+        md = counters_summary(d, workload, digest)
+        if md:
+            with open(os.path.join(ROOT, "profiles", f"msda_kernels_{workload}_counters.md"), "w") as fh:
+                fh.write("\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
+
+
+def ceilings_leg(wl, dev, fwd_us: float, step_gbps: float) -> dict:
+    """The secondary ceilings of the core's access patterns, measured on the
+    same workload with the kernels of libmsda_micro.so (include/msda_micro.h):
+
+    - gather only: the forward's corner-row loads (same groups, same rows,
+      16-byte lane loads, four samples in flight), loads only and with the
+      fp32 FMAs;
+    - atomic scatter: one float32 atomic add per element of every corner
+      row, lanes on adjacent addresses and lanes 16 bytes apart (a
+      per-sample backward scattering grad_value directly);
+    - a streaming device copy of 512 MiB (read + write bytes / time)."""
+    import torch
+    from scale_deformable_attention_03_amd import _micro
+
+    bs, K, M, D = wl.value.shape
+    Q, L, P = wl.sampling_locations.shape[1], wl.sampling_locations.shape[3], wl.sampling_locations.shape[4]
+    e = wl.value.element_size()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ngroups, samples = bs * M * Q, L * P
+
+    def timed(fn, reps, warm=1):
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    res = {}
+    loc = wl.sampling_locations.float().numpy()
+    lanes = D * e // 16
+    if lanes in (2, 4, 8, 16):
+        tab = torch.from_numpy(_micro.corner_table(loc, wl.spatial_shapes, wl.level_start_index, K,
+                                                   lanes).view(np.int32)).to(dev)
+        rows = wl.value.to(dev)
+        out = torch.empty(ngroups * lanes * 4, dtype=torch.float32, device=dev)
+        row_bytes = ngroups * samples * 4 * lanes * 16
+        g_only = timed(lambda: _micro.gather(rows.data_ptr(), tab.data_ptr(), out.data_ptr(), ngroups, samples,
+                                             lanes, False, sp), 5, 2)
+        res.update({"corner_row_bytes": row_bytes, "gather_only_us": round(g_only, 2),
+                    "gather_request_tbps": round(row_bytes / (g_only * 1e-6) / 1e12, 2),
+                    "fwd_over_gather_only": round(fwd_us / g_only, 3)})
+        if e == 4:
+            g_fma = timed(lambda: _micro.gather(rows.data_ptr(), tab.data_ptr(), out.data_ptr(), ngroups, samples,
+                                                lanes, True, sp), 5, 2)
+            res["gather_fma_us"] = round(g_fma, 2)
+        del rows, out, tab
+    lanes32 = D // 4                             # float32 rows (grad_value or its workspace)
+    if lanes32 in (2, 4, 8, 16):
+        tab = torch.from_numpy(_micro.corner_table(loc, wl.spatial_shapes, wl.level_start_index, K,
+                                                   lanes32).view(np.int32)).to(dev)
+        dst = torch.zeros(bs * K * M * D, dtype=torch.float32, device=dev)
+        n_atomic = ngroups * samples * 4 * D
+        sc = {}
+        for name, contig in (("lane_contiguous", True), ("lane_stride_16B", False)):
+            sc[name] = timed(lambda: _micro.scatter(dst.data_ptr(), tab.data_ptr(), ngroups, samples, lanes32,
+                                                    contig, sp), 3, 1)
+        res["scatter_atomic_us"] = {k: round(v, 1) for k, v in sc.items()}
+        res["scatter_atomics"] = n_atomic
+        res["atomic_g_per_s"] = {k: round(n_atomic / (v * 1e-6) / 1e9, 1) for k, v in sc.items()}
+        del dst, tab
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    c_us = timed(lambda: dst.copy_(src), 5, 2)
+    res["copy_gbps"] = round(2 * src.numel() * 4 / (c_us * 1e-6) / 1e9, 1)
+    res["step_pct_of_copy_ceiling"] = round(100 * step_gbps / res["copy_gbps"], 2)
+    return res
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -428,6 +605,8 @@ def main() -> int:
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision leg")
     ap.add_argument("--no-module", action="store_true", help="skip the module-step leg")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the gather / atomic-scatter / copy ceiling measurements")
     ap.add_argument("--ingest-profiles", metavar="DIR",
                     help="summarise the rocprofv3 output of the profiling commands under DIR into profiles/ "
                          "(no GPU needed) and exit")
@@ -522,7 +701,18 @@ def main() -> int:
     wall = time.perf_counter() - t0
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    step_us = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e3
     ms_per_step = wall * 1e3 / args.steps
+
+    # warm: the same steps back to back on one buffer set (its working set
+    # may stay in the Infinity Cache between steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd(sets[0])
+        bwd(sets[0])
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
         f"bwd {bwd_ms * 1e3:.1f} us")
 
@@ -624,16 +814,24 @@ def main() -> int:
         "effective_gbps": round(eff_gbps, 1),
         "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "graph_replay_ms_per_step": round(graph_ms, 5),
+        "warm_ms_per_step": round(warm_ms, 5),
+        "step_us_percentiles": {"p10": round(float(np.percentile(step_us, 10)), 2),
+                                "p50": round(float(np.percentile(step_us, 50)), 2),
+                                "p90": round(float(np.percentile(step_us, 90)), 2)},
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
         "bwd_stages_us": stages_us,
         "algorithmic_bytes": ab,
         "touched_value_rows": rows,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count},
+                   "cus": props.multi_processor_count, "l2_bytes": getattr(props, "L2_cache_size", None),
+                   "memory_bytes": props.total_memory, "hip": torch.version.hip},
         "kernel_digest": digest,
         "roofline": roofline,
     }
+    if not args.no_ceilings:
+        result["ceilings"] = ceilings_leg(wl, dev, fwd_ms * 1e3, eff_gbps)
+        log(f"[bench] ceilings: {result['ceilings']}")
     if not args.no_fused:
         result["fused_prologue"] = fused_prologue_leg(wl, dev, max(10, args.steps // 2), max(2, args.warmup // 2),
                                                       nsets)
