@@ -217,6 +217,40 @@ def max_constraint(dtype: str = "f16") -> Workload:
                 loc_dist="uniform", loc_args=(-0.1, 1.1))
 
 
+# Levels whose value bytes per batch (8 heads x 32 dims: 1 KiB per key in
+# float32, 512 B in fp16 / bf16) fall within 4 MiB below 2^31, the envelope's
+# per-batch byte limit.
+OFFSET_LIMIT_LEVELS = {4: [(1448, 1446), (4, 5)], 2: [(2048, 2046), (4, 5)]}
+
+
+def offset_limit(dtype: str = "f32", seed: int = 1031, queries: int = 48) -> Workload:
+    """bs 2 at the per-batch byte limit of the envelope: two levels (the
+    large one sized for the dtype, then (4, 5)), 8 heads x 32 dims
+    (2,144,079,872 value bytes per batch in float32, 2,145,396,736 in 16-bit;
+    batch 1 starts 2 GiB into the tensor), 4 points, `queries` queries.
+    Level-0 locations U[0.97, 1.02]^2 (the map's last rows and columns, some
+    corners off the map), level-1 locations U[-0.1, 1.1]^2 (the last keys of
+    the batch).  value is U[-1, 1), drawn directly in float32 to keep the
+    draw cheap, then rounded to the dtype; weights and grad_output as in
+    make()."""
+    shapes = np.asarray(OFFSET_LIMIT_LEVELS[4 if dtype == "f32" else 2], dtype=np.int64)
+    K = int((shapes[:, 0] * shapes[:, 1]).sum())
+    bs, M, D, L, P, Q = 2, 8, 32, 2, 4, queries
+    rng = np.random.default_rng(seed)
+    v = rng.random((bs, K, M, D), dtype=np.float32)
+    v *= 2.0
+    v -= 1.0
+    value = torch.from_numpy(v).to(DTYPES[dtype])
+    del v
+    loc = np.empty((bs, Q, M, L, P, 2))
+    loc[:, :, :, 0] = rng.uniform(0.97, 1.02, size=(bs, Q, M, P, 2))
+    loc[:, :, :, 1] = rng.uniform(-0.1, 1.1, size=(bs, Q, M, P, 2))
+    w = _softmax_last(rng.standard_normal((bs, Q, M, L * P))).reshape(bs, Q, M, L, P)
+    g = rng.standard_normal((bs, Q, M * D))
+    return Workload(f"offset_limit_{dtype}", dtype, shapes, level_starts(shapes), value, _cast(loc, dtype),
+                    _cast(w, dtype), _cast(g, dtype))
+
+
 NAMED = {
     "tiny_single_level": tiny_single_level,
     "detr_encoder": detr_encoder,

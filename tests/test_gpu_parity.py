@@ -138,6 +138,46 @@ def test_edge_case(case):
     check_backward(wl, gpu_backward(wl, t))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_byte_offset_limit(dtype):
+    """Per batch, value bytes within 4 MiB below 2^31 (the envelope's limit on
+    32-bit byte offsets; one past the last byte is the off-map sentinel), bs
+    2 so that batch 1's rows lie beyond 2^31 bytes from the tensor start;
+    samples on the map's last rows and columns and in the last level.  At
+    this size the backward scatters with float atomics (more keys than the
+    binned records address), for fp16 into a float32 workspace of more than
+    2^31 elements that is then rounded.  Forward, grad_loc and grad_w in full
+    against the oracle; grad_value on every row either side touched, the
+    tolerance's RMS taken over the whole tensor, and every other row exactly
+    zero."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    wl = W.offset_limit(dtype)
+    bs, K, M, D = wl.value.shape
+    per_batch = K * M * D * wl.value.element_size()
+    assert 2 ** 31 - (4 << 20) < per_batch < 2 ** 31
+    print(f"[gpu] offset limit {dtype}: bs {bs} K {K} bytes per batch {per_batch}", flush=True)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+    assert _lib.validate(prob) == 0
+    t = to_device(wl)
+    check_forward(wl, gpu_forward(wl, t))
+    gv, gl, gw = gpu_backward(wl, t)
+    del t
+    rgv, rgl, rgw = oracle_backward(wl)
+    rtol, arms, atol = TOL[(dtype, "bwd")]
+    assert_close(f"{wl.name}/grad_attention_weights", f64(gw), rgw, rtol, arms)
+    assert_close(f"{wl.name}/grad_sampling_locations", f64(gl), rgl, rtol, arms)
+    ref_rows = rgv.reshape(bs * K, M * D)
+    ref_touched = np.flatnonzero(np.any(ref_rows != 0.0, axis=1))
+    gpu_rows = gv.view(bs * K, M * D)
+    gpu_touched = torch.nonzero(gpu_rows.abs().amax(dim=1) != 0).flatten().cpu().numpy()
+    rows = np.union1d(ref_touched, gpu_touched)
+    assert rows.size > 0 and rows.max() >= K, "batch 1 holds touched rows"
+    rms = float(np.sqrt(np.sum(ref_rows[ref_touched] ** 2) / ref_rows.size))
+    got = gpu_rows[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    assert_close(f"{wl.name}/grad_value (touched rows)", got, ref_rows[rows], rtol, atol=arms * rms)
+    assert np.setdiff1d(gpu_touched, ref_touched).size == 0
+
+
 def test_pixel_centres_and_kinks():
     """Locations on exact pixel centres (integer pixel coordinates: every
     sample is a kink) on non-power-of-two maps: same floor decisions as the
