@@ -138,6 +138,33 @@ def test_edge_case(case):
     check_backward(wl, gpu_backward(wl, t))
 
 
+@pytest.mark.parametrize("levels,dtype,binned", [
+    ([(512, 1024)], "f32", True),                # 2048 segments of 256 keys: the LDS histogram's size
+    ([(512, 1024)], "bf16", True),
+    ([(512, 1024), (2, 64)], "f32", False),      # 2052 segments: float atomics instead
+], ids=["2048_f32", "2048_bf16", "2052_f32"])
+def test_segment_limit(levels, dtype, binned):
+    """The binned backward at its segment limit: embed_dims 8 and few records
+    per key give segments of 256 keys, so a level of 512 x 1024 keys fills
+    exactly the 2048 histogram slots per plane; a second level of 2 x 64 keys
+    (four more segments) takes the float-atomic backward.  The path taken
+    shows in the workspace size (float32 problems need none without
+    records).  (A 1 x 1 second level would make one element per head and
+    channel the float32 sum of about 8,000 largely cancelling atomic adds in
+    arbitrary order; its rounding then exceeds the elementwise bar on
+    occasional elements, whatever the kernel.)"""
+    from scale_deformable_attention_03_amd import _lib, ops
+    wl = W.make(f"segments_{dtype}", 1, levels, 2, 8, 4, 2000, dtype, seed=1041, loc_args=(-0.05, 1.05))
+    print(f"[gpu] segment limit {levels} {dtype}", flush=True)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+    ws = _lib.workspace_bytes(prob)
+    if dtype == "f32":
+        assert (ws > 0) == binned
+    t = to_device(wl)
+    check_forward(wl, gpu_forward(wl, t))
+    check_backward(wl, gpu_backward(wl, t))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_byte_offset_limit(dtype):
     """Per batch, value bytes within 4 MiB below 2^31 (the envelope's limit on
