@@ -165,6 +165,23 @@ def test_segment_limit(levels, dtype, binned):
     check_backward(wl, gpu_backward(wl, t))
 
 
+def test_query_field_limit():
+    """2^24 - 1 queries in one plane, the most the binned records' 24-bit
+    query field holds (one head, one level of 64 x 64 keys, one point,
+    embed_dims 8): every query index up to the field's maximum is packed
+    into a record and read back as a grad_output row."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    Q = (1 << 24) - 1
+    wl = W.make("query_limit", 1, [(64, 64)], 1, 8, 1, Q, "f32", seed=1042, loc_args=(-0.05, 1.05),
+                weight_dist="u+1e-5")
+    print(f"[gpu] query field limit: Q {Q}", flush=True)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+    assert _lib.workspace_bytes(prob) > 0, "binned backward"
+    t = to_device(wl)
+    check_forward(wl, gpu_forward(wl, t))
+    check_backward(wl, gpu_backward(wl, t))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_byte_offset_limit(dtype):
     """Per batch, value bytes within 4 MiB below 2^31 (the envelope's limit on
