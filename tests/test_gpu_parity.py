@@ -125,6 +125,10 @@ EDGE = [
     ("planes72_sparse", 9, [(20, 27), (10, 14)], 8, 16, 2, 40, "f32", "uniform", (-0.1, 1.1)),
     ("planes130_dense", 26, [(6, 7), (3, 4)], 5, 8, 4, 300, "f32", "uniform", (-0.1, 1.1)),
     ("planes72_dense_bf16", 9, [(8, 9), (4, 5)], 8, 16, 4, 150, "bf16", "uniform", (-0.1, 1.1)),
+    # level extents at the binned path's limit (16-bit cell fields: x0 + 1 and
+    # y0 + 1 up to 65534)
+    ("width65534_binned", 1, [(2, 65534)], 1, 8, 2, 3000, "f32", "uniform", (-0.05, 1.05)),
+    ("height65534_binned", 1, [(65534, 2)], 1, 8, 2, 3000, "f32", "uniform", (-0.05, 1.05)),
 ]
 
 
