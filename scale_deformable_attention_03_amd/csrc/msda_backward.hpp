@@ -507,24 +507,20 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         __syncthreads();
     }
 
-    // prologue: one lane per sample.  With REF != 0 the weight kept is the
-    // softmax weight even for a sample off the map (its gradient reaches the
-    // other logits of the group); nothing reads it there but the softmax
-    // backward.
-    for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-        const int g = i / LP, lp = i - g * LP, l = lp / P;
-        const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-        const int4 lv = s_lv[l];
+    // prologue: sample i = g * LP + lp of the workgroup, its location xy and
+    // (REF == 0) its attention weight w_in -> LDS record and segment counts.
+    // With REF != 0 the weight kept is the softmax weight even for a sample
+    // off the map (its gradient reaches the other logits of the group);
+    // nothing reads it there but the softmax backward.
+    auto stage = [&](int i, int g, int lp, float2 xy, float w_in) {
+        const int4 lv = s_lv[lp / P];
         const int H = lv.x, W = lv.y;
-        const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
-        const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(W), static_cast<float>(H),
-                                                   static_cast<float>(P));
         Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
         // padded corners read as zero; their records still go to the
         // accumulation, which writes padded rows as zero
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, W);
         float aw;
-        if constexpr (REF == 0) aw = c.ok ? load_scalar<ST>(attw, si) : 0.0f;
+        if constexpr (REF == 0) aw = c.ok ? w_in : 0.0f;
         else aw = se[i] / group_total(se + g * LP, LP);
         uint32_t* r = srec + g * gstride + lp * 8;
         const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
@@ -536,6 +532,30 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             if (c.ok)
                 for_each_record(c.x0, c.y0, W, H, lv.w & 0xff, lv.w >> 8,
                                 [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
+        }
+    };
+    if constexpr (kPairedPrologue<ST, REF, L_CT, P_CT>) {
+        // two samples of one group per lane: one 16-byte location load and
+        // one 8-byte weight load
+        for (int i = 2 * threadIdx.x; i < t.gcount * LP; i += 2 * blockDim.x) {
+            const int g = i / LP, lp = i - g * LP;
+            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+            const float4 xy2 = *reinterpret_cast<const float4*>(static_cast<const float*>(loc) + 2 * si);
+            const float2 w2 = *reinterpret_cast<const float2*>(static_cast<const float*>(attw) + si);
+            stage(i, g, lp, make_float2(xy2.x, xy2.y), w2.x);
+            stage(i + 1, g, lp + 1, make_float2(xy2.z, xy2.w), w2.y);
+        }
+    } else {
+        for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+            const int g = i / LP, lp = i - g * LP, l = lp / P;
+            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+            const int4 lv = s_lv[l];
+            const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
+            const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
+                                                       static_cast<float>(lv.x), static_cast<float>(P));
+            float w_in = 0.0f;
+            if constexpr (REF == 0) w_in = load_scalar<ST>(attw, si);
+            stage(i, g, lp, xy, w_in);
         }
     }
     __syncthreads();

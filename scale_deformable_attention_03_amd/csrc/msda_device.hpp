@@ -286,6 +286,13 @@ __device__ __forceinline__ float2 sample_location(const void* loc_or_off, const 
     }
 }
 
+// Prologues take two samples per lane (one 16-byte location load, one
+// 8-byte weight load) when the samples are float32 locations and weights
+// (not the fused form) and L * P is a fixed even number, so that a lane's
+// pair never straddles two groups and its loads stay aligned.
+template <int ST, int REF, int L_CT, int P_CT>
+constexpr bool kPairedPrologue = ST == kF32 && REF == 0 && L_CT != 0 && P_CT != 0 && (L_CT * P_CT) % 2 == 0;
+
 // Softmax of each (batch, query, head)'s L*P logits, staged through LDS for
 // the gcount groups G0, G0 + M, ... of a workgroup (sample i = g * LP + lp):
 // load_logits fills sv; after a barrier exp_logits writes

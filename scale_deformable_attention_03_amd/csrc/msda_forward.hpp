@@ -138,23 +138,44 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         __syncthreads();
     }
 
-    // prologue: one lane per sample
-    for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-        const int g = i / LP, lp = i - g * LP, l = lp / P;
-        const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-        const int4 lv = s_lv[l];
-        const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
-        const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
-                                                   static_cast<float>(lv.x), static_cast<float>(P));
+    // prologue: sample i = g * LP + lp of the workgroup, its location xy and
+    // (REF == 0) its attention weight w_in -> LDS record
+    auto stage = [&](int i, int g, int lp, float2 xy, float w_in) {
+        const int4 lv = s_lv[lp / P];
         Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
         float aw;
-        if constexpr (REF == 0) aw = c.ok ? load_scalar<ST>(attw, si) : 0.0f;
+        if constexpr (REF == 0) aw = c.ok ? w_in : 0.0f;
         else aw = c.ok ? se[i] / group_total(se + g * LP, LP) : 0.0f;
         const float wy0 = aw * c.hy, wy1 = aw * c.ly;
         uint32_t* r = sm + g * gstride + lp * 8;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
         *reinterpret_cast<float4*>(r + 4) = make_float4(wy0 * c.hx, wy0 * c.lx, wy1 * c.hx, wy1 * c.lx);
+    };
+    if constexpr (kPairedPrologue<ST, REF, L_CT, P_CT>) {
+        // two samples of one group per lane: their locations in one 16-byte
+        // load, their weights in one 8-byte load (fewer load instructions
+        // through the texture path the main loop saturates)
+        for (int i = 2 * threadIdx.x; i < t.gcount * LP; i += 2 * blockDim.x) {
+            const int g = i / LP, lp = i - g * LP;
+            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+            const float4 xy2 = *reinterpret_cast<const float4*>(static_cast<const float*>(loc) + 2 * si);
+            const float2 w2 = *reinterpret_cast<const float2*>(static_cast<const float*>(attw) + si);
+            stage(i, g, lp, make_float2(xy2.x, xy2.y), w2.x);
+            stage(i + 1, g, lp + 1, make_float2(xy2.z, xy2.w), w2.y);
+        }
+    } else {
+        for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
+            const int g = i / LP, lp = i - g * LP, l = lp / P;
+            const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
+            const int4 lv = s_lv[l];
+            const int64_t ri = (static_cast<int64_t>(t.b) * pb.Q + t.q0 + g) * L + l;
+            const float2 xy = sample_location<ST, REF>(loc, ref, si, ri, static_cast<float>(lv.y),
+                                                       static_cast<float>(lv.x), static_cast<float>(P));
+            float w_in = 0.0f;
+            if constexpr (REF == 0) w_in = load_scalar<ST>(attw, si);
+            stage(i, g, lp, xy, w_in);
+        }
     }
     __syncthreads();
 
