@@ -534,16 +534,20 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                 [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
         }
     };
-    if constexpr (kPairedPrologue<ST, REF, L_CT, P_CT>) {
-        // two samples of one group per lane: one 16-byte location load and
-        // one 8-byte weight load
-        for (int i = 2 * threadIdx.x; i < t.gcount * LP; i += 2 * blockDim.x) {
+    if constexpr (kPrologueSamples<ST, REF, L_CT, P_CT> > 1) {
+        // S samples of one group per lane: their locations in one 16-byte
+        // load, their weights in one 8-byte load (fewer load instructions
+        // through the texture path the main loop saturates)
+        constexpr int S = kPrologueSamples<ST, REF, L_CT, P_CT>;
+        constexpr int SE = Elem<ST>::bytes;
+        for (int i = S * threadIdx.x; i < t.gcount * LP; i += S * blockDim.x) {
             const int g = i / LP, lp = i - g * LP;
             const int64_t si = (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + lp;
-            const float4 xy2 = *reinterpret_cast<const float4*>(static_cast<const float*>(loc) + 2 * si);
-            const float2 w2 = *reinterpret_cast<const float2*>(static_cast<const float*>(attw) + si);
-            stage(i, g, lp, make_float2(xy2.x, xy2.y), w2.x);
-            stage(i + 1, g, lp + 1, make_float2(xy2.z, xy2.w), w2.y);
+            float xy[2 * S], wv[S];
+            widen<ST, 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * si * SE), xy);
+            widen<ST, S * SE>(load_raw<S * SE>(static_cast<const char*>(attw) + si * SE), wv);
+#pragma unroll
+            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, make_float2(xy[2 * k], xy[2 * k + 1]), wv[k]);
         }
     } else {
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {

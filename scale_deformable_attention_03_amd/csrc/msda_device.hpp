@@ -286,12 +286,15 @@ __device__ __forceinline__ float2 sample_location(const void* loc_or_off, const 
     }
 }
 
-// Prologues take two samples per lane (one 16-byte location load, one
-// 8-byte weight load) when the samples are float32 locations and weights
-// (not the fused form) and L * P is a fixed even number, so that a lane's
-// pair never straddles two groups and its loads stay aligned.
+// Samples per lane in the prologues: S = 16 / (2 * sample bytes) (2 for
+// float32 locations and weights, 4 for 16-bit ones), so that one 16-byte
+// load holds a lane's S locations and one 8-byte load its S weights.  Taken
+// for the plain form (not the fused one) when L * P is fixed and a multiple
+// of S, so a lane's samples never straddle two groups and its loads stay
+// aligned; 1 (one sample per lane, scalar loads) otherwise.
 template <int ST, int REF, int L_CT, int P_CT>
-constexpr bool kPairedPrologue = ST == kF32 && REF == 0 && L_CT != 0 && P_CT != 0 && (L_CT * P_CT) % 2 == 0;
+constexpr int kPrologueSamples =
+    REF == 0 && L_CT != 0 && P_CT != 0 && (L_CT * P_CT) % (8 / Elem<ST>::bytes) == 0 ? 8 / Elem<ST>::bytes : 1;
 
 // Softmax of each (batch, query, head)'s L*P logits, staged through LDS for
 // the gcount groups G0, G0 + M, ... of a workgroup (sample i = g * LP + lp):
