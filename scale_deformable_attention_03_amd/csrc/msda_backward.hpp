@@ -589,6 +589,17 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // (two for float32, whose occupancy then doubles; four for 16-bit rows)
         constexpr int kSBMax = E == 4 ? 2 : 4;
         constexpr int kSB = kC % kSBMax == 0 ? kSBMax : 1;
+        // Plain form with L * P = kOwn * LPR and 2 * kOwn sample elements of
+        // 16 bytes: lane li keeps the results of samples kOwn * li ..
+        // kOwn * li + kOwn - 1 over all chunks and stores them once, one
+        // 16-byte grad_loc store and one 8-byte grad_w store.
+        constexpr int kOwn = REF == 0 && kFixedLP && (L_CT * P_CT) % LPR == 0 &&
+                                     2 * ((L_CT * P_CT) / LPR) * Elem<ST>::bytes == 16
+                                 ? (L_CT * P_CT) / LPR
+                                 : 1;
+        float keep_w[kOwn], keep_x[kOwn], keep_y[kOwn];
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k) keep_w[k] = keep_x[k] = keep_y[k] = 0.0f;
 #pragma unroll 1
         for (int c0 = 0; c0 < LP; c0 += kC) {
             float own_w = 0.0f, own_x = 0.0f, own_y = 0.0f;
@@ -644,7 +655,24 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     // a sample off the map (all four corners at kOffMap) gets exactly
                     // zero gradients, whatever grad_output holds
                     const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
-                    if (li == b0 + u) {
+                    if constexpr (kOwn > 1) {
+                        // chunks start at multiples of LPR, a multiple of kOwn:
+                        // the slot (b0 + u) % kOwn is known at compile time
+                        if (li == lp / kOwn) {
+                            const int l = lp / P;            // uniform across the wave
+                            const float vw = off ? 0.0f : sw;
+                            const float vx = off ? 0.0f : sx * (static_cast<float>(pb.lv.W[l]) * fr.z);
+                            const float vy = off ? 0.0f : sy * (static_cast<float>(pb.lv.H[l]) * fr.z);
+#pragma unroll
+                            for (int k = 0; k < kOwn; ++k) {
+                                if ((b0 + u) % kOwn == k) {
+                                    keep_w[k] = vw;
+                                    keep_x[k] = vx;
+                                    keep_y[k] = vy;
+                                }
+                            }
+                        }
+                    } else if (li == b0 + u) {
                         const int l = lp / P;                // uniform across the wave
                         own_w = off ? 0.0f : sw;
                         if constexpr (REF == 0) {
@@ -660,7 +688,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     }
                 }
             }
-            if (li < kC) {
+            if (kOwn == 1 && li < kC) {
                 const int64_t s = G * LP + c0 + li;
                 if constexpr (REF == 0) {
                     store_scalar<ST>(grad_w, s, own_w);
@@ -677,6 +705,18 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 }
                 store_pair<ST>(grad_loc, s, own_x, own_y);
             }
+        }
+        if constexpr (kOwn > 1) {
+            constexpr int SE = Elem<ST>::bytes;
+            const int64_t s0 = G * LP + kOwn * li;
+            float xy[2 * kOwn];
+#pragma unroll
+            for (int k = 0; k < kOwn; ++k) {
+                xy[2 * k] = keep_x[k];
+                xy[2 * k + 1] = keep_y[k];
+            }
+            store_raw<16>(static_cast<char*>(grad_loc) + s0 * 2 * SE, narrow<ST, 16>(xy));
+            store_raw<kOwn * SE>(static_cast<char*>(grad_w) + s0 * SE, narrow<ST, kOwn * SE>(keep_w));
         }
     }
     if constexpr (REF != 0) {
