@@ -589,13 +589,15 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // (two for float32, whose occupancy then doubles; four for 16-bit rows)
         constexpr int kSBMax = E == 4 ? 2 : 4;
         constexpr int kSB = kC % kSBMax == 0 ? kSBMax : 1;
-        // Plain form with L * P = kOwn * LPR and 2 * kOwn sample elements of
-        // 16 bytes: lane li keeps the results of samples kOwn * li ..
-        // kOwn * li + kOwn - 1 over all chunks and stores them once, one
-        // 16-byte grad_loc store and one 8-byte grad_w store.
-        constexpr int kOwn = REF == 0 && kFixedLP && (L_CT * P_CT) % LPR == 0 &&
-                                     2 * ((L_CT * P_CT) / LPR) * Elem<ST>::bytes == 16
-                                 ? (L_CT * P_CT) / LPR
+        // Plain form with L * P = kOwn * LPR, kOwn dividing LPR and kOwn
+        // weights filling 8 or 16 bytes: lane li keeps the results of samples
+        // kOwn * li .. kOwn * li + kOwn - 1 over all chunks and stores them
+        // once, grad_loc in one or two 16-byte stores and grad_w in one.
+        constexpr int kOwnLP = kFixedLP ? (L_CT * P_CT) / LPR : 0;
+        constexpr int kOwn = REF == 0 && kFixedLP && (L_CT * P_CT) % LPR == 0 && kOwnLP > 1 &&
+                                     LPR % kOwnLP == 0 &&
+                                     (kOwnLP * Elem<ST>::bytes == 8 || kOwnLP * Elem<ST>::bytes == 16)
+                                 ? kOwnLP
                                  : 1;
         float keep_w[kOwn], keep_x[kOwn], keep_y[kOwn];
 #pragma unroll
@@ -715,7 +717,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 xy[2 * k] = keep_x[k];
                 xy[2 * k + 1] = keep_y[k];
             }
-            store_raw<16>(static_cast<char*>(grad_loc) + s0 * 2 * SE, narrow<ST, 16>(xy));
+            char* gl = static_cast<char*>(grad_loc) + s0 * 2 * SE;
+            store_raw<16>(gl, narrow<ST, 16>(xy));
+            if constexpr (2 * kOwn * SE == 32) store_raw<16>(gl + 16, narrow<ST, 16>(xy + 16 / SE));
             store_raw<kOwn * SE>(static_cast<char*>(grad_w) + s0 * SE, narrow<ST, kOwn * SE>(keep_w));
         }
     }
