@@ -140,11 +140,15 @@ msda::Problem pack(const msda_problem_t* p) {
     pb.lpr_active = lane_split(p->embed_dims, p->dtype).active;
     pb.ngroups = int64_t(p->batch) * p->num_queries * p->num_heads;
     pb.nplanes = p->batch * p->num_heads;
-    // Sparse problems (fewer than one record per key on average: two per
-    // sample, Q * L * P samples per plane) have many short units; they take
-    // smaller units and tiles (16 KB instead of 32 KB), so that more units
-    // run per CU.
-    const bool sparse = 2.0 * double(p->num_queries) * p->num_levels * p->num_points < double(p->num_keys);
+    // Sparse problems have many short units; they take smaller units and
+    // tiles (16 KB instead of 32 KB), so that more units run per CU.  A
+    // problem is sparse when its largest level gets fewer than one record per
+    // key (two per sample, Q * P samples per level and plane): that level's
+    // segments hold most of the units.
+    int64_t largest = 0;
+    for (int l = 0; l < p->num_levels; ++l)
+        largest = std::max<int64_t>(largest, p->spatial_shapes[2 * l] * p->spatial_shapes[2 * l + 1]);
+    const bool sparse = 2.0 * double(p->num_queries) * p->num_points < double(largest);
     pb.unit_records = sparse ? msda::kSparseUnitRecords : msda::kUnitRecords;
     const int max_shift = floor_log2(std::min<int64_t>(msda::kMaxSegKeys, (sparse ? 4096 : 8192) / p->embed_dims));
     int64_t nseg = 0;
