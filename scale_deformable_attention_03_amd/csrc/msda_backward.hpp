@@ -19,16 +19,18 @@
 // grad_value is a transposed gather: row (b, key, m) sums w * (bilinear
 // weight) * grad_output[b, q, m] over every sample corner that lands on it.
 // Scattering those D-wide contributions with float atomics costs one L2
-// atomic per row per sample corner; measured on MI355X that path tops out
-// near 340 G float updates/s, far below what the gather side runs at.  So the
-// backward bins instead:
+// atomic per element per sample corner: on MI355X the scatter kernel of
+// msda_micro.hip adds the DETR encoder's 584 M such updates at 68-119 G/s
+// (4.9-8.6 ms), against well under a millisecond for the whole binned
+// backward.  So the backward bins instead:
 //
 //   1. count     each (batch, head) plane's keys are cut into segments; the
 //                in-map corners of one image row of a sample's cell make a
-//                record; count records per segment (LDS histograms, one
-//                global add per non-empty bin).
-//   2. scan      exclusive prefix over the counts gives each segment a record
-//                range and a cursor; segments are split into units of at most
+//                record; count records per segment (an LDS histogram per
+//                workgroup, written out as that workgroup's row of counts).
+//   2. scan      sum the rows, then an exclusive prefix over the counts gives
+//                each segment a record range and a cursor (small planes count
+//                and scan in one kernel); segments are split into units of at most
 //                unit_records (kUnitRecords, or kSparseUnitRecords for sparse
 //                problems) records.
 //   3. gradient  the gather kernel (grad_w, grad_loc) also writes its records
@@ -39,7 +41,7 @@
 //                accumulating rows in registers, merge into an LDS tile, and
 //                write every row of the segment once with plain stores (units
 //                of a segment split in several use float atomics instead, into
-//                rows the scan zeroed).
+//                rows the gradient kernel zeroed).
 //
 // Segment sizes per level are planned on the host from the expected records
 // per key, so that most segments fit one unit.  Outside the envelope of the
