@@ -9,10 +9,11 @@
 // plane; consecutive workgroups walk a plane's queries, and the XCD-aware
 // block order gives each XCD contiguous runs of them, so a plane's value
 // rows (K * D elements) stay in that XCD's L2.
-//   prologue   one lane per sample: pixel coordinates, the cell's four corner
-//              byte offsets within the plane (kOffMap for a corner off the
-//              map) and the four corner weights times the attention weight,
-//              into LDS (8 words per sample);
+//   prologue   one lane per sample (two or four per lane, with vector loads,
+//              where kPrologueSamples allows): pixel coordinates, the cell's
+//              four corner byte offsets within the plane (kOffMap for a
+//              corner off the map) and the four corner weights times the
+//              attention weight, into LDS (8 words per sample);
 //   main loop  LPR lanes per query, VECB bytes of the D channels per lane:
 //              per sample, two broadcast LDS reads, four raw-buffer loads
 //              (off-map corners read as zeros) and 4*VEC FMAs into float32
