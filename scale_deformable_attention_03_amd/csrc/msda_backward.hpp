@@ -70,7 +70,7 @@ constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
 constexpr int kMaxWgSamples = 1024;    // samples one gradient workgroup holds
 constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path (16-bit cell fields)
 constexpr int kCountBlock = 512;       // lanes of a counting workgroup
-constexpr int kCountChunk = 8192;      // samples one counting workgroup bins (at least)
+constexpr int kCountChunk = 4096;      // samples one counting workgroup bins (at least)
 constexpr int kMaxCountChunks = 64;    // counting workgroups (histogram rows) per plane
 
 // Corners of one row that a record covers.
