@@ -403,28 +403,38 @@ __device__ void scan_plane(const int32_t* s_cnt, int32_t* s_wrec, int32_t* s_wun
     }
 }
 
-// One workgroup per plane: sums the plane's nchunks histogram rows, then
-// scan_plane.  (static: every translation unit that launches it has its own
-// copy, as for the other non-template kernels.)
-[[maybe_unused]] static __global__ void __launch_bounds__(kBlock)
+// One workgroup of kScanBlock lanes per plane: sums the plane's nchunks
+// histogram rows, then scan_plane.  Up to four lanes share a segment's rows
+// (every parts-th row each, combined by lane shuffles), so that a segment's
+// loads are spread over several lanes.  (static: every translation unit that
+// launches it has its own copy, as for the other non-template kernels.)
+constexpr int kScanBlock = 1024;
+
+[[maybe_unused]] static __global__ void __launch_bounds__(kScanBlock)
 msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* __restrict__ cursor,
                      int32_t* __restrict__ nunits, int32_t* __restrict__ multi, int4* __restrict__ units,
                      int accumulate, Problem pb, int plane_records, int plane_units) {
     __shared__ int32_t s_cnt[kMaxSegments];
-    __shared__ int32_t s_wrec[kBlock / 64], s_wunit[kBlock / 64];
+    __shared__ int32_t s_wrec[kScanBlock / 64], s_wunit[kScanBlock / 64];
     __shared__ int32_t s_nmulti;
     const int pl = blockIdx.x, n = pb.nseg;
     if (threadIdx.x == 0) s_nmulti = 0;
     const int32_t* rows = counts + static_cast<int64_t>(pl) * nchunks * n;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
+    // lanes per segment: 4, 2 or 1, as many as the workgroup holds; a
+    // segment's lanes are adjacent (same wave, same trip count)
+    const int parts = 4 * n <= kScanBlock ? 4 : (2 * n <= kScanBlock ? 2 : 1);
+    const int t = static_cast<int>(threadIdx.x), part = t % parts;
+    for (int i = t / parts; i < n; i += kScanBlock / parts) {
         int sum = 0;
 #pragma unroll 8
-        for (int c = 0; c < nchunks; ++c) sum += rows[static_cast<int64_t>(c) * n + i];
-        s_cnt[i] = sum;
+        for (int c = part; c < nchunks; c += parts) sum += rows[static_cast<int64_t>(c) * n + i];
+        if (parts >= 2) sum += __shfl_xor(sum, 1, 64);
+        if (parts >= 4) sum += __shfl_xor(sum, 2, 64);
+        if (part == 0) s_cnt[i] = sum;
     }
     __syncthreads();
-    scan_plane<kBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb, pl,
-                       plane_records, plane_units);
+    scan_plane<kScanBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb, pl,
+                           plane_records, plane_units);
 }
 
 // Count and scan in one launch, one workgroup of kCountScanBlock lanes per
