@@ -166,9 +166,11 @@ size_t msda_backward_workspace_bytes(const msda_problem_t *problem);
  *   the factors W and H); at an integer pixel coordinate the cell that floor
  *   selects is used (the right derivative).  Samples outside the map get zero
  *   gradients.
- *   All three gradients are OVERWRITTEN (not accumulated).  grad_value is
- *   accumulated with float32 atomics, so its low bits may vary from run to
- *   run; the other two gradients are bitwise repeatable.
+ *   All three gradients are OVERWRITTEN (not accumulated).  grad_value sums
+ *   its contributions in an order set at run time (record slots taken with
+ *   atomics; float32 atomics where a key segment spans several units), so
+ *   its low bits may vary from run to run; the other two gradients are
+ *   bitwise repeatable.
  *   workspace: device, at least msda_backward_workspace_bytes(problem) bytes
  *   (may be NULL when that is 0), 16-byte aligned, owned by the caller; its
  *   contents are scratch on entry and on exit.  Calls that overlap in time
