@@ -125,6 +125,16 @@ EDGE = [
     ("planes72_sparse", 9, [(20, 27), (10, 14)], 8, 16, 2, 40, "f32", "uniform", (-0.1, 1.1)),
     ("planes130_dense", 26, [(6, 7), (3, 4)], 5, 8, 4, 300, "f32", "uniform", (-0.1, 1.1)),
     ("planes72_dense_bf16", 9, [(8, 9), (4, 5)], 8, 16, 4, 150, "bf16", "uniform", (-0.1, 1.1)),
+    # the fixed L4P4 / L4P16 kernels at other lane splits: samples per lane in
+    # the prologues (2 for float32, 4 for 16-bit), samples kept per lane for
+    # the grad_loc / grad_w stores (16- and 32-byte grad_loc), and none
+    ("L4P4_f32_D16", 2, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 16, 4, 70, "f32", "uniform", (-0.1, 1.1)),
+    ("L4P4_bf16_D16", 2, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 16, 4, 70, "bf16", "uniform", (-0.1, 1.1)),
+    ("L4P4_f16_D64", 2, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 64, 4, 70, "f16", "uniform", (-0.1, 1.1)),
+    ("L4P4_f32_D64", 1, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 64, 4, 70, "f32", "uniform", (-0.1, 1.1)),
+    ("L4P16_f32_D16", 2, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 16, 16, 45, "f32", "uniform", (-0.1, 1.1)),
+    ("L4P16_bf16_D32", 2, [(12, 14), (6, 7), (3, 4), (2, 2)], 4, 32, 16, 45, "bf16", "uniform", (-0.1, 1.1)),
+    ("L4P16_f16_D64", 1, [(12, 14), (6, 7), (3, 4), (2, 2)], 8, 64, 16, 45, "f16", "uniform", (-0.1, 1.1)),
     # level extents at the binned path's limit (16-bit cell fields: x0 + 1 and
     # y0 + 1 up to 65534)
     ("width65534_binned", 1, [(2, 65534)], 1, 8, 2, 3000, "f32", "uniform", (-0.05, 1.05)),
