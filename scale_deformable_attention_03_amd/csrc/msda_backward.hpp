@@ -213,36 +213,57 @@ __device__ __forceinline__ void count_samples(const void* __restrict__ loc, cons
     const int L = L_CT ? L_CT : pb.L;
     const int P = P_CT ? P_CT : pb.P;
     const int LP = L * P;
-    constexpr int kU = 4;                            // samples whose loads fly together
-    for (int s0 = s_begin + static_cast<int>(threadIdx.x); s0 < s_end; s0 += kU * NT) {
-        float lx[kU], ly[kU];
+    // S samples per location load (one 16-byte load of S consecutive samples
+    // of a group, as in the gradient kernel's prologue); s_begin and s_end are
+    // multiples of S then
+    constexpr int S = kPrologueSamples<sample_dt(DT), REF, L_CT, P_CT>;
+    constexpr int SE = Elem<sample_dt(DT)>::bytes;
+    constexpr int kU = 4;                            // loads in flight together
+    for (int s0 = s_begin + S * static_cast<int>(threadIdx.x); s0 < s_end; s0 += kU * S * NT) {
+        float lx[kU * S], ly[kU * S];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int s = s0 + u * NT;
-            lx[u] = ly[u] = -2.0f;                       // off the map
+            const int s = s0 + u * S * NT;
+#pragma unroll
+            for (int k = 0; k < S; ++k) lx[u * S + k] = ly[u * S + k] = -2.0f;   // off the map
             if (s < s_end) {
                 const int q = s / LP, lp = s - q * LP, l = lp / P;
                 const int64_t i = ((static_cast<int64_t>(b) * pb.Q + q) * pb.M + m) * LP + lp;
-                const int64_t ri = (static_cast<int64_t>(b) * pb.Q + q) * L + l;
-                const int4 lv = s_lv[l];
-                const float2 xy = sample_location<sample_dt(DT), REF>(loc, ref, i, ri, static_cast<float>(lv.y),
-                                                           static_cast<float>(lv.x), static_cast<float>(P));
-                lx[u] = xy.x;
-                ly[u] = xy.y;
+                if constexpr (S > 1) {
+                    float xy[2 * S];
+                    widen<sample_dt(DT), 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * i * SE), xy);
+#pragma unroll
+                    for (int k = 0; k < S; ++k) {
+                        lx[u * S + k] = xy[2 * k];
+                        ly[u * S + k] = xy[2 * k + 1];
+                    }
+                } else {
+                    const int64_t ri = (static_cast<int64_t>(b) * pb.Q + q) * L + l;
+                    const int4 lv = s_lv[l];
+                    const float2 xy = sample_location<sample_dt(DT), REF>(loc, ref, i, ri, static_cast<float>(lv.y),
+                                                                           static_cast<float>(lv.x),
+                                                                           static_cast<float>(P));
+                    lx[u] = xy.x;
+                    ly[u] = xy.y;
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int s = s0 + u * NT;
-            if (s >= s_end) break;
-            const int lp = s % LP, l = lp / P;
-            const int4 lv = s_lv[l];
-            const int H = lv.x, W = lv.y;
-            float x, y;
-            if (!pixel_coords(lx[u], ly[u], static_cast<float>(W), static_cast<float>(H), x, y)) continue;
-            const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
-            for_each_record(x0, y0, W, H, lv.w & 0xff, lv.w >> 8,
-                            [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                const int s = s0 + u * S * NT + k;
+                if (s >= s_end) break;
+                const int lp = s % LP, l = lp / P;
+                const int4 lv = s_lv[l];
+                const int H = lv.x, W = lv.y;
+                float x, y;
+                if (!pixel_coords(lx[u * S + k], ly[u * S + k], static_cast<float>(W), static_cast<float>(H), x, y))
+                    continue;
+                const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
+                for_each_record(x0, y0, W, H, lv.w & 0xff, lv.w >> 8,
+                                [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
+            }
         }
     }
 }

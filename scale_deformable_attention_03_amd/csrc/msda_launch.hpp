@@ -62,7 +62,8 @@ const void* kfn(K* k) { return reinterpret_cast<const void*>(k); }
 inline int64_t count_chunk(const msda::Problem& pb) {
     const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
     const int64_t chunk = pb.nseg <= msda::kBlock ? msda::kCountChunk : 2 * msda::kCountChunk;
-    return std::max<int64_t>(chunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks);
+    // a multiple of 4 samples: the count loads 2 or 4 consecutive samples at once
+    return (std::max<int64_t>(chunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks) + 3) & ~int64_t(3);
 }
 inline int64_t count_chunks(const msda::Problem& pb) {
     const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
