@@ -65,6 +65,11 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
+def percentiles(us) -> dict:
+    """p10 / p50 / p90 of per-step event times (microseconds)."""
+    return {f"p{p}": round(float(np.percentile(us, p)), 2) for p in (10, 50, 90)}
+
+
 def kernel_digest() -> str:
     """Digest of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
@@ -419,6 +424,26 @@ def ceilings_leg(wl, dev, fwd_us: float, step_gbps: float) -> dict:
     return res
 
 
+def device_info(props) -> dict:
+    """What the run's device reports: name, architecture, compute units, L2
+    and memory sizes, peak engine and memory clocks (kHz, from the HIP
+    runtime torch loaded), HIP version."""
+    import torch
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+            "l2_bytes": getattr(props, "L2_cache_size", None), "memory_bytes": props.total_memory,
+            "hip": torch.version.hip}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        dev = torch.cuda.current_device()
+        for key, attr in (("clock_khz", 5), ("memory_clock_khz", 60)):    # hipDeviceAttribute values
+            v = ctypes.c_int()
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0:
+                info[key] = v.value
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     import oracle
     args = (wl.f32("value"), wl.spatial_shapes, wl.level_start_index,
@@ -713,6 +738,8 @@ def main() -> int:
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     step_us = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e3
+    fwd_us_all = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
+    bwd_us_all = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
     ms_per_step = wall * 1e3 / args.steps
 
     # warm: the same steps back to back on one buffer set (its working set
@@ -826,17 +853,15 @@ def main() -> int:
         "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "graph_replay_ms_per_step": round(graph_ms, 5),
         "warm_ms_per_step": round(warm_ms, 5),
-        "step_us_percentiles": {"p10": round(float(np.percentile(step_us, 10)), 2),
-                                "p50": round(float(np.percentile(step_us, 50)), 2),
-                                "p90": round(float(np.percentile(step_us, 90)), 2)},
+        "step_us_percentiles": percentiles(step_us),
+        "fwd_us_percentiles": percentiles(fwd_us_all),
+        "bwd_us_percentiles": percentiles(bwd_us_all),
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
         "bwd_stages_us": stages_us,
         "algorithmic_bytes": ab,
         "touched_value_rows": rows,
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count, "l2_bytes": getattr(props, "L2_cache_size", None),
-                   "memory_bytes": props.total_memory, "hip": torch.version.hip},
+        "device": device_info(props),
         "kernel_digest": digest,
         "roofline": roofline,
     }
