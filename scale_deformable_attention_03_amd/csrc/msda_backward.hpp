@@ -46,7 +46,8 @@
 // Segment sizes per level are planned on the host from the expected records
 // per key, so that most segments fit one unit.  Outside the envelope of the
 // record format (binned_ok on the host) the gradient kernel scatters
-// grad_value with float atomics instead.
+// grad_value with float atomics instead, after merging its own corners that
+// share a row (pre_reduce_scatter).
 #pragma once
 
 #include "msda_device.hpp"
@@ -488,6 +489,114 @@ msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// 3a. float-atomic grad_value with a workgroup pre-reduction
+// ---------------------------------------------------------------------------
+// Outside the record envelope the gradient workgroup adds its grad_value
+// contributions into float32 rows with global atomics.  Adding every sample
+// corner on its own makes a row that many samples reach (a coarse level) the
+// float32 sum of thousands of atomic adds in arbitrary order, whose rounding
+// can exceed the float32 bar.  So the workgroup first merges its corners by
+// row: every in-map corner of its samples is an entry (sample * 4 + corner,
+// 16 bits), counting-sorted into kPreBuckets buckets by a hash of the row;
+// one worker (LPR lanes) walks a bucket, summing the contributions
+// w * (bilinear weight) * grad_output of consecutive entries of one row in
+// registers, and adds each run once.  Rows that share a bucket interleave
+// there, which only splits their runs.  No LDS float atomics (slow on
+// gfx950): the sort uses integer ones.  A row reached by n corners of the
+// workgroup gets one atomic add per element instead of n.
+constexpr int kPreBuckets = 1024;
+
+__device__ __forceinline__ int pre_bucket(uint32_t off) { return static_cast<int>((off * 0x9E3779B1u) >> 22); }
+
+// srec: the prologue's sample records (8 words each: the four corner byte
+// offsets, lx, ly, the attention weight, the cell); pre_g: the workgroup's
+// grad_output rows as float32; gplane: the float32 rows of the workgroup's
+// (batch, head) plane, element offset = corner byte offset / E.  Starts
+// after a barrier; every lane of the workgroup calls it.
+template <int DT, int VECB, int LPR>
+__device__ void pre_reduce_scatter(const uint32_t* srec, int gstride, int LP, int gcount, const float* pre_g,
+                                   int32_t* start, int32_t* end, uint16_t* ids, float* gplane, const Problem& pb) {
+    constexpr int E = Elem<DT>::bytes;
+    constexpr int VEC = VECB / E;
+    const int nt = blockDim.x, ns = gcount * LP;
+    for (int i = threadIdx.x; i < kPreBuckets; i += nt) end[i] = 0;
+    __syncthreads();
+    for (int s = threadIdx.x; s < ns; s += nt) {
+        const uint4 o = *reinterpret_cast<const uint4*>(srec + (s / LP) * gstride + (s % LP) * 8);
+        if (o.x != kOffMap) atomicAdd(&end[pre_bucket(o.x)], 1);
+        if (o.y != kOffMap) atomicAdd(&end[pre_bucket(o.y)], 1);
+        if (o.z != kOffMap) atomicAdd(&end[pre_bucket(o.z)], 1);
+        if (o.w != kOffMap) atomicAdd(&end[pre_bucket(o.w)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {                          // exclusive scan of the counts, one wave
+        constexpr int kPer = kPreBuckets / 64;
+        const int lane = threadIdx.x;
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) sum += end[lane * kPer + j];
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int c = end[lane * kPer + j];
+            start[lane * kPer + j] = run;
+            end[lane * kPer + j] = run;              // the cursor; the bucket's end once filled
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int s = threadIdx.x; s < ns; s += nt) {
+        const uint4 o = *reinterpret_cast<const uint4*>(srec + (s / LP) * gstride + (s % LP) * 8);
+        const uint32_t oc[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (oc[c] != kOffMap) ids[atomicAdd(&end[pre_bucket(oc[c])], 1)] = static_cast<uint16_t>(4 * s + c);
+    }
+    __syncthreads();
+    const int nw = nt / LPR, w = threadIdx.x / LPR, li = threadIdx.x % LPR;
+    const bool active = li < pb.lpr_active;
+    float* dst = gplane + li * VEC;
+    for (int bk = w; bk < kPreBuckets; bk += nw) {
+        const int e1 = end[bk];
+        uint32_t row = kOffMap;
+        float acc[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+        for (int e = start[bk]; e < e1; ++e) {
+            const int id = ids[e], s = id >> 2, c = id & 3, g = s / LP;
+            const uint32_t* r = srec + g * gstride + (s - g * LP) * 8;
+            const uint32_t off = r[c];
+            const float lx = __uint_as_float(r[4]), ly = __uint_as_float(r[5]), aw = __uint_as_float(r[6]);
+            // the corner's weight: w * (1-ly or ly) * (1-lx or lx)
+            const float wy = aw * ((c & 2) ? ly : 1.0f - ly);
+            const float cw = wy * ((c & 1) ? lx : 1.0f - lx);
+            if (off != row) {
+                if (row != kOffMap && active) {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) atomic_add_f32(dst + row / E + i, acc[i]);
+                }
+                row = off;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+            }
+            const float* gg = pre_g + g * pb.D + li * VEC;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] += cw * gg[i];
+        }
+        if (row != kOffMap && active) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) atomic_add_f32(dst + row / E + i, acc[i]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 3. gradient (gather): grad_w, grad_loc, and grad_value records or atomics
 // ---------------------------------------------------------------------------
 // Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes, plane-local
@@ -501,7 +610,8 @@ msda_bin_count_scan_kernel(const void* __restrict__ loc, const void* __restrict_
 // record ranges, writes the records, and has the plane's workgroups zero the
 // rows of the plane's multi-unit segments (the accumulation adds into them).
 // LDS: gpb * (8 * L * P + 4) words; when BINNED also 2 * nseg int32 (counts,
-// then cursors, and bases).
+// then cursors, and bases); otherwise the pre-reduction's gpb * D floats,
+// 2 * kPreBuckets int32 and 4 * gpb * L * P uint16 (pre_reduce_scatter).
 template <int DTK, int VECB, int LPR, int L_CT, int P_CT, bool BINNED, int REF>
 __global__ void __launch_bounds__(kBlock)
 msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
@@ -526,6 +636,12 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
     // fused prologue: logits (later the weights' gradients) and exponentials
     float* sv = reinterpret_cast<float*>(lhist + (BINNED ? 2 * pb.nseg : 0));
     float* se = sv + gpb * LP;
+    // float-atomic path: the workgroup's grad_output rows (gpb * D floats),
+    // bucket starts and ends (kPreBuckets int32 each), entry ids (4 * gpb * LP u16)
+    float* pre_g = REF != 0 ? se + gpb * LP : sv;
+    int32_t* pre_start = reinterpret_cast<int32_t*>(pre_g + gpb * pb.D);
+    int32_t* pre_end = pre_start + kPreBuckets;
+    uint16_t* pre_id = reinterpret_cast<uint16_t*>(pre_end + kPreBuckets);
 
     const PlaneTile t = plane_tile(pb, gpb);
     const uint32_t pitch = static_cast<uint32_t>(pb.M * pb.D * E);
@@ -605,7 +721,6 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // lanes past the row read zeros through an off-map offset
         const uint32_t lane_b = active ? static_cast<uint32_t>(li * VECB) : kOffMap;
         const uint32_t* rec = srec + lg * gstride;
-        float* gb = gacc + (static_cast<int64_t>(t.b) * pb.K * pb.M + t.m) * pb.D + li * VEC;
 
         float g[VEC];
         if (active) {
@@ -613,6 +728,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         } else {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
+        }
+        if constexpr (!BINNED) {
+            // the query's grad_output row, for the pre-reduction below
+            if (active) {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) pre_g[lg * pb.D + li * VEC + i] = g[i];
+            }
         }
         // Samples go in chunks of kC (LPR, or all of them when fewer): lane li
         // of the group keeps the results of the chunk's sample li and stores
@@ -656,7 +778,6 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     const int lp = c0 + b0 + u;
                     const float4 fr = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);    // lx ly w cell
                     const float4 f = make_float4(1.0f - fr.x, fr.x, 1.0f - fr.y, fr.y);      // hx lx hy ly
-                    const float wy0 = fr.z * f.z, wy1 = fr.z * f.w;                          // w*hy w*ly
                     float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
                     widen<DT, VECB>(raw[u][0], v00);
                     widen<DT, VECB>(raw[u][1], v01);
@@ -669,18 +790,6 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                         d01 += g[i] * v01[i];
                         d10 += g[i] * v10[i];
                         d11 += g[i] * v11[i];
-                    }
-                    if constexpr (!BINNED) {
-                        if (active) {
-                            if (o[u].x != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].x / E + i, wy0 * f.x * g[i]);
-                            if (o[u].y != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].y / E + i, wy0 * f.y * g[i]);
-                            if (o[u].z != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].z / E + i, wy1 * f.x * g[i]);
-                            if (o[u].w != kOffMap)
-                                for (int i = 0; i < VEC; ++i) atomic_add_f32(gb + o[u].w / E + i, wy1 * f.y * g[i]);
-                        }
                     }
                     const float top = f.x * d00 + f.y * d01;
                     const float bot = f.x * d10 + f.y * d11;
@@ -769,6 +878,11 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const float wi = __uint_as_float(r[8 * (i - g * LP)]);
             store_scalar<ST>(grad_w, (t.G0 + static_cast<int64_t>(g) * pb.M) * LP + (i - g * LP), wi * (sv[i] - dot));
         }
+    }
+    if constexpr (!BINNED) {
+        __syncthreads();
+        pre_reduce_scatter<DT, VECB, LPR>(srec, gstride, LP, t.gcount, pre_g, pre_start, pre_end, pre_id,
+                                          gacc + (static_cast<int64_t>(t.b) * pb.K * pb.M + t.m) * pb.D, pb);
     }
     if constexpr (BINNED) {
         __syncthreads();
@@ -869,7 +983,10 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     constexpr int NW = kAccBlock / LPR;              // workers
     // consecutive units (neighbouring segments of one plane) run on one XCD,
     // so the plane's grad_output rows they gather stay in that XCD's L2
-    const int np = pb.nplanes, total = nunits[3 * np];
+    // (clamped to the grid and to [0, np): the words come from the gradient
+    // kernel's workgroup 0, and the host launches this kernel only after a
+    // gradient kernel with at least one workgroup)
+    const int np = pb.nplanes, total = min(nunits[3 * np], static_cast<int>(gridDim.x));
     if (static_cast<int>(blockIdx.x) >= total) return;
     // workgroups 0 .. total-1 cover the units; each XCD gets a contiguous run
     const int r = static_cast<int>(xcd_tile(blockIdx.x, total));
@@ -883,7 +1000,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
         lo += k;
         if (k < 64) break;
     }
-    const int4 unit = units[static_cast<int64_t>(lo) * plane_units + (r - nunits[2 * np + lo])];
+    lo = min(max(lo, 0), np - 1);
+    const int ui = min(max(r - nunits[2 * np + lo], 0), plane_units - 1);
+    const int4 unit = units[static_cast<int64_t>(lo) * plane_units + ui];
     const int pl = unit.x / pb.nseg, seg = unit.x - pl * pb.nseg;
     const int b = pl / pb.M, m = pl - b * pb.M;
     const int lvl = level_of_segment(pb, seg);

@@ -98,6 +98,9 @@ struct Grad {
         const int64_t blocks = plane_blocks(pb, gpb);
         size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
         if (binned) lds += sizeof(int32_t) * 2 * size_t(pb.nseg);
+        else  // the pre-reduction: grad_output rows, bucket starts and ends, entry ids
+            lds += sizeof(float) * size_t(gpb) * pb.D + sizeof(int32_t) * 2 * msda::kPreBuckets +
+                   sizeof(uint16_t) * 4 * size_t(gpb) * LP;
         const void* k;
         if (binned)
             k = ref_dims == 0   ? grad_kernel<DT, VECB, LPR, true, 0>(pb)
