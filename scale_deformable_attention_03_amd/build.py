@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmsda.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("msda_api.hip", "msda_kernels_f32.hip", "msda_kernels_f16.hip",
                                             "msda_kernels_bf16.hip", "msda_kernels_f16_f32.hip",
                                             "msda_kernels_bf16_f32.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp",
+HEADERS = [os.path.join(CSRC, f) for f in ("msda_types.hpp", "msda_plan.hpp", "msda_device.hpp", "msda_forward.hpp", "msda_backward.hpp",
                                            "msda_launch.hpp", "msda_launch_impl.hpp")] + [os.path.join(INCLUDE, "msda.h")]
 MICRO_LIB = os.path.join(PKG, "libmsda_micro.so")
 MICRO_SOURCES = [os.path.join(CSRC, "msda_micro.hip")]

@@ -21,10 +21,23 @@ using msda::kBF16;
 using msda::kBlock;
 using msda::kF16;
 using msda::kF32;
-using msda_host::count_chunks;
-using msda_host::fused_count_scan;
 using msda_host::kfn;
-using msda_host::LaneSplit;
+using msda_plan::BackwardPlan;
+using msda_plan::check_problem;
+using msda_plan::elem_bytes;
+using msda_plan::fill_blocks;
+using msda_plan::lane_split;
+using msda_plan::LaneSplit;
+using msda_plan::Layout;
+using msda_plan::layout;
+using msda_plan::out_elems;
+using msda_plan::pack;
+using msda_plan::plan_backward;
+using msda_plan::plane_records;
+using msda_plan::plane_units;
+using msda_plan::sample_elems;
+using msda_plan::value_dtype;
+using msda_plan::value_elems;
 using msda_host::launch;
 using msda_host::Launch;
 using msda_host::mark;
@@ -35,16 +48,6 @@ using msda_host::kStageGrad;
 using msda_host::kStageAccum;
 using msda_host::kStageNarrow;
 using msda_host::kStageEnd;
-
-constexpr int64_t kIndexLimit = int64_t(1) << 31;
-
-// Bytes of a value-side element (value, output and their gradients): 2
-// for fp16, bf16 and the mixed codes, whose per-sample tensors are float32.
-int elem_bytes(msda_dtype_t dt) { return dt == MSDA_F32 ? 4 : 2; }
-
-msda_dtype_t value_dtype(msda_dtype_t dt) {
-    return dt == MSDA_F16_F32 ? MSDA_F16 : dt == MSDA_BF16_F32 ? MSDA_BF16 : dt;
-}
 
 // Calls f(std::integral_constant<int, code>) for the kernels' dtype code.
 template <typename F>
@@ -60,191 +63,12 @@ msda_status_t by_code(msda_dtype_t dt, F&& f) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-LaneSplit lane_split(int embed_dims, msda_dtype_t dt) {
-    const int row = embed_dims * elem_bytes(dt);   // a multiple of 16 bytes
-    LaneSplit s;
-    s.vecb = row >= 64 ? 16 : (row % 8 == 0 && row >= 32 ? 8 : 4);
-    s.active = row / s.vecb;
-    s.lpr = 4;
-    while (s.lpr < s.active) s.lpr *= 2;
-    return s;
-}
-
-msda_status_t check_problem(const msda_problem_t* p) {
-    if (p == nullptr) return MSDA_ERROR_INVALID_VALUE;
-    if (p->dtype != MSDA_F32 && p->dtype != MSDA_F16 && p->dtype != MSDA_BF16 && p->dtype != MSDA_F16_F32 &&
-        p->dtype != MSDA_BF16_F32)
-        return MSDA_ERROR_INVALID_VALUE;
-    if (p->batch < 0 || p->num_queries < 0 || p->num_keys < 1 || p->num_heads < 1 ||
-        p->embed_dims < 1 || p->num_levels < 1 || p->num_points < 1)
-        return MSDA_ERROR_INVALID_VALUE;
-    if (p->spatial_shapes == nullptr || p->level_start_index == nullptr)
-        return MSDA_ERROR_INVALID_VALUE;
-    // Envelope of the Ascend API page (constraints): L*P <= 64, heads <= 8,
-    // embed_dims <= 256 and a multiple of 8.
-    if (p->embed_dims % 8 != 0 || p->embed_dims > 256 || p->num_heads > 8 ||
-        int64_t(p->num_levels) * p->num_points > 64)
-        return MSDA_ERROR_NOT_SUPPORTED;
-    int64_t keys = 0;
-    for (int l = 0; l < p->num_levels; ++l) {
-        const int64_t H = p->spatial_shapes[2 * l], W = p->spatial_shapes[2 * l + 1];
-        if (H < 1 || W < 1 || H >= kIndexLimit || W >= kIndexLimit) return MSDA_ERROR_INVALID_VALUE;
-        if (p->level_start_index[l] != keys) return MSDA_ERROR_INVALID_VALUE;
-        keys += H * W;
-        if (keys >= kIndexLimit) return MSDA_ERROR_INVALID_VALUE;
-    }
-    if (keys != p->num_keys) return MSDA_ERROR_INVALID_VALUE;
-    const int64_t pitch = int64_t(p->num_heads) * p->embed_dims;
-    // Per batch, value and output bytes are addressed with 32-bit offsets.
-    if (int64_t(p->num_keys) * pitch * elem_bytes(p->dtype) >= kIndexLimit) return MSDA_ERROR_NOT_SUPPORTED;
-    if (int64_t(p->num_queries) * pitch * elem_bytes(p->dtype) >= kIndexLimit) return MSDA_ERROR_NOT_SUPPORTED;
-    if (int64_t(p->num_queries) * p->num_heads * p->num_levels * p->num_points * 2 >= kIndexLimit)
-        return MSDA_ERROR_NOT_SUPPORTED;
-    return MSDA_SUCCESS;
-}
-
-int64_t value_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_keys * p->num_heads * p->embed_dims;
-}
-int64_t sample_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_queries * p->num_heads * p->num_levels * p->num_points;
-}
-int64_t out_elems(const msda_problem_t* p) {
-    return int64_t(p->batch) * p->num_queries * p->num_heads * p->embed_dims;
-}
-
-int floor_log2(int64_t v) {
-    int s = 0;
-    while ((int64_t(2) << s) <= v) ++s;
-    return s;
-}
-
-// Problem descriptor for the kernels, including the key segments of the
-// binned backward: level l gets segments of 2^shift keys, sized so that a
-// segment receives about 3/4 of a unit's records when the samples spread
-// evenly over the level (two records per sample and level, Q*P samples per
-// level and plane), but never fewer than 32 keys: a denser level spreads a
-// segment over several units (merged with atomics) rather than letting
-// many workers of one unit fold into the same few rows.  A tile of
-// 2^shift keys * D floats stays within 32 KB (16 KB for sparse problems).
-msda::Problem pack(const msda_problem_t* p) {
-    msda::Problem pb;
-    memset(&pb, 0, sizeof(pb));
-    pb.bs = p->batch;
-    pb.K = p->num_keys;
-    pb.M = p->num_heads;
-    pb.D = p->embed_dims;
-    pb.L = p->num_levels;
-    pb.P = p->num_points;
-    pb.Q = p->num_queries;
-    pb.lpr_active = lane_split(p->embed_dims, p->dtype).active;
-    pb.ngroups = int64_t(p->batch) * p->num_queries * p->num_heads;
-    pb.nplanes = p->batch * p->num_heads;
-    // Sparse problems have many short units; they take smaller units and
-    // tiles (16 KB instead of 32 KB), so that more units run per CU.  A
-    // problem is sparse when its largest level gets fewer than one record per
-    // key (two per sample, Q * P samples per level and plane): that level's
-    // segments hold most of the units.
-    int64_t largest = 0;
-    for (int l = 0; l < p->num_levels; ++l)
-        largest = std::max<int64_t>(largest, p->spatial_shapes[2 * l] * p->spatial_shapes[2 * l + 1]);
-    const bool sparse = 2.0 * double(p->num_queries) * p->num_points < double(largest);
-    pb.unit_records = sparse ? msda::kSparseUnitRecords : msda::kUnitRecords;
-    const int max_shift = floor_log2(std::min<int64_t>(msda::kMaxSegKeys, (sparse ? 4096 : 8192) / p->embed_dims));
-    int64_t nseg = 0;
-    for (int l = 0; l < p->num_levels; ++l) {
-        const int64_t H = p->spatial_shapes[2 * l], W = p->spatial_shapes[2 * l + 1];
-        pb.lv.H[l] = static_cast<int32_t>(H);
-        pb.lv.W[l] = static_cast<int32_t>(W);
-        pb.lv.start[l] = static_cast<int32_t>(p->level_start_index[l]);
-        const double per_key = 2.0 * double(p->num_queries) * p->num_points / double(H * W);
-        const double keys = per_key > 0 ? (3 * pb.unit_records / 4) / per_key : double(msda::kMaxSegKeys);
-        int shift = keys >= 1.0 ? floor_log2(static_cast<int64_t>(keys)) : 0;
-        if (shift < 5) shift = 5;
-        if (shift > max_shift) shift = max_shift;
-        pb.seg_shift[l] = shift;
-        pb.seg_base[l] = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
-        nseg += (H * W + (int64_t(1) << shift) - 1) >> shift;
-    }
-    pb.seg_base[p->num_levels] = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
-    pb.nseg = static_cast<int32_t>(std::min<int64_t>(nseg, kIndexLimit - 1));
-    return pb;
-}
-
-// The binned backward needs: query indices within the record's 24-bit
-// field, level extents within the 16-bit cell fields, at most kMaxSegments
-// segments per plane, record positions and unit counts within int32.
-int64_t max_records(const msda_problem_t* p) { return 4 * sample_elems(p); }
-
-// Per plane: at most 4 records per sample, so a fixed region of
-// plane_records; at most one unit per segment plus one per unit_records.
-int64_t plane_records(const msda_problem_t* p) {
-    return 4 * int64_t(p->num_queries) * p->num_levels * p->num_points;
-}
-int64_t plane_units(const msda_problem_t* p, const msda::Problem& pb) {
-    return pb.nseg + (plane_records(p) + pb.unit_records - 1) / pb.unit_records;
-}
-
-bool binned_ok(const msda_problem_t* p, const msda::Problem& pb) {
-    for (int l = 0; l < p->num_levels; ++l)
-        if (p->spatial_shapes[2 * l] > msda::kMaxBinnedExtent || p->spatial_shapes[2 * l + 1] > msda::kMaxBinnedExtent)
-            return false;
-    return p->num_queries < (1 << msda::kQueryBits) && pb.nseg <= msda::kMaxSegments &&
-           max_records(p) < kIndexLimit / 2 && int64_t(pb.nplanes) * plane_units(p, pb) < kIndexLimit / 2;
-}
-
-// ---- workspace layout --------------------------------------------------------
-
-struct Layout {
-    bool binned;
-    size_t counts, cursor, nunits, multi, units, recs, acc, total;
-    int64_t max_units;
-};
-
-size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
-
-Layout layout(const msda_problem_t* p, const msda::Problem& pb) {
-    Layout w;
-    memset(&w, 0, sizeof(w));
-    w.binned = binned_ok(p, pb);
-    size_t off = 0;
-    if (w.binned) {
-        const int64_t nbins = int64_t(pb.nplanes) * pb.nseg;
-        w.max_units = int64_t(pb.nplanes) * plane_units(p, pb);
-        // one histogram row per counting workgroup
-        w.counts = off;
-        if (!fused_count_scan(pb)) off += round_up(nbins * count_chunks(pb) * 4);
-        w.cursor = off;
-        off += round_up(nbins * 4);
-        // [p] units of plane p, [nplanes + p] its multi-unit segments (both
-        // from the scan), [2 nplanes + p] units before plane p and
-        // [3 nplanes] all units (from the gradient kernel)
-        w.nunits = off;
-        off += round_up((size_t(pb.nplanes) * 3 + 1) * 4);
-        w.multi = off;
-        off += round_up(nbins * 4);
-        w.units = off;
-        off += round_up(w.max_units * 16);
-        w.recs = off;
-        off += round_up(max_records(p) * 12);
-    }
-    w.acc = off;
-    if (p->dtype != MSDA_F32) off += round_up(value_elems(p) * 4);
-    w.total = off;
-    return w;
-}
-
 // A device pointer must be non-NULL when its tensor has elements, and
 // 16-byte aligned when non-NULL.
 msda_status_t check_ptr(const void* ptr, int64_t elems) {
     if (elems > 0 && ptr == nullptr) return MSDA_ERROR_INVALID_VALUE;
     if (ptr != nullptr && !aligned16(ptr)) return MSDA_ERROR_MISALIGNED;
     return MSDA_SUCCESS;
-}
-
-int64_t fill_blocks(int64_t n) {
-    const int64_t want = (n + kBlock - 1) / kBlock;
-    return want < 8192 ? (want > 0 ? want : 1) : 8192;
 }
 
 msda_status_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
@@ -336,11 +160,13 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
                             const uint8_t* kmask, const void* loc, const void* w, const void* gout, float* gacc,
                             void* gfinal, void* gloc, void* gw, char* ws, int accumulate, hipEvent_t* ev,
                             hipStream_t st) {
-    const bool narrow16 = !accumulate && problem->dtype != MSDA_F32;
+    // which launches run, and their grids, come from the host plan (checked
+    // on the CPU in the tests)
+    const BackwardPlan plan = plan_backward(problem, accumulate != 0);
     if (sample_elems(problem) == 0) {
         // no samples (Q = 0): grad_value is zero and nothing else is written
         MSDA_TRY(mark(ev, kStageZero, st));
-        if (!accumulate)
+        if (plan.zero_blocks > 0)
             MSDA_TRY(zero_bytes(gfinal, size_t(value_elems(problem)) * (problem->dtype == MSDA_F32 ? 4 : 2), st));
         for (int stage = kStageCount; stage <= kStageNarrow; ++stage) MSDA_TRY(mark(ev, stage, st));
         return MSDA_SUCCESS;
@@ -348,28 +174,29 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
     const msda::Problem pb = pack(problem);
     const Layout lay = layout(problem, pb);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
-    if (!lay.binned) {
+    if (!plan.binned) {
         // Float atomics straight into gacc.
         MSDA_TRY(mark(ev, kStageZero, st));
-        if (!accumulate) MSDA_TRY(zero_bytes(gacc, size_t(value_elems(problem)) * 4, st));
+        if (plan.zero_blocks > 0) MSDA_TRY(zero_bytes(gacc, size_t(value_elems(problem)) * 4, st));
         MSDA_TRY(mark(ev, kStageCount, st));
         MSDA_TRY(mark(ev, kStageScan, st));
         MSDA_TRY(mark(ev, kStageGrad, st));
         MSDA_TRY(gradient(problem->dtype, s, pb, false, ref_dims, value, ref, kmask, loc, w, gout, gacc,
-                                      static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr),
-                                      static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
-                                      gloc, gw, st));
+                          static_cast<uint3*>(nullptr), static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+                          static_cast<const int32_t*>(nullptr), gloc, gw, st));
         MSDA_TRY(mark(ev, kStageAccum, st));
         MSDA_TRY(mark(ev, kStageNarrow, st));
-        if (narrow16) {
+        if (plan.narrow_blocks > 0) {
             const int64_t n8 = value_elems(problem) / 8;
             const void* k = value_dtype(problem->dtype) == MSDA_F16 ? kfn(&msda::msda_narrow_kernel<kF16>)
-                                                       : kfn(&msda::msda_narrow_kernel<kBF16>);
-            MSDA_TRY(launch(k, fill_blocks(n8), kBlock, 0, st, reinterpret_cast<const float4*>(gacc),
+                                                                    : kfn(&msda::msda_narrow_kernel<kBF16>);
+            MSDA_TRY(launch(k, plan.narrow_blocks, kBlock, 0, st, reinterpret_cast<const float4*>(gacc),
                             static_cast<uint4*>(gfinal), n8));
         }
         return MSDA_SUCCESS;
     }
+    // the accumulation reads words only a gradient workgroup writes
+    if (plan.accum_blocks > 0 && plan.grad_blocks < 1) return MSDA_ERROR_INVALID_VALUE;
     int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
     int32_t* nunits = reinterpret_cast<int32_t*>(ws + lay.nunits);
@@ -382,21 +209,18 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
     MSDA_TRY(count_scan(problem->dtype, pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
                         prec, pun, ev, st));
     MSDA_TRY(mark(ev, kStageGrad, st));
-    MSDA_TRY(gradient(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs,
-                                  cursor,
-                                  nunits, static_cast<const int32_t*>(multi), gloc, gw,
-                                  st));
+    MSDA_TRY(gradient(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs, cursor,
+                      nunits, static_cast<const int32_t*>(multi), gloc, gw, st));
     MSDA_TRY(mark(ev, kStageAccum, st));
-    MSDA_TRY(accumulate_rows(problem->dtype, s, pb, lay.max_units, static_cast<int>(plane_units(problem, pb)),
-                                   gout, static_cast<const uint3*>(recs), static_cast<const int32_t*>(nunits),
-                                   static_cast<const int4*>(units), kmask, gacc, narrow16 ? gfinal : nullptr, st));
+    MSDA_TRY(accumulate_rows(problem->dtype, s, pb, plan.accum_blocks, pun, gout, static_cast<const uint3*>(recs),
+                             static_cast<const int32_t*>(nunits), static_cast<const int4*>(units), kmask, gacc,
+                             plan.narrow_blocks > 0 ? gfinal : nullptr, st));
     MSDA_TRY(mark(ev, kStageNarrow, st));
-    if (narrow16) {
+    if (plan.narrow_blocks > 0) {
         const void* k = value_dtype(problem->dtype) == MSDA_F16 ? kfn(&msda::msda_narrow_segments_kernel<kF16>)
-                                                   : kfn(&msda::msda_narrow_segments_kernel<kBF16>);
-        MSDA_TRY(launch(k, int64_t(pb.nplanes) * msda::kNarrowPerPlane, kBlock, 0, st,
-                        static_cast<const float*>(gacc), gfinal, static_cast<const int32_t*>(nunits),
-                        static_cast<const int32_t*>(multi), pb));
+                                                                : kfn(&msda::msda_narrow_segments_kernel<kBF16>);
+        MSDA_TRY(launch(k, plan.narrow_blocks, kBlock, 0, st, static_cast<const float*>(gacc), gfinal,
+                        static_cast<const int32_t*>(nunits), static_cast<const int32_t*>(multi), pb));
     }
     return MSDA_SUCCESS;
 }

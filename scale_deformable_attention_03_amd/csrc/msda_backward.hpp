@@ -62,17 +62,7 @@ namespace msda {
 //   w2    float2: weight of that key's corner and of the next key's corner
 //         (0 when the row's second corner is off the map or in the next
 //         segment), each w * (1-ly or ly) * (1-lx or lx)
-constexpr int kQueryBits = 24;         // queries per plane for the binned path
-constexpr int kMaxSegKeys = 256;       // keys per segment (8-bit key field)
 constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the map
-constexpr int kUnitRecords = 2048;     // records one accumulation unit sorts
-constexpr int kSparseUnitRecords = 512; // the same for sparse problems (fewer than one record per key)
-constexpr int kMaxSegments = 2048;     // segments per plane (LDS histograms)
-constexpr int kMaxWgSamples = 1024;    // samples one gradient workgroup holds
-constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path (16-bit cell fields)
-constexpr int kCountBlock = 512;       // lanes of a counting workgroup
-constexpr int kCountChunk = 4096;      // samples one counting workgroup bins (at least)
-constexpr int kMaxCountChunks = 64;    // counting workgroups (histogram rows) per plane
 
 // Corners of one row that a record covers.
 enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
@@ -341,7 +331,6 @@ __device__ void narrow_segment(const Problem& pb, const float* gacc, void* out, 
 // 16-bit dtypes: the rows of the segments split over several units (the
 // only rows the accumulation leaves in the float32 workspace), rounded into
 // grad_value.  Grid: nplanes * kNarrowPerPlane workgroups.
-constexpr int kNarrowPerPlane = 8;
 
 template <int DT>
 __global__ void __launch_bounds__(kBlock)
@@ -463,7 +452,6 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* _
 // plane, for planes of at most kCountScanSamples samples (a latency-bound
 // size: one launch and no histogram rows in memory).
 constexpr int kCountScanBlock = 1024;
-constexpr int kCountScanSamples = 8192;
 
 template <int DTK, int L_CT, int P_CT, int REF>
 __global__ void __launch_bounds__(kCountScanBlock)

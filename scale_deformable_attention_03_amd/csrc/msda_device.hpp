@@ -12,48 +12,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "msda_types.hpp"
+
 namespace msda {
-
-enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
-
-// Kernel dtype codes: kF32, kF16, kBF16 (every float tensor in that type),
-// or mixed precision: kF16M / kBF16M keep value, output and their gradients
-// in fp16 / bf16 and the per-sample tensors (locations or offsets, weights
-// or logits, reference points, and their gradients) in float32.
-constexpr int kF16M = 3, kBF16M = 4;
-// type of the value-side tensors, and of the per-sample tensors
-constexpr int value_dt(int code) { return code == kF16M ? kF16 : code == kBF16M ? kBF16 : code; }
-constexpr int sample_dt(int code) { return code >= kF16M ? kF32 : code; }
-
-template <int DT> struct Elem;
-template <> struct Elem<kF32> { static constexpr int bytes = 4; };
-template <> struct Elem<kF16> { static constexpr int bytes = 2; };
-template <> struct Elem<kBF16> { static constexpr int bytes = 2; };
-
-constexpr int kMaxLevels = 64;   // L*P <= 64 bounds L
-
-// Level geometry as launch arguments: uniform across the grid, so the
-// compiler keeps the entries it reads in scalar registers.
-struct LevelTable {
-    int32_t H[kMaxLevels];
-    int32_t W[kMaxLevels];
-    int32_t start[kMaxLevels];
-};
-
-struct Problem {
-    int32_t bs, K, M, D, L, P, Q;
-    int32_t lpr_active;      // lanes of a group that own channels
-    int64_t ngroups;         // bs * Q * M
-    LevelTable lv;
-    // Key segments of the binned backward (see msda_backward.hpp): level l
-    // is cut into segments of 2^seg_shift[l] keys, numbered from
-    // seg_base[l] within a (batch, head) plane; seg_base[L] = nseg.
-    int32_t nseg;
-    int32_t nplanes;         // bs * M
-    int32_t unit_records;    // records per accumulation unit (kUnitRecords or kSparseUnitRecords)
-    int32_t seg_shift[kMaxLevels];
-    int32_t seg_base[kMaxLevels + 1];
-};
 
 // ---- per-level table in LDS ------------------------------------------------
 
@@ -358,8 +319,6 @@ __device__ __forceinline__ Cell make_cell(float x, float y, int32_t W, int32_t H
 }
 
 // ---- launch geometry -----------------------------------------------------------
-
-constexpr int kBlock = 256;   // lanes of a full workgroup
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that each XCD walks one contiguous range of tiles: neighbouring

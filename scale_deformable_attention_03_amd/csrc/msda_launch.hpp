@@ -14,6 +14,7 @@
 #include "msda.h"
 #include "msda_backward.hpp"
 #include "msda_forward.hpp"
+#include "msda_plan.hpp"
 
 namespace msda_host {
 
@@ -22,11 +23,7 @@ using msda::kBlock;
 using msda::kF16;
 using msda::kF32;
 
-// Lane split of one group: VECB bytes per lane, LPR lanes (a power of two,
-// at least 4) of which `active` own channels.
-struct LaneSplit {
-    int vecb, lpr, active;
-};
+using msda_plan::LaneSplit;
 
 #define MSDA_TRY(expr)                                  \
     do {                                                \
@@ -51,27 +48,9 @@ msda_status_t launch(const void* kernel, int64_t blocks, int threads, size_t lds
 template <typename K>
 const void* kfn(K* k) { return reinterpret_cast<const void*>(k); }
 
-// Counting: samples per counting workgroup (one histogram row each) and the
-// number of rows per plane; planes of at most kCountScanSamples samples are
-// counted and scanned by one workgroup instead (no rows).  At most
-// kMaxCountChunks rows per plane; workgroups of kCountChunk samples when the
-// plane has at most one segment per scan lane, of twice that otherwise
-// (measured: 4096-sample chunks shorten the encoder's count by 3.7 us for
-// 0.5 us more scan; with 842 segments per plane the fp16 stress workload's
-// scan grew by 6 us for 4 us less count).
-inline int64_t count_chunk(const msda::Problem& pb) {
-    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
-    const int64_t chunk = pb.nseg <= msda::kBlock ? msda::kCountChunk : 2 * msda::kCountChunk;
-    // a multiple of 4 samples: the count loads 2 or 4 consecutive samples at once
-    return (std::max<int64_t>(chunk, (nsamp + msda::kMaxCountChunks - 1) / msda::kMaxCountChunks) + 3) & ~int64_t(3);
-}
-inline int64_t count_chunks(const msda::Problem& pb) {
-    const int64_t nsamp = int64_t(pb.Q) * pb.L * pb.P;
-    return (nsamp + count_chunk(pb) - 1) / count_chunk(pb);
-}
-inline bool fused_count_scan(const msda::Problem& pb) {
-    return int64_t(pb.Q) * pb.L * pb.P <= msda::kCountScanSamples;
-}
+using msda_plan::count_chunk;
+using msda_plan::count_chunks;
+using msda_plan::fused_count_scan;
 
 // Records events[k] (when events is not NULL) on the stream just before
 // backward stage k; stage kStageEnd marks the end of the last stage.

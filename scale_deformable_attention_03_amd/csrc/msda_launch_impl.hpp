@@ -33,23 +33,9 @@ inline bool is_l4p4(const msda::Problem& pb) { return pb.L == 4 && pb.P == 4; }
 // forward gained nothing from it and stays generic)
 inline bool is_l4p16(const msda::Problem& pb) { return pb.L == 4 && pb.P == 16; }
 
-inline int64_t plane_blocks(const msda::Problem& pb, int gpb) {
-    return int64_t(pb.nplanes) * ((pb.Q + gpb - 1) / gpb);
-}
-
-// Queries per workgroup: the full 256 lanes unless the per-sample LDS
-// records would exceed `max_samples` samples per workgroup.  With `shrink`,
-// small problems (fewer than two workgroups per compute unit) take smaller
-// workgroups, down to one wave, so that more compute units share the
-// latency-bound work.
-inline int tile_queries(const msda::Problem& pb, int lpr, int max_samples, bool shrink) {
-    constexpr int64_t kFill = 2 * 256;
-    int gpb = kBlock / lpr;
-    const int cap = max_samples / (pb.L * pb.P);
-    if (gpb > cap) gpb = cap < 1 ? 1 : cap;
-    while (shrink && plane_blocks(pb, gpb) < kFill && gpb * lpr > 64 && gpb % 2 == 0) gpb /= 2;
-    return gpb;
-}
+using msda_plan::grad_tile;
+using msda_plan::plane_blocks;
+using msda_plan::tile_queries;
 
 // Reference-point form of a call: 0 (locations and weights given), 2 or 4
 // (reference points, offsets and logits given; the fused prologue).
@@ -91,9 +77,7 @@ struct Grad {
                              uint3* recs,
                              int32_t* cursor, int32_t* nunits, const int32_t* multi, void* gloc, void* gw,
                              hipStream_t st) {
-        // (the gradient kernel keeps full workgroups: measured, its per-workgroup
-        // cursor reservation makes smaller ones slower on small problems)
-        const int gpb = tile_queries(pb, LPR, msda::kMaxWgSamples, false);
+        const int gpb = grad_tile(pb, LPR);
         const int LP = pb.L * pb.P;
         const int64_t blocks = plane_blocks(pb, gpb);
         size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
