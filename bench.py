@@ -46,7 +46,8 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak
 MALL_BYTES = 256 << 20       # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "scale_deformable_attention_03_amd", "csrc", f)
-                  for f in ("msda_api.hip", "msda_forward.hpp", "msda_backward.hpp", "msda_device.hpp",
+                  for f in ("msda_api.hip", "msda_types.hpp", "msda_plan.hpp", "msda_forward.hpp",
+                            "msda_backward.hpp", "msda_device.hpp",
                             "msda_launch.hpp", "msda_launch_impl.hpp", "msda_kernels_f32.hip",
                             "msda_kernels_f16.hip", "msda_kernels_bf16.hip", "msda_kernels_f16_f32.hip",
                             "msda_kernels_bf16_f32.hip")]
@@ -444,24 +445,71 @@ def device_info(props) -> dict:
     return info
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _query_slice(wl, nq: int):
+    """The first nq queries of every batch of the workload (same value map)."""
+    class Slice:
+        pass
+    sl = Slice()
+    sl.value = wl.value
+    sl.spatial_shapes, sl.level_start_index = wl.spatial_shapes, wl.level_start_index
+    sl.sampling_locations = wl.sampling_locations[:, :nq].contiguous()
+    sl.attention_weights = wl.attention_weights[:, :nq].contiguous()
+    sl.grad_output = wl.grad_output[:, :nq].contiguous()
+    sl.f32 = lambda name: wl.__class__.f32(sl, name)
+    return sl
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
+    """The oracle (float64 scalar C) as it stands, on the host cores: forward
+    and backward timed separately, with all threads on the whole workload and
+    with one thread on a slice of its queries.  About `seconds` of CPU time."""
     import oracle
-    args = (wl.f32("value"), wl.spatial_shapes, wl.level_start_index,
-            wl.f32("sampling_locations"), wl.f32("attention_weights"))
-    g = wl.f32("grad_output")
     cores = oracle.threads(0)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(*args)
-        oracle.backward(*args, g)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
     bs, Q = wl.sampling_locations.shape[:2]
-    return {"value": reps * bs * Q / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} full fwd+bwd passes of the benchmark workload ({bs}x{Q} queries), "
-                      f"{dt:.1f} s, float64 scalar C with OpenMP"}
+
+    def rate(w, fn, nthreads, budget):
+        args = (w.f32("value"), w.spatial_shapes, w.level_start_index,
+                w.f32("sampling_locations"), w.f32("attention_weights"))
+        g = w.f32("grad_output")
+        call = (lambda: oracle.forward(*args, nthreads)) if fn == "fwd" else \
+               (lambda: oracle.backward(*args, g, nthreads))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            call()
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+        nq = w.sampling_locations.shape[0] * w.sampling_locations.shape[1]
+        return reps * nq / dt, reps, dt
+
+    q = seconds / 4
+    fa, fr, _ = rate(wl, "fwd", 0, q)
+    ba, br, _ = rate(wl, "bwd", 0, q)
+    nq1 = max(1, min(Q, 1024))
+    sl = _query_slice(wl, nq1)
+    f1, _, _ = rate(sl, "fwd", 1, q)
+    b1, _, _ = rate(sl, "bwd", 1, q)
+    step_all = 1.0 / (1.0 / fa + 1.0 / ba)
+    step_one = 1.0 / (1.0 / f1 + 1.0 / b1)
+    return {"value": round(step_all, 1), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "fwd_queries_per_s": {"all_threads": round(fa, 1), "one_thread": round(f1, 1)},
+            "bwd_queries_per_s": {"all_threads": round(ba, 1), "one_thread": round(b1, 1)},
+            "one_thread_step_queries_per_s": round(step_one, 1),
+            "sample": f"all {cores} threads: {fr} forward and {br} backward passes over the whole workload "
+                      f"({bs}x{Q} queries); one thread: the first {nq1} queries of each batch, same value map; "
+                      f"~{q:.0f} s each, float64 scalar C (OpenMP); value = fwd+bwd step rate with all threads"}
 
 
 def fused_prologue_leg(wl_core, dev, steps: int, warmup: int, nsets: int) -> dict:
@@ -628,6 +676,189 @@ def module_step_leg(dev, steps: int, warmup: int) -> dict:
             "queries_per_s": round(rows_q / (ms * 1e-3), 1), "linear_gflop_per_step": round(3 * linear_flops / 1e9, 2)}
 
 
+def measure_workload(wl, name: str, dev, steps: int, warmup: int, extras: bool) -> dict:
+    """Time `steps` forward + backward steps of one workload through the C ABI
+    on rotating buffer sets (inputs resident in HBM), then the backward's
+    stages (msda_backward_profile events) and the roofline of the dominant
+    kernel.  With extras: also the warm and graph-replay timings."""
+    import torch
+    from scale_deformable_attention_03_amd import _lib, ops
+
+    bs, K, M, D = wl.value.shape
+    Q, L, P = wl.sampling_locations.shape[1], wl.sampling_locations.shape[3], wl.sampling_locations.shape[4]
+    rows = touched_rows(wl)
+    ab = algorithmic_bytes(wl, rows)
+    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
+
+    # Rotating buffer sets: the sets together exceed twice the Infinity Cache.
+    step_bytes = sum(t.numel() * t.element_size() for t in
+                     (wl.value, wl.sampling_locations, wl.attention_weights, wl.grad_output)) * 2
+    nsets = max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1)
+    nsets = min(nsets, 8)
+    sets = []
+    need_ws = _lib.workspace_bytes(prob)
+    for _ in range(nsets):
+        s = dict(value=wl.value.to(dev), loc=wl.sampling_locations.to(dev), w=wl.attention_weights.to(dev),
+                 g=wl.grad_output.to(dev))
+        s["out"] = torch.empty(bs, Q, M * D, dtype=wl.value.dtype, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["gl"] = torch.empty_like(s["loc"])
+        s["gw"] = torch.empty_like(s["w"])
+        s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
+        s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def fwd(s):
+        p = s["ptr"]
+        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
+
+    def bwd(s):
+        p = s["ptr"]
+        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                      p["ws"] if need_ws else 0, need_ws, sp)
+
+    log(f"[bench] {name}: bs {bs} K {K} Q {Q} M {M} D {D} L {L} P {P} {wl.dtype}; "
+        f"{nsets} buffer sets; warmup {warmup} steps {steps}")
+    for i in range(warmup):
+        fwd(sets[i % nsets])
+        bwd(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s = sets[i % nsets]
+        ev[i][0].record(stream)
+        fwd(s)
+        ev[i][1].record(stream)
+        bwd(s)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    step_us = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e3
+    fwd_us_all = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
+    bwd_us_all = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
+    ms_per_step = wall * 1e3 / steps
+    log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
+        f"bwd {bwd_ms * 1e3:.1f} us")
+
+    out = {}
+    if extras:
+        # warm: the same steps back to back on one buffer set (its working set
+        # may stay in the Infinity Cache between steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fwd(sets[0])
+            bwd(sets[0])
+        torch.cuda.synchronize()
+        out["warm_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / steps, 5)
+
+        # The same steps captured as HIP graphs (one per buffer set) and
+        # replayed: the launches cost no host time, which matters for the
+        # small problems.
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for s_ in sets:
+                fwd(s_)
+                bwd(s_)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for s_ in sets:
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                gsp = torch.cuda.current_stream(dev).cuda_stream
+                p_ = s_["ptr"]
+                _lib.forward(prob, p_["value"], p_["loc"], p_["w"], p_["out"], gsp)
+                _lib.backward(prob, p_["value"], p_["loc"], p_["w"], p_["g"], p_["gv"], p_["gl"], p_["gw"],
+                              p_["ws"] if need_ws else 0, need_ws, gsp)
+            graphs.append(g_)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % nsets].replay()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for i in range(steps):
+            graphs[i % nsets].replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        out["graph_replay_ms_per_step"] = round(ga.elapsed_time(gb) / steps, 5)
+        log(f"[bench] graph replay: {out['graph_replay_ms_per_step'] * 1e3:.1f} us/step")
+        del graphs
+
+    # Per-stage times of msda_backward (HIP events recorded by the library
+    # between its kernels, msda_backward_profile), live, same rotation.
+    hip = ctypes.CDLL("libamdhip64.so.7")     # PyTorch's runtime, already loaded
+    nstage = len(_lib.BACKWARD_STAGES)
+    nk = max(20, steps // 4)
+    evs = []
+    for _ in range(nk):
+        arr = (ctypes.c_void_p * (nstage + 1))()
+        for j in range(nstage + 1):
+            if hip.hipEventCreate(ctypes.byref(arr, j * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        evs.append(arr)
+    for i in range(nk):
+        s = sets[i % nsets]
+        p = s["ptr"]
+        fwd(s)
+        _lib.backward_profile(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                              p["ws"] if need_ws else 0, need_ws, evs[i], sp)
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(nstage)
+    f = ctypes.c_float()
+    for arr in evs:
+        for j in range(nstage):
+            if hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arr[j]), ctypes.c_void_p(arr[j + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            stage_ms[j] += f.value / nk
+        for j in range(nstage + 1):
+            hip.hipEventDestroy(ctypes.c_void_p(arr[j]))
+    stages_us = {n_: round(float(v) * 1e3, 2) for n_, v in zip(_lib.BACKWARD_STAGES, stage_ms)}
+    log(f"[bench] backward stages (us): {stages_us}")
+    del sets
+
+    digest = kernel_digest()
+    kernels = {"msda_forward_kernel": (fwd_ms, ab["fwd"]),
+               "msda_backward_kernel": (stage_ms[3], ab["grad"]),
+               "msda_accumulate_kernel": (stage_ms[4], ab["accum"])}
+    kname = max(kernels, key=lambda k: kernels[k][0])
+    kms, kbytes = kernels[kname]
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = load_traffic(digest, kname, name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kname,
+                "kernel_us": round(kms * 1e3, 2), "algorithmic_bytes_per_launch": kbytes}
+    eff_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    out.update({
+        "workload": name,
+        "dtype": wl.dtype + ("+" + wl.sample_dtype if wl.sample_dtype else ""),
+        "shape": {"batch": bs, "num_queries": Q, "num_keys": K, "num_heads": M, "embed_dims": D,
+                  "num_levels": L, "num_points": P},
+        "ms_per_step": round(ms_per_step, 5),
+        "queries_per_s": round(bs * Q / (ms_per_step * 1e-3), 1),
+        "effective_gbps": round(eff_gbps, 1),
+        "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "step_us_percentiles": percentiles(step_us),
+        "fwd_us_percentiles": percentiles(fwd_us_all),
+        "bwd_us_percentiles": percentiles(bwd_us_all),
+        "fwd_us": round(fwd_ms * 1e3, 2),
+        "bwd_us": round(bwd_ms * 1e3, 2),
+        "bwd_stages_us": stages_us,
+        "algorithmic_bytes_total": ab["total"],
+        "kernel_digest": digest,
+        "roofline": roofline,
+        "ab": ab, "rows": rows, "nsets": nsets,
+    })
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -635,12 +866,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="detr_encoder",
                     choices=["detr_encoder", "large_batch_encoder", "max_constraint", "detr_decoder",
-                             "tiny_single_level", "detr_encoder_bf16_f32"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+                             "detr_decoder_f16", "tiny_single_level", "detr_encoder_bf16_f32"])
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-prologue comparison")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision leg")
     ap.add_argument("--no-module", action="store_true", help="skip the module-step leg")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the large-batch, max-constraint, decoder and tiny workloads' lines")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the gather / atomic-scatter / copy ceiling measurements")
     ap.add_argument("--ingest-profiles", metavar="DIR",
@@ -682,159 +915,14 @@ def main() -> int:
         return 0
 
     wl = W.NAMED[args.workload]()
+    m = measure_workload(wl, args.workload, dev, args.steps, args.warmup, extras=True)
     bs, K, M, D = wl.value.shape
     Q, L, P = wl.sampling_locations.shape[1], wl.sampling_locations.shape[3], wl.sampling_locations.shape[4]
-    rows = touched_rows(wl)
-    ab = algorithmic_bytes(wl, rows)
-    prob, keep = ops.problem_for(wl.value, wl.spatial_shapes, wl.level_start_index, wl.sampling_locations)
-
-    # Rotating buffer sets: the sets together exceed twice the Infinity Cache.
-    step_bytes = sum(t.numel() * t.element_size() for t in
-                     (wl.value, wl.sampling_locations, wl.attention_weights, wl.grad_output)) * 2
-    nsets = max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1)
-    nsets = min(nsets, 8)
-    sets = []
-    need_ws = _lib.workspace_bytes(prob)
-    for _ in range(nsets):
-        s = dict(value=wl.value.to(dev), loc=wl.sampling_locations.to(dev), w=wl.attention_weights.to(dev),
-                 g=wl.grad_output.to(dev))
-        s["out"] = torch.empty(bs, Q, M * D, dtype=wl.value.dtype, device=dev)
-        s["gv"] = torch.empty_like(s["value"])
-        s["gl"] = torch.empty_like(s["loc"])
-        s["gw"] = torch.empty_like(s["w"])
-        s["ws"] = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=dev)
-        s["ptr"] = {k: v.data_ptr() for k, v in s.items() if isinstance(v, torch.Tensor)}
-        sets.append(s)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-
-    def fwd(s):
-        p = s["ptr"]
-        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
-
-    def bwd(s):
-        p = s["ptr"]
-        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
-                      p["ws"] if need_ws else 0, need_ws, sp)
-
-    log(f"[bench] {args.workload}: bs {bs} K {K} Q {Q} M {M} D {D} L {L} P {P} {wl.dtype}; "
-        f"{nsets} buffer sets; warmup {args.warmup} steps {args.steps}")
-    for i in range(args.warmup):
-        fwd(sets[i % nsets])
-        bwd(sets[i % nsets])
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        s = sets[i % nsets]
-        ev[i][0].record(stream)
-        fwd(s)
-        ev[i][1].record(stream)
-        bwd(s)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    step_us = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e3
-    fwd_us_all = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
-    bwd_us_all = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
-    ms_per_step = wall * 1e3 / args.steps
-
-    # warm: the same steps back to back on one buffer set (its working set
-    # may stay in the Infinity Cache between steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        fwd(sets[0])
-        bwd(sets[0])
-    torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    log(f"[bench] timed: {ms_per_step:.4f} ms/step wall; events fwd {fwd_ms * 1e3:.1f} us, "
-        f"bwd {bwd_ms * 1e3:.1f} us")
-
-    # The same steps captured as HIP graphs (one per buffer set) and replayed:
-    # the launches cost no host time, which matters for the small problems.
-    graphs = []
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        for s_ in sets:
-            fwd(s_)
-            bwd(s_)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    for s_ in sets:
-        g_ = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_):
-            gsp = torch.cuda.current_stream(dev).cuda_stream
-            p_ = s_["ptr"]
-            _lib.forward(prob, p_["value"], p_["loc"], p_["w"], p_["out"], gsp)
-            _lib.backward(prob, p_["value"], p_["loc"], p_["w"], p_["g"], p_["gv"], p_["gl"], p_["gw"],
-                          p_["ws"] if need_ws else 0, need_ws, gsp)
-        graphs.append(g_)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % nsets].replay()
-    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ga.record(stream)
-    for i in range(args.steps):
-        graphs[i % nsets].replay()
-    gb.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = ga.elapsed_time(gb) / args.steps
-    log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
-
-    # Per-stage times of msda_backward (HIP events recorded by the library
-    # between its kernels, msda_backward_profile), live, same rotation.
-    hip = ctypes.CDLL("libamdhip64.so.7")     # PyTorch's runtime, already loaded
-    nstage = len(_lib.BACKWARD_STAGES)
-    nk = max(20, args.steps // 4)
-    evs = []
-    for _ in range(nk):
-        arr = (ctypes.c_void_p * (nstage + 1))()
-        for j in range(nstage + 1):
-            if hip.hipEventCreate(ctypes.byref(arr, j * ctypes.sizeof(ctypes.c_void_p))) != 0:
-                raise RuntimeError("hipEventCreate failed")
-        evs.append(arr)
-    for i in range(nk):
-        s = sets[i % nsets]
-        p = s["ptr"]
-        fwd(s)
-        _lib.backward_profile(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
-                              p["ws"] if need_ws else 0, need_ws, evs[i], sp)
-    torch.cuda.synchronize()
-    stage_ms = np.zeros(nstage)
-    f = ctypes.c_float()
-    for arr in evs:
-        for j in range(nstage):
-            if hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arr[j]), ctypes.c_void_p(arr[j + 1])) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            stage_ms[j] += f.value / nk
-        for j in range(nstage + 1):
-            hip.hipEventDestroy(ctypes.c_void_p(arr[j]))
-    stages_us = {name: round(float(v) * 1e3, 2) for name, v in zip(_lib.BACKWARD_STAGES, stage_ms)}
-    log(f"[bench] backward stages (us): {stages_us}")
-
-    digest = kernel_digest()
-    kernels = {"msda_forward_kernel": (fwd_ms, ab["fwd"]),
-               "msda_backward_kernel": (stage_ms[3], ab["grad"]),
-               "msda_accumulate_kernel": (stage_ms[4], ab["accum"])}
-    kname = max(kernels, key=lambda k: kernels[k][0])
-    kms, kbytes = kernels[kname]
-    achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = load_traffic(digest, kname, args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kname,
-                "kernel_us": round(kms * 1e3, 2), "algorithmic_bytes_per_launch": kbytes}
-
-    queries = bs * Q
-    value = queries / (ms_per_step * 1e-3)
-    eff_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    ms_per_step, nsets, ab, rows = m["ms_per_step"], m["nsets"], m["ab"], m["rows"]
+    fwd_ms = m["fwd_us"] * 1e-3
     result = {
         "metric": "MSDeformAttn fwd+bwd queries/s and achieved HBM GB/s (% roofline), DETR encoder",
-        "value": round(value, 1),
+        "value": m["queries_per_s"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -843,28 +931,48 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype + ("+" + wl.sample_dtype if wl.sample_dtype else ""),
+        "dtype": m["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": bs, "num_queries": Q, "num_keys": K,
                    "num_heads": M, "embed_dims": D, "num_levels": L, "num_points": P,
-                   "spatial_shapes": [list(map(int, s)) for s in wl.spatial_shapes],
+                   "spatial_shapes": [list(map(int, s_)) for s_ in wl.spatial_shapes],
                    "buffer_sets": nsets, "parallelism": "single GPU"},
-        "effective_gbps": round(eff_gbps, 1),
-        "pct_hbm_roofline": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
-        "graph_replay_ms_per_step": round(graph_ms, 5),
-        "warm_ms_per_step": round(warm_ms, 5),
-        "step_us_percentiles": percentiles(step_us),
-        "fwd_us_percentiles": percentiles(fwd_us_all),
-        "bwd_us_percentiles": percentiles(bwd_us_all),
-        "fwd_us": round(fwd_ms * 1e3, 2),
-        "bwd_us": round(bwd_ms * 1e3, 2),
-        "bwd_stages_us": stages_us,
+        "effective_gbps": m["effective_gbps"],
+        "pct_hbm_roofline": m["pct_hbm_roofline"],
+        "graph_replay_ms_per_step": m["graph_replay_ms_per_step"],
+        "warm_ms_per_step": m["warm_ms_per_step"],
+        "step_us_percentiles": m["step_us_percentiles"],
+        "fwd_us_percentiles": m["fwd_us_percentiles"],
+        "bwd_us_percentiles": m["bwd_us_percentiles"],
+        "fwd_us": m["fwd_us"],
+        "bwd_us": m["bwd_us"],
+        "bwd_stages_us": m["bwd_stages_us"],
         "algorithmic_bytes": ab,
         "touched_value_rows": rows,
         "device": device_info(props),
-        "kernel_digest": digest,
-        "roofline": roofline,
+        "kernel_digest": m["kernel_digest"],
+        "roofline": m["roofline"],
     }
+    eff_gbps = m["effective_gbps"]
+    del m
+    if args.workload == "detr_encoder" and not args.no_other_workloads:
+        # the large-batch bf16 encoder (the second encoder line, held to the
+        # same target) and the other workloads, each with its own roofline
+        others = {}
+        for name in ("large_batch_encoder", "max_constraint", "detr_decoder", "detr_decoder_f16",
+                     "tiny_single_level"):
+            owl = W.NAMED[name]()
+            om = measure_workload(owl, name, dev, max(10, args.steps), max(3, args.warmup), extras=False)
+            for k in ("ab", "rows", "nsets"):
+                om.pop(k, None)
+            others[name] = om
+            log(f"[bench] {name}: {om['ms_per_step'] * 1e3:.1f} us/step, {om['queries_per_s']:.4g} queries/s, "
+                f"{om['pct_hbm_roofline']:.2f}% of HBM roofline; dominant {om['roofline']['kernel']} "
+                f"frac {om['roofline']['frac']}")
+            del owl
+            torch.cuda.empty_cache()
+        result["large_batch_encoder"] = others.pop("large_batch_encoder")
+        result["other_workloads"] = others
     if not args.no_ceilings:
         result["ceilings"] = ceilings_leg(wl, dev, fwd_ms * 1e3, eff_gbps)
         log(f"[bench] ceilings: {result['ceilings']}")

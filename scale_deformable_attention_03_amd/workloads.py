@@ -255,6 +255,7 @@ NAMED = {
     "tiny_single_level": tiny_single_level,
     "detr_encoder": detr_encoder,
     "detr_decoder": detr_decoder,
+    "detr_decoder_f16": lambda: detr_decoder("f16"),
     "large_batch_encoder": large_batch_encoder,
     "max_constraint": max_constraint,
     # mixed precision: bf16 value side, float32 locations and weights
