@@ -253,6 +253,37 @@ msda_status_t msda_backward_profile(const msda_problem_t *problem,
                                     hipStream_t stream);
 
 /*
+ * msda_backward_noalloc: msda_backward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *   Same arguments, semantics, checks and results as msda_backward, without
+ *   the workspace arguments: the workspace comes from a scratch array of
+ *   msda_backward_noalloc_max_workspace() bytes (64 MiB) that the library
+ *   holds in device memory, one per GPU it runs on, until the process ends.
+ *   The call allocates nothing (no hipMalloc, hipFree or allocating library
+ *   routine).  Its first call on a device looks up that device's copy of the
+ *   array (hipGetSymbolAddress, with the device current); make that first
+ *   call outside any graph capture.
+ *   A problem whose msda_backward_workspace_bytes() exceeds the maximum
+ *   returns MSDA_ERROR_NOT_SUPPORTED before anything is enqueued (use
+ *   msda_backward with a workspace of its own).  The array keeps the last
+ *   call's contents; nothing in it needs to start at zero.
+ *   Calls that overlap on one GPU (on different streams, or from several
+ *   host threads without ordering) share that GPU's array and race: order
+ *   them on one stream.
+ */
+size_t msda_backward_noalloc_max_workspace(void);
+msda_status_t msda_backward_noalloc(const msda_problem_t *problem,
+                                    const void *value,
+                                    const void *sampling_locations,
+                                    const void *attention_weights,
+                                    const void *grad_output,
+                                    void *grad_value,
+                                    void *grad_sampling_locations,
+                                    void *grad_attention_weights,
+                                    hipStream_t stream);
+
+/*
  * Fused prologue: the step that feeds the core in MSDeformAttn.forward
  * ("Deformable DETR walkthrough" (zhangshiyu.com/post/59697), section 2.2.4;
  * the two reference-point forms in sections 2.4.1 and 2.4.2, step 3), done

@@ -20,7 +20,8 @@ STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_S
           3: "MSDA_ERROR_MISALIGNED", 4: "MSDA_ERROR_HIP"}
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
            "msda_backward_accumulate", "msda_backward_profile", "msda_forward_fused",
-           "msda_backward_fused", "msda_status_string", "msda_abi_version")
+           "msda_backward_fused", "msda_status_string", "msda_abi_version",
+           "msda_backward_noalloc", "msda_backward_noalloc_max_workspace")
 BACKWARD_STAGES = ("zero_fill", "count", "scan", "gradient", "accumulate", "narrow")
 
 
@@ -93,6 +94,10 @@ def _load():
     lib.msda_forward_fused.restype = ctypes.c_int
     lib.msda_backward_fused.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward_fused.restype = ctypes.c_int
+    lib.msda_backward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msda_backward_noalloc.restype = ctypes.c_int
+    lib.msda_backward_noalloc_max_workspace.argtypes = []
+    lib.msda_backward_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
@@ -131,6 +136,19 @@ def backward_accumulate(problem: Problem, value: int, loc: int, w: int, gout: in
                                       workspace, workspace_bytes_, stream)
     if st != 0:
         raise MsdaError(st, "msda_backward_accumulate")
+
+
+def backward_noalloc(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,
+                     gw: int, stream: int) -> None:
+    """msda_backward with the library's own scratch memory as its workspace
+    (no allocation; at most noalloc_max_workspace() bytes of workspace)."""
+    st = lib.msda_backward_noalloc(ctypes.byref(problem), value, loc, w, gout, gvalue, gloc, gw, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_noalloc")
+
+
+def noalloc_max_workspace() -> int:
+    return int(lib.msda_backward_noalloc_max_workspace())
 
 
 def backward_profile(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "msda.h"
@@ -250,6 +251,35 @@ msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const v
     return mark(ev, kStageEnd, stream);
 }
 
+// ---- scratch memory of the no-allocation backward ----------------------------
+// msda_backward_noalloc takes its workspace from this file-scope array
+// instead of a caller buffer.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the array's device address on a device comes
+// from hipGetSymbolAddress, taken once per device (with that device current)
+// on the entry point's first call there, and only that address is ever
+// passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`.
+msda_status_t scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSDA_ERROR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MSDA_ERROR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +372,24 @@ msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void
     return backward_into(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value_acc, nullptr, grad_sampling_locations, grad_attention_weights,
                          static_cast<char*>(workspace), 1, nullptr, stream);
+}
+
+size_t msda_backward_noalloc_max_workspace(void) { return kScratchBytes; }
+
+msda_status_t msda_backward_noalloc(const msda_problem_t* problem, const void* value, const void* sampling_locations,
+                                    const void* attention_weights, const void* grad_output, void* grad_value,
+                                    void* grad_sampling_locations, void* grad_attention_weights,
+                                    hipStream_t stream) {
+    MSDA_TRY(check_problem(problem));
+    MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output, grad_value,
+                                 grad_sampling_locations, grad_attention_weights));
+    if (value_elems(problem) == 0) return MSDA_SUCCESS;
+    const size_t need = layout(problem, pack(problem)).total;
+    if (need > kScratchBytes) return MSDA_ERROR_NOT_SUPPORTED;
+    void* ws = nullptr;
+    if (need > 0) MSDA_TRY(scratch_for_current_device(&ws));
+    return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value, grad_sampling_locations, grad_attention_weights, ws, need, nullptr, stream);
 }
 
 }  // extern "C"

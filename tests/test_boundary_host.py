@@ -165,3 +165,17 @@ def test_empty_tensors_may_be_null():
 def test_single_hip_runtime_in_process():
     """libmsda.so must share PyTorch's HIP runtime (one libamdhip64 mapped)."""
     assert len(_lib._hip_runtimes()) == 1, _lib._hip_runtimes()
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """msda_backward_noalloc refuses, before anything is enqueued, a problem
+    whose workspace exceeds its scratch array (the encoder's is over 200 MB)."""
+    lib = _lib.lib
+    assert _lib.noalloc_max_workspace() == 64 << 20
+    p, keep = prob(Q=17821)
+    assert _lib.workspace_bytes(p) > _lib.noalloc_max_workspace()
+    good = 0x10000
+    assert lib.msda_backward_noalloc(ctypes.byref(p), *([good] * 7), None) == UNSUPPORTED
+    bad, keep2 = prob(D=12)
+    assert lib.msda_backward_noalloc(ctypes.byref(bad), *([good] * 7), None) == UNSUPPORTED
+    assert lib.msda_backward_noalloc(ctypes.byref(p), None, *([good] * 6), None) == INVALID
