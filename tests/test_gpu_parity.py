@@ -387,12 +387,18 @@ def test_atomic_fallback_path():
     check_backward(wl, gpu_backward(wl, t))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_accumulate_adds(dtype):
+@pytest.mark.parametrize("dtype,levels,P,Q", [
+    ("f32", [(20, 30), (10, 15)], 4, 90),
+    ("bf16", [(20, 30), (10, 15)], 4, 90),
+    ("f32", [(30, 40), (3, 4)], 8, 3000),      # 4,000 records per key of the 3 x 4 level:
+    ("bf16", [(30, 40), (3, 4)], 8, 3000),     # its segment spans many units
+], ids=["f32", "bf16", "hot_level_f32", "hot_level_bf16"])
+def test_backward_accumulate_adds(dtype, levels, P, Q):
     """msda_backward_accumulate adds grad_value into a float32 buffer: two
-    calls on a pre-filled buffer give prefill + 2 * grad_value."""
+    calls on a pre-filled buffer give prefill + 2 * grad_value (also for a
+    level whose segment is split over many accumulation units)."""
     from scale_deformable_attention_03_amd import _lib, ops
-    wl = W.make("accumulate", 2, [(20, 30), (10, 15)], 4, 32, 4, 90, dtype, seed=8)
+    wl = W.make("accumulate", 2, levels, 4, 32, P, Q, dtype, seed=8)
     t = to_device(wl)
     prob, keep = ops.problem_for(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"])
     need = _lib.workspace_bytes(prob)
