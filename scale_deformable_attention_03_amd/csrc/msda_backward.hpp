@@ -710,13 +710,14 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         const uint32_t lane_b = active ? static_cast<uint32_t>(li * VECB) : kOffMap;
         const uint32_t* rec = srec + lg * gstride;
 
-        float g[VEC];
-        if (active) {
-            widen<DT, VECB>(load_raw<VECB>(static_cast<const char*>(gout) + (G * pb.D + li * VEC) * E), g);
-        } else {
+        // the query's grad_output row: packed (16-bit dtypes, for the dot2
+        // products below) and widened
+        Raw<VECB> graw;
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
-        }
+        for (int i = 0; i < VECB / 4; ++i) graw.w[i] = 0u;
+        if (active) graw = load_raw<VECB>(static_cast<const char*>(gout) + (G * pb.D + li * VEC) * E);
+        float g[VEC];
+        widen<DT, VECB>(graw, g);
         if constexpr (!BINNED) {
             // the query's grad_output row, for the pre-reduction below
             if (active) {
@@ -766,18 +767,31 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     const int lp = c0 + b0 + u;
                     const float4 fr = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);    // lx ly w cell
                     const float4 f = make_float4(1.0f - fr.x, fr.x, 1.0f - fr.y, fr.y);      // hx lx hy ly
-                    float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-                    widen<DT, VECB>(raw[u][0], v00);
-                    widen<DT, VECB>(raw[u][1], v01);
-                    widen<DT, VECB>(raw[u][2], v10);
-                    widen<DT, VECB>(raw[u][3], v11);
                     float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
+                    if constexpr (DT == kF32) {
+                        float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+                        widen<DT, VECB>(raw[u][0], v00);
+                        widen<DT, VECB>(raw[u][1], v01);
+                        widen<DT, VECB>(raw[u][2], v10);
+                        widen<DT, VECB>(raw[u][3], v11);
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) {
-                        d00 += g[i] * v00[i];
-                        d01 += g[i] * v01[i];
-                        d10 += g[i] * v10[i];
-                        d11 += g[i] * v11[i];
+                        for (int i = 0; i < VEC; ++i) {
+                            d00 += g[i] * v00[i];
+                            d01 += g[i] * v01[i];
+                            d10 += g[i] * v10[i];
+                            d11 += g[i] * v11[i];
+                        }
+                    } else {
+                        // 16-bit rows: <g, v> two elements per instruction
+                        // (v_dot2_f32_{f16,bf16}: exact products, float32
+                        // sums), straight from the packed rows
+#pragma unroll
+                        for (int i = 0; i < VECB / 4; ++i) {
+                            d00 = dot2<DT>(raw[u][0].w[i], graw.w[i], d00);
+                            d01 = dot2<DT>(raw[u][1].w[i], graw.w[i], d01);
+                            d10 = dot2<DT>(raw[u][2].w[i], graw.w[i], d10);
+                            d11 = dot2<DT>(raw[u][3].w[i], graw.w[i], d11);
+                        }
                     }
                     const float top = f.x * d00 + f.y * d01;
                     const float bot = f.x * d10 + f.y * d11;

@@ -96,6 +96,19 @@ __device__ __forceinline__ void store_pair(void* base, int64_t i, float a, float
     }
 }
 
+// a.lo * b.lo + a.hi * b.hi + c for two packed 16-bit pairs (fp16 or bf16),
+// float32 result: the products of 16-bit values are exact in float32.
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == kF16) {
+        typedef _Float16 __attribute__((ext_vector_type(2))) h2;
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+    } else {
+        typedef __bf16 __attribute__((ext_vector_type(2))) b2;
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+    }
+}
+
 // ---- vector row slices -------------------------------------------------------
 
 // VECB raw bytes of a row, held in 32-bit words.
