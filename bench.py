@@ -127,40 +127,50 @@ def algorithmic_bytes(wl, rows: int) -> dict:
 
 def load_traffic(digest: str, kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when they were taken on other kernel sources or another workload."""
+    when they were taken on other kernel sources or not for this workload."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    ent = rec.get(kernel, {})
-    if rec.get("kernel_digest") != digest or not isinstance(ent, dict) or ent.get("workload") != workload:
+    if rec.get("kernel_digest") != digest:
         return None
-    return ent.get("hbm_bytes_per_launch")
+    ent = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return ent.get("hbm_bytes_per_launch") if isinstance(ent, dict) else None
 
 
 # The profiling commands whose output --ingest-profiles reads (REPO is the
 # repository root, DIR the directory later handed to --ingest-profiles; run
 # from /tmp with TMPDIR=/tmp).
+_BENCH_ARGS = "--workload WL --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings --no-other-workloads"
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python3 REPO/bench.py --steps 30 --warmup 5 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+             f"python3 REPO/bench.py --steps 30 --warmup 5 {_BENCH_ARGS}",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+             f"python3 REPO/bench.py --steps 4 --warmup 1 {_BENCH_ARGS}",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+             f"python3 REPO/bench.py --steps 4 --warmup 1 {_BENCH_ARGS}",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- "
                   "python3 REPO/bench.py --calibrate-copy",
     "cache": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TA_TA_BUSY_sum TD_TD_BUSY_sum TCP_TOTAL_CACHE_ACCESSES_sum "
              "TCP_TCC_READ_REQ_sum GRBM_GUI_ACTIVE --output-format csv -d DIR/cache -o run -- "
-             "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+             f"python3 REPO/bench.py --steps 4 --warmup 1 {_BENCH_ARGS}",
     "micro_trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/micro_trace -o run -- "
-                   "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module",
+                   "python3 REPO/bench.py --workload WL --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed "
+                   "--no-module --no-other-workloads",
     "sq": "rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE "
           "SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d DIR/sq -o run -- "
-          "python3 REPO/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-fused --no-mixed --no-module --no-ceilings",
+          f"python3 REPO/bench.py --steps 4 --warmup 1 {_BENCH_ARGS}",
 }
+
+
+def profile_command(name: str, workload: str) -> str:
+    """The rocprofv3 command PROFILE_COMMANDS[name] for one workload (REPO,
+    DIR left as placeholders)."""
+    return PROFILE_COMMANDS[name].replace("WL", workload)
+
+
 # MI355X: 256 compute units in 8 XCDs, 4 SIMDs per CU (GRBM_GUI_ACTIVE is
 # summed over the XCDs; TA/TD/TCP counters over the CUs).
 N_XCD, N_CU, N_SIMD = 8, 256, 1024
@@ -231,7 +241,7 @@ def counters_summary(d: str, workload: str, digest: str) -> list:
           "  the LDS-active cycles (SQ_LDS_BANK_CONFLICT, SQ_LDS_ADDR_CONFLICT: same-address atomics);",
           "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of wave lifetime spent waiting).", "",
           "Commands (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
-          f"    {PROFILE_COMMANDS['cache']}", f"    {PROFILE_COMMANDS['sq']}", "",
+          f"    {profile_command('cache', workload)}", f"    {profile_command('sq', workload)}", "",
           "| kernel | waves | cycles | L2 hit | L1 hit | TA busy | TD busy | VALU issue | LDS active | "
           "LDS bank conflict | LDS address conflict | waiting |",
           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -278,22 +288,30 @@ def ingest_profiles(d: str, workload: str) -> None:
     write_scale = COPY_BYTES / (np.mean(cw[kc]) * 1024.0)
     fetch = _counter_csv(os.path.join(d, "fetch"), "FETCH_SIZE")
     write = _counter_csv(os.path.join(d, "write"), "WRITE_SIZE")
-    rec = {"kernel_digest": digest, "workload": workload,
-           "calibration": {"copy_kernel": _short(kc), "copy_bytes": COPY_BYTES,
-                           "fetch_kib": round(float(np.mean(cf[kc])), 1), "fetch_scale": round(fetch_scale, 4),
-                           "write_kib": round(float(np.mean(cw[kc])), 1), "write_scale": round(write_scale, 4)},
-           "commands": {k: PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")}}
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("kernel_digest") != digest or "workloads" not in rec:
+        rec = {"kernel_digest": digest, "workloads": {}}
+    rec["calibration"] = {"copy_kernel": _short(kc), "copy_bytes": COPY_BYTES,
+                          "fetch_kib": round(float(np.mean(cf[kc])), 1), "fetch_scale": round(fetch_scale, 4),
+                          "write_kib": round(float(np.mean(cw[kc])), 1), "write_scale": round(write_scale, 4)}
+    rec["commands"] = {k: PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch", "copy_write")}
+    rec["commands"]["note"] = "WL: the workload's name (--workload)"
     rows = []
+    ents = {}
     for k in sorted(set(fetch) | set(write)):
         if "msda" not in k:
             continue
         f_kib = float(np.mean(fetch.get(k, [0.0])))
         w_kib = float(np.mean(write.get(k, [0.0])))
         hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
-        ent = {"workload": workload, "dispatches": len(fetch.get(k, [])), "fetch_kib": round(f_kib, 1),
+        ent = {"dispatches": len(fetch.get(k, [])), "fetch_kib": round(f_kib, 1),
                "write_kib": round(w_kib, 1), "hbm_bytes_per_launch": int(round(hbm))}
-        rec.setdefault(_short(k), ent)
+        ents.setdefault(_short(k), ent)
         rows.append((_short(k), k, ent))
+    rec["workloads"][workload] = ents
     json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
     md = [f"# HBM traffic per launch, msda kernels, workload {workload}", "",
           f"Kernel sources digest {digest}. FETCH_SIZE / WRITE_SIZE are rocprofv3 per-dispatch",
@@ -303,7 +321,7 @@ def ingest_profiles(d: str, workload: str) -> None:
           f"WRITE_SIZE read {rec['calibration']['write_kib']} KiB -> scale {write_scale:.4f}.",
           "The counters see traffic between L2 and the memory side (Infinity Cache included).", "",
           "Commands (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", ""]
-    md += [f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    md += [f"    {profile_command(k, workload)}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
     md += ["", "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes per launch (scaled) |",
            "|---|---|---|---|---|"]
     for short, _, e in rows:
@@ -317,7 +335,7 @@ def ingest_profiles(d: str, workload: str) -> None:
               f"Kernel sources digest {digest}. rocprofv3 --stats over a short bench run",
               "(30 timed + 5 warm-up steps, plus the per-stage profiling pass).", "",
               "Command (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
-              f"    {PROFILE_COMMANDS['trace']}", "",
+              f"    {profile_command('trace', workload)}", "",
               "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
         for r in csv.DictReader(open(stats[0])):
             ns = {k: float(r.get(k) or "nan") for k in ("AverageNs", "MinNs", "MaxNs", "Percentage")}
@@ -332,7 +350,7 @@ def ingest_profiles(d: str, workload: str) -> None:
               "libmsda_micro.so on the workload's own corner rows (gather: loads only, then with FMAs;",
               "scatter: lanes on adjacent addresses, then 16 bytes apart), beside the core's kernels.", "",
               "Command (REPO = repository root, DIR = output directory; run from /tmp, TMPDIR=/tmp):", "",
-              f"    {PROFILE_COMMANDS['micro_trace']}", "",
+              f"    {profile_command('micro_trace', workload)}", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
         for r in csv.DictReader(open(stats[0])):
             name = r.get("Name", "?")
