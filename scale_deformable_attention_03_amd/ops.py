@@ -45,6 +45,8 @@ host (a device copy is fetched once per call, which synchronises).
 """
 from __future__ import annotations
 
+import weakref
+
 import numpy as np
 import torch
 
@@ -67,10 +69,28 @@ def dtype_code(value_dtype, sample_dtype) -> int:
                     "(one type for all, or float16/bfloat16 values with float32 per-sample tensors)")
 
 
+# Host copies of device shape tensors (spatial_shapes, level_start_index):
+# copying one to the host synchronises the device, so each tensor is copied
+# once and the copy kept, keyed by the tensor object (a weak reference, so a
+# new tensor at a reused address never hits) and its version counter (an
+# in-place change invalidates the copy).
+_HOST_COPIES: dict = {}
+_HOST_COPIES_MAX = 64
+
+
 def _host_int64(x) -> np.ndarray:
     if isinstance(x, torch.Tensor):
-        x = x.detach().to("cpu")
-        return np.ascontiguousarray(x.numpy().astype(np.int64, copy=False))
+        if x.device.type != "cpu":
+            ent = _HOST_COPIES.get(id(x))
+            if ent is not None and ent[0]() is x and ent[1] == x._version:
+                return ent[2]
+        host = np.ascontiguousarray(x.detach().to("cpu").numpy().astype(np.int64, copy=False))
+        if x.device.type != "cpu":
+            host.setflags(write=False)
+            if len(_HOST_COPIES) >= _HOST_COPIES_MAX:
+                _HOST_COPIES.clear()
+            _HOST_COPIES[id(x)] = (weakref.ref(x), x._version, host)
+        return host
     return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
 
 

@@ -416,3 +416,18 @@ def test_backward_accumulate_adds(dtype, levels, P, Q):
     rtol, arms, atol = TOL[("f32", "bwd")] if dtype == "f32" else TOL[(dtype, "bwd")]
     assert_close("accumulate/grad_value", f64(acc), 0.25 + 2 * rgv, rtol, arms, atol)
     assert_close("accumulate/grad_w", f64(gw), rgw, *TOL[(dtype, "bwd")])
+
+
+def test_device_shape_tensors_copied_to_host_once():
+    """Device spatial_shapes / level_start_index are copied to the host once
+    per tensor (the copy synchronises the device) and reused; an in-place
+    change of the tensor, or a new tensor, is copied afresh."""
+    from scale_deformable_attention_03_amd import ops
+    t = torch.tensor([[100, 134], [50, 67]], dtype=torch.int64, device="cuda")
+    a = ops._host_int64(t)
+    assert ops._host_int64(t) is a
+    t.mul_(1)                                        # bumps the version counter
+    b = ops._host_int64(t)
+    assert b is not a and np.array_equal(a, b)
+    u = torch.tensor([[7, 9], [3, 4]], dtype=torch.int64, device="cuda")
+    assert np.array_equal(ops._host_int64(u), [[7, 9], [3, 4]])
