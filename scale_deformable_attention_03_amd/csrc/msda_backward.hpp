@@ -895,26 +895,51 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         __syncthreads();
         // records, from the prologue's cell and weights in LDS, at base + a
         // slot taken from the segment's cursor
+        // Samples are walked point-major: consecutive lanes take consecutive
+        // queries at one (level, point), whose records mostly fall in one
+        // segment and take consecutive slots there.  A sample's (at most
+        // four) records are formed first, then their slots are taken
+        // together and the records stored.
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-            const int g = i / LP, lp = i - g * LP, l = lp / P;
+            const int lp = i / t.gcount, g = i - lp * t.gcount, l = lp / P;
             const uint32_t* r = srec + g * gstride + lp * 8;
             const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
             const uint32_t cell = __float_as_uint(fr.w);
             if (cell == kNoCell) continue;
             const int4 lv = s_lv[l];
-            const int H = lv.x, W = lv.y;
+            const int H = lv.x, W = lv.y, shift = lv.w & 0xff, segbase = lv.w >> 8;
+            const int x0 = static_cast<int>(cell & 0xffffu) - 1, y0 = static_cast<int>(cell >> 16) - 1;
+            const bool lin = x0 >= 0, rin = x0 + 1 < W;
             const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
             const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
             const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
-            for_each_record(static_cast<int>(cell & 0xffffu) - 1, static_cast<int>(cell >> 16) - 1, W, H,
-                            lv.w & 0xff, lv.w >> 8, [&](int seg, int key, int row, int mode) {
-                                const float wy = row ? wy1 : wy0;
-                                const float cl = wy * hx, cr = wy * fr.x;
-                                const int pos = lbase[seg] + atomicAdd(&lhist[seg], 1);
-                                recs[pos] = make_uint3(qk | static_cast<uint32_t>(key),
-                                                       __float_as_uint(mode == kRightOnly ? cr : cl),
-                                                       __float_as_uint(mode == kBoth ? cr : 0.0f));
-                            });
+            const int kmask = (1 << shift) - 1;
+            int seg[4], pos[4];
+            uint3 rec[4];
+            bool valid[4];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int yc = y0 + rr;
+                const bool rowok = yc >= 0 && yc < H;
+                const int kl = yc * W + x0, kr = kl + 1;
+                const bool split = lin && rin && (kl >> shift) != (kr >> shift);
+                const float wy = rr ? wy1 : wy0;
+                const float cl = wy * hx, cr = wy * fr.x;
+                const int k1 = lin ? kl : kr;
+                valid[2 * rr] = rowok;
+                seg[2 * rr] = segbase + (k1 >> shift);
+                rec[2 * rr] = make_uint3(qk | static_cast<uint32_t>(k1 & kmask), __float_as_uint(lin ? cl : cr),
+                                         __float_as_uint(lin && rin && !split ? cr : 0.0f));
+                valid[2 * rr + 1] = rowok && split;
+                seg[2 * rr + 1] = segbase + (kr >> shift);
+                rec[2 * rr + 1] = make_uint3(qk | static_cast<uint32_t>(kr & kmask), __float_as_uint(cr), 0u);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (valid[k]) pos[k] = lbase[seg[k]] + atomicAdd(&lhist[seg[k]], 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (valid[k]) recs[pos[k]] = rec[k];
         }
         // workgroup 0 also lays the planes' units out in one dense order for
         // the accumulation: units before each plane, and their total
@@ -1128,7 +1153,10 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
             for (int j = 0; j < kBatch; ++j) {
                 bkey[j] = static_cast<int>(rr[j] & 0xffu);
                 bw[j] = ww[j];
-                graw[j] = buffer_load<VECB>(gr, (rr[j] >> 8) * qstride + lane_b);
+                // (24-bit products are exact here: query indices are below
+                // 2^24, the row pitch M * D * E below 2^14, and the byte
+                // offset below 2^31)
+                graw[j] = buffer_load<VECB>(gr, __umul24(rr[j] >> 8, qstride) + lane_b);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
