@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the MSDeformAttn core, forward + backward, on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-msda_forward followed by msda_backward (zero-fill, gradient kernel and, for
-16-bit dtypes, the float32 -> dtype conversion), both through the C ABI on
-torch's current stream.  Inputs are resident in HBM before timing starts.
+A step is one pass of the whole hot path over one batch of synthetic input,
+as a training step runs it: msda_forward_train (the forward, which also
+counts the backward's records per key segment) followed by
+msda_backward_counted (scan, gradient kernel, accumulation and, for 16-bit
+dtypes, the float32 -> dtype conversion of split segments), both through the
+C ABI on torch's current stream.  Inputs are resident in HBM before timing
+starts.
 To keep the 256 MB Infinity Cache from serving a whole step's working set,
 steps rotate over several identical copies of every buffer.
 
@@ -630,9 +633,9 @@ def mixed_precision_leg(dev, steps: int, warmup: int, nsets: int) -> dict:
 
     def step(s):
         p = s["ptr"]
-        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
-        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
-                      p["ws"] if need_ws else 0, need_ws, sp)
+        _lib.forward_train(prob, p["value"], p["loc"], p["w"], p["out"], p["ws"] if need_ws else 0, need_ws, sp)
+        _lib.backward_counted(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                              p["ws"] if need_ws else 0, need_ws, sp)
 
     for i in range(warmup):
         step(sets[i % nsets])
@@ -728,14 +731,15 @@ def measure_workload(wl, name: str, dev, steps: int, warmup: int, extras: bool) 
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
+    # the training pair: the forward also counts the backward's records
     def fwd(s):
         p = s["ptr"]
-        _lib.forward(prob, p["value"], p["loc"], p["w"], p["out"], sp)
+        _lib.forward_train(prob, p["value"], p["loc"], p["w"], p["out"], p["ws"] if need_ws else 0, need_ws, sp)
 
     def bwd(s):
         p = s["ptr"]
-        _lib.backward(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
-                      p["ws"] if need_ws else 0, need_ws, sp)
+        _lib.backward_counted(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                              p["ws"] if need_ws else 0, need_ws, sp)
 
     log(f"[bench] {name}: bs {bs} K {K} Q {Q} M {M} D {D} L {L} P {P} {wl.dtype}; "
         f"{nsets} buffer sets; warmup {warmup} steps {steps}")
@@ -793,9 +797,10 @@ def measure_workload(wl, name: str, dev, steps: int, warmup: int, extras: bool) 
             with torch.cuda.graph(g_):
                 gsp = torch.cuda.current_stream(dev).cuda_stream
                 p_ = s_["ptr"]
-                _lib.forward(prob, p_["value"], p_["loc"], p_["w"], p_["out"], gsp)
-                _lib.backward(prob, p_["value"], p_["loc"], p_["w"], p_["g"], p_["gv"], p_["gl"], p_["gw"],
-                              p_["ws"] if need_ws else 0, need_ws, gsp)
+                _lib.forward_train(prob, p_["value"], p_["loc"], p_["w"], p_["out"], p_["ws"] if need_ws else 0,
+                                   need_ws, gsp)
+                _lib.backward_counted(prob, p_["value"], p_["loc"], p_["w"], p_["g"], p_["gv"], p_["gl"],
+                                      p_["gw"], p_["ws"] if need_ws else 0, need_ws, gsp)
             graphs.append(g_)
         torch.cuda.synchronize()
         for i in range(warmup):
@@ -810,8 +815,8 @@ def measure_workload(wl, name: str, dev, steps: int, warmup: int, extras: bool) 
         log(f"[bench] graph replay: {out['graph_replay_ms_per_step'] * 1e3:.1f} us/step")
         del graphs
 
-    # Per-stage times of msda_backward (HIP events recorded by the library
-    # between its kernels, msda_backward_profile), live, same rotation.
+    # Per-stage times of the backward (HIP events recorded by the library
+    # between its kernels, msda_backward_counted_profile), live, same rotation.
     hip = ctypes.CDLL("libamdhip64.so.7")     # PyTorch's runtime, already loaded
     nstage = len(_lib.BACKWARD_STAGES)
     nk = max(20, steps // 4)
@@ -826,8 +831,8 @@ def measure_workload(wl, name: str, dev, steps: int, warmup: int, extras: bool) 
         s = sets[i % nsets]
         p = s["ptr"]
         fwd(s)
-        _lib.backward_profile(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
-                              p["ws"] if need_ws else 0, need_ws, evs[i], sp)
+        _lib.backward_counted_profile(prob, p["value"], p["loc"], p["w"], p["g"], p["gv"], p["gl"], p["gw"],
+                                      p["ws"] if need_ws else 0, need_ws, evs[i], sp)
     torch.cuda.synchronize()
     stage_ms = np.zeros(nstage)
     f = ctypes.c_float()
@@ -954,7 +959,8 @@ def main() -> int:
         "config": {"workload": args.workload, "batch": bs, "num_queries": Q, "num_keys": K,
                    "num_heads": M, "embed_dims": D, "num_levels": L, "num_points": P,
                    "spatial_shapes": [list(map(int, s_)) for s_ in wl.spatial_shapes],
-                   "buffer_sets": nsets, "parallelism": "single GPU"},
+                   "buffer_sets": nsets, "parallelism": "single GPU",
+                   "step": "msda_forward_train + msda_backward_counted"},
         "effective_gbps": m["effective_gbps"],
         "pct_hbm_roofline": m["pct_hbm_roofline"],
         "graph_replay_ms_per_step": m["graph_replay_ms_per_step"],

@@ -198,6 +198,55 @@ msda_status_t msda_backward(const msda_problem_t *problem,
                             hipStream_t stream);
 
 /*
+ * msda_forward_train: msda_forward for a training step, which also does the
+ * backward's first pass.  The binned backward starts by counting each
+ * sample's records per key segment from the sampling locations alone
+ * (histogram rows in the workspace); this forward computes every sample's
+ * bilinear cell anyway ("Deformable DETR walkthrough" section 2.2.4,
+ * ms_deform_attn_core_pytorch: the grid_sample of each level), so it counts
+ * them there and leaves the rows in `workspace` for msda_backward_counted.
+ *   Arguments as msda_forward, plus workspace / workspace_bytes as for
+ *   msda_backward (the same size, msda_backward_workspace_bytes).  The output
+ *   is the one msda_forward writes, bit for bit.  Enqueues a kernel that
+ *   zeroes the histogram rows, then the forward, on `stream`.  Problems whose
+ *   backward counts and scans in one launch (at most 8192 samples per
+ *   (batch, head)) or falls back to float atomics get a plain forward; their
+ *   msda_backward_counted is then msda_backward.
+ *   Errors: as msda_forward, and MSDA_ERROR_INVALID_VALUE for a missing or
+ *   short workspace (checked before anything is enqueued).
+ */
+msda_status_t msda_forward_train(const msda_problem_t *problem,
+                                 const void *value,
+                                 const void *sampling_locations,
+                                 const void *attention_weights,
+                                 void *output,
+                                 void *workspace,
+                                 size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * msda_backward_counted: msda_backward after msda_forward_train, without
+ * the counting pass.
+ *   Arguments, results and errors as msda_backward.  Precondition: a
+ *   msda_forward_train with the same problem and the same
+ *   sampling_locations contents was enqueued on this workspace, and nothing
+ *   else used the workspace in between (the histogram rows it left are read
+ *   here; with other locations the records would overflow their segments'
+ *   ranges).  Same workspace ownership rules as msda_backward.
+ */
+msda_status_t msda_backward_counted(const msda_problem_t *problem,
+                                    const void *value,
+                                    const void *sampling_locations,
+                                    const void *attention_weights,
+                                    const void *grad_output,
+                                    void *grad_value,
+                                    void *grad_sampling_locations,
+                                    void *grad_attention_weights,
+                                    void *workspace,
+                                    size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
  * msda_backward_accumulate: msda_backward, adding grad_value into a float32
  * buffer instead of overwriting it.
  *   grad_value_acc (device, float32, laid out like value whatever the
@@ -251,6 +300,25 @@ msda_status_t msda_backward_profile(const msda_problem_t *problem,
                                     size_t workspace_bytes,
                                     hipEvent_t *stage_events,
                                     hipStream_t stream);
+
+/*
+ * msda_backward_counted_profile: msda_backward_counted with the stage events
+ * of msda_backward_profile (measurement only).  Stage 1 (count) has no
+ * kernel where msda_forward_train counted; otherwise as
+ * msda_backward_profile, with msda_backward_counted's precondition.
+ */
+msda_status_t msda_backward_counted_profile(const msda_problem_t *problem,
+                                            const void *value,
+                                            const void *sampling_locations,
+                                            const void *attention_weights,
+                                            const void *grad_output,
+                                            void *grad_value,
+                                            void *grad_sampling_locations,
+                                            void *grad_attention_weights,
+                                            void *workspace,
+                                            size_t workspace_bytes,
+                                            hipEvent_t *stage_events,
+                                            hipStream_t stream);
 
 /*
  * msda_backward_noalloc: msda_backward for callers that cannot allocate

@@ -21,7 +21,8 @@ STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_S
 EXPORTS = ("msda_validate", "msda_forward", "msda_backward_workspace_bytes", "msda_backward",
            "msda_backward_accumulate", "msda_backward_profile", "msda_forward_fused",
            "msda_backward_fused", "msda_status_string", "msda_abi_version",
-           "msda_backward_noalloc", "msda_backward_noalloc_max_workspace")
+           "msda_backward_noalloc", "msda_backward_noalloc_max_workspace", "msda_forward_train",
+           "msda_backward_counted", "msda_backward_counted_profile")
 BACKWARD_STAGES = ("zero_fill", "count", "scan", "gradient", "accumulate", "narrow")
 
 
@@ -98,6 +99,12 @@ def _load():
     lib.msda_backward_noalloc.restype = ctypes.c_int
     lib.msda_backward_noalloc_max_workspace.argtypes = []
     lib.msda_backward_noalloc_max_workspace.restype = ctypes.c_size_t
+    lib.msda_forward_train.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msda_forward_train.restype = ctypes.c_int
+    lib.msda_backward_counted.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.msda_backward_counted.restype = ctypes.c_int
+    lib.msda_backward_counted_profile.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.msda_backward_counted_profile.restype = ctypes.c_int
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
@@ -130,6 +137,24 @@ def backward(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: 
         raise MsdaError(st, "msda_backward")
 
 
+def forward_train(problem: Problem, value: int, loc: int, w: int, out: int, workspace: int,
+                  workspace_bytes_: int, stream: int) -> None:
+    """msda_forward that also counts the backward's records into the
+    workspace, for a following backward_counted on the same workspace."""
+    st = lib.msda_forward_train(ctypes.byref(problem), value, loc, w, out, workspace, workspace_bytes_, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_forward_train")
+
+
+def backward_counted(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,
+                     gw: int, workspace: int, workspace_bytes_: int, stream: int) -> None:
+    """msda_backward after forward_train on the same locations and workspace."""
+    st = lib.msda_backward_counted(ctypes.byref(problem), value, loc, w, gout, gvalue, gloc, gw,
+                                   workspace, workspace_bytes_, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_counted")
+
+
 def backward_accumulate(problem: Problem, value: int, loc: int, w: int, gout: int, gacc: int,
                         gloc: int, gw: int, workspace: int, workspace_bytes_: int, stream: int) -> None:
     st = lib.msda_backward_accumulate(ctypes.byref(problem), value, loc, w, gout, gacc, gloc, gw,
@@ -159,6 +184,15 @@ def backward_profile(problem: Problem, value: int, loc: int, w: int, gout: int, 
                                    workspace, workspace_bytes_, events, stream)
     if st != 0:
         raise MsdaError(st, "msda_backward_profile")
+
+
+def backward_counted_profile(problem: Problem, value: int, loc: int, w: int, gout: int, gvalue: int, gloc: int,
+                             gw: int, workspace: int, workspace_bytes_: int, events, stream: int) -> None:
+    """backward_counted with the stage events of backward_profile."""
+    st = lib.msda_backward_counted_profile(ctypes.byref(problem), value, loc, w, gout, gvalue, gloc, gw,
+                                           workspace, workspace_bytes_, events, stream)
+    if st != 0:
+        raise MsdaError(st, "msda_backward_counted_profile")
 
 
 def forward_fused(problem: Problem, ref_dims: int, value: int, mask: int, ref: int, off: int, logits: int,

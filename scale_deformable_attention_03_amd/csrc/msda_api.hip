@@ -25,8 +25,10 @@ using msda::kF32;
 using msda_host::kfn;
 using msda_plan::BackwardPlan;
 using msda_plan::check_problem;
+using msda_plan::count_chunks;
 using msda_plan::elem_bytes;
 using msda_plan::fill_blocks;
+using msda_plan::fused_count_scan;
 using msda_plan::lane_split;
 using msda_plan::LaneSplit;
 using msda_plan::Layout;
@@ -85,9 +87,20 @@ msda_status_t check_ref(const msda_problem_t* p, int ref_dims, const void* ref) 
     return check_ptr(ref, int64_t(p->batch) * p->num_queries * p->num_levels * ref_dims);
 }
 
+// Whether a counting forward fills the backward's histogram rows: binned
+// problems with samples whose planes are counted apart from the scan (small
+// planes count and scan in one launch inside the backward).
+bool forward_counts(const msda_problem_t* problem, const msda::Problem& pb) {
+    return sample_elems(problem) > 0 && value_elems(problem) > 0 && layout(problem, pb).binned &&
+           !fused_count_scan(pb);
+}
+
+// The forward.  ws != null (plain form only): also count the backward's
+// records into the workspace's histogram rows (zeroed first), for a
+// following msda_backward_counted on the same workspace.
 msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
                            const uint8_t* kmask, const void* sampling_locations, const void* attention_weights,
-                           void* output, hipStream_t stream) {
+                           void* output, char* ws, hipStream_t stream) {
     MSDA_TRY(check_problem(problem));
     MSDA_TRY(check_ref(problem, ref_dims, ref));
     MSDA_TRY(check_ptr(value, value_elems(problem)));
@@ -97,9 +110,18 @@ msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const vo
     if (out_elems(problem) == 0) return MSDA_SUCCESS;
     const msda::Problem pb = pack(problem);
     const LaneSplit s = lane_split(problem->embed_dims, problem->dtype);
+    int32_t* counts = nullptr;
+    int nchunks = 0;
+    if (ws != nullptr && ref_dims == 0 && forward_counts(problem, pb)) {
+        const Layout lay = layout(problem, pb);
+        counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+        nchunks = static_cast<int>(count_chunks(pb));
+        // (the rows' region is padded to 256 bytes: zeroed whole, in 16-byte words)
+        MSDA_TRY(zero_bytes(counts, msda_plan::round_up(size_t(pb.nplanes) * pb.nseg * nchunks * 4), stream));
+    }
     return by_code(problem->dtype, [&](auto c) {
         return Launch<decltype(c)::value>::forward(s, pb, ref_dims, value, ref, kmask, sampling_locations,
-                                                   attention_weights, output, stream);
+                                                   attention_weights, output, counts, nchunks, stream);
     });
 }
 
@@ -142,10 +164,11 @@ msda_status_t accumulate_rows(msda_dtype_t dt, const LaneSplit& s, const msda::P
 
 msda_status_t count_scan(msda_dtype_t dt, const msda::Problem& pb, int ref_dims, const void* ref,
                          const void* loc, int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi,
-                         int4* units, int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
+                         int4* units, int accumulate, int plane_recs, int plane_us, bool counted, hipEvent_t* ev,
+                         hipStream_t st) {
     return by_code(dt, [&](auto c) {
         return Launch<decltype(c)::value>::count_scan(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units,
-                                                      accumulate, plane_recs, plane_us, ev, st);
+                                                      accumulate, plane_recs, plane_us, counted, ev, st);
     });
 }
 
@@ -156,11 +179,12 @@ msda_status_t count_scan(msda_dtype_t dt, const msda::Problem& pb, int ref_dims,
 // holds only rows the kernels add into (and is rounded into gfinal at the
 // end).
 // ref_dims != 0: the fused prologue (loc and w are the offsets and logits,
-// gloc and gw receive their gradients).
+// gloc and gw receive their gradients).  counted: a counting forward on the
+// same locations filled the histogram rows (see forward_counts).
 msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const void* value, const void* ref,
                             const uint8_t* kmask, const void* loc, const void* w, const void* gout, float* gacc,
-                            void* gfinal, void* gloc, void* gw, char* ws, int accumulate, hipEvent_t* ev,
-                            hipStream_t st) {
+                            void* gfinal, void* gloc, void* gw, char* ws, int accumulate, bool counted,
+                            hipEvent_t* ev, hipStream_t st) {
     // which launches run, and their grids, come from the host plan (checked
     // on the CPU in the tests)
     const BackwardPlan plan = plan_backward(problem, accumulate != 0);
@@ -208,7 +232,7 @@ msda_status_t backward_into(const msda_problem_t* problem, int ref_dims, const v
     MSDA_TRY(mark(ev, kStageZero, st));             // no zero fill on this path
     const int prec = static_cast<int>(plane_records(problem)), pun = static_cast<int>(plane_units(problem, pb));
     MSDA_TRY(count_scan(problem->dtype, pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                        prec, pun, ev, st));
+                        prec, pun, counted && ref_dims == 0 && forward_counts(problem, pb), ev, st));
     MSDA_TRY(mark(ev, kStageGrad, st));
     MSDA_TRY(gradient(problem->dtype, s, pb, true, ref_dims, value, ref, kmask, loc, w, gout, gacc, recs, cursor,
                       nunits, static_cast<const int32_t*>(multi), gloc, gw, st));
@@ -230,7 +254,7 @@ msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const v
                             const uint8_t* kmask, const void* sampling_locations, const void* attention_weights,
                             const void* grad_output, void* grad_value, void* grad_sampling_locations,
                             void* grad_attention_weights, void* workspace, size_t workspace_bytes, hipEvent_t* ev,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool counted = false) {
     MSDA_TRY(check_problem(problem));
     MSDA_TRY(check_ref(problem, ref_dims, ref));
     MSDA_TRY(check_backward_ptrs(problem, value, sampling_locations, attention_weights, grad_output,
@@ -247,7 +271,8 @@ msda_status_t backward_call(const msda_problem_t* problem, int ref_dims, const v
     float* gacc = problem->dtype == MSDA_F32 ? static_cast<float*>(grad_value)
                                              : reinterpret_cast<float*>(ws + lay.acc);
     MSDA_TRY(backward_into(problem, ref_dims, value, ref, kmask, sampling_locations, attention_weights, grad_output,
-                           gacc, grad_value, grad_sampling_locations, grad_attention_weights, ws, 0, ev, stream));
+                           gacc, grad_value, grad_sampling_locations, grad_attention_weights, ws, 0, counted, ev,
+                           stream));
     return mark(ev, kStageEnd, stream);
 }
 
@@ -302,7 +327,21 @@ const char* msda_status_string(msda_status_t status) {
 msda_status_t msda_forward(const msda_problem_t* problem, const void* value,
                            const void* sampling_locations, const void* attention_weights,
                            void* output, hipStream_t stream) {
-    return forward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, output, stream);
+    return forward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, output, nullptr,
+                        stream);
+}
+
+msda_status_t msda_forward_train(const msda_problem_t* problem, const void* value, const void* sampling_locations,
+                                 const void* attention_weights, void* output, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    MSDA_TRY(check_problem(problem));
+    const size_t need = value_elems(problem) == 0 ? 0 : layout(problem, pack(problem)).total;
+    if (need > 0) {
+        if (workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
+        MSDA_TRY(check_ptr(workspace, 1));
+    }
+    return forward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, output,
+                        need > 0 ? static_cast<char*>(workspace) : nullptr, stream);
 }
 
 msda_status_t msda_forward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
@@ -311,7 +350,7 @@ msda_status_t msda_forward_fused(const msda_problem_t* problem, int32_t ref_dims
                                  hipStream_t stream) {
     if (ref_dims != 2 && ref_dims != 4) return MSDA_ERROR_INVALID_VALUE;
     return forward_call(problem, ref_dims, value, reference_points, key_padding_mask, sampling_offsets,
-                        attention_logits, output, stream);
+                        attention_logits, output, nullptr, stream);
 }
 
 size_t msda_backward_workspace_bytes(const msda_problem_t* problem) {
@@ -328,6 +367,16 @@ msda_status_t msda_backward(const msda_problem_t* problem, const void* value,
     return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
                          nullptr, stream);
+}
+
+msda_status_t msda_backward_counted(const msda_problem_t* problem, const void* value,
+                                    const void* sampling_locations, const void* attention_weights,
+                                    const void* grad_output, void* grad_value,
+                                    void* grad_sampling_locations, void* grad_attention_weights,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
+                         nullptr, stream, true);
 }
 
 msda_status_t msda_backward_fused(const msda_problem_t* problem, int32_t ref_dims, const void* value,
@@ -355,6 +404,18 @@ msda_status_t msda_backward_profile(const msda_problem_t* problem, const void* v
                          stage_events, stream);
 }
 
+msda_status_t msda_backward_counted_profile(const msda_problem_t* problem, const void* value,
+                                            const void* sampling_locations, const void* attention_weights,
+                                            const void* grad_output, void* grad_value,
+                                            void* grad_sampling_locations, void* grad_attention_weights,
+                                            void* workspace, size_t workspace_bytes, hipEvent_t* stage_events,
+                                            hipStream_t stream) {
+    if (stage_events == nullptr) return MSDA_ERROR_INVALID_VALUE;
+    return backward_call(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
+                         grad_value, grad_sampling_locations, grad_attention_weights, workspace, workspace_bytes,
+                         stage_events, stream, true);
+}
+
 msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void* value,
                                        const void* sampling_locations, const void* attention_weights,
                                        const void* grad_output, float* grad_value_acc,
@@ -371,7 +432,7 @@ msda_status_t msda_backward_accumulate(const msda_problem_t* problem, const void
     if (value_elems(problem) == 0) return MSDA_SUCCESS;
     return backward_into(problem, 0, value, nullptr, nullptr, sampling_locations, attention_weights, grad_output,
                          grad_value_acc, nullptr, grad_sampling_locations, grad_attention_weights,
-                         static_cast<char*>(workspace), 1, nullptr, stream);
+                         static_cast<char*>(workspace), 1, false, nullptr, stream);
 }
 
 size_t msda_backward_noalloc_max_workspace(void) { return kScratchBytes; }

@@ -55,49 +55,6 @@
 
 namespace msda {
 
-// ---- records -----------------------------------------------------------------
-// A record is one image row (y0 or y0 + 1) of one sample's bilinear cell,
-// restricted to the row's in-map corners of one segment:
-//   key   u32: query index << 8 | key of its first corner within the segment
-//   w2    float2: weight of that key's corner and of the next key's corner
-//         (0 when the row's second corner is off the map or in the next
-//         segment), each w * (1-ly or ly) * (1-lx or lx)
-constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the map
-
-// Corners of one row that a record covers.
-enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
-
-// Enumerate the records of a valid sample whose cell starts at (x0, y0) on
-// a W x H level (-1 <= x0 < W, -1 <= y0 < H): for each of the rows y0,
-// y0 + 1 that lie on the map, the in-map corners of that row.  A pair whose
-// two corners fall in different segments is split in two records.
-// emit(segment, key within segment, row 0/1, mode).
-template <typename Emit>
-__device__ __forceinline__ void for_each_record(int x0, int y0, int W, int H, int shift, int segbase,
-                                                Emit&& emit) {
-    const int mask = (1 << shift) - 1;
-    const bool lin = x0 >= 0, rin = x0 + 1 < W;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int yc = y0 + r;
-        if (yc < 0 || yc >= H) continue;
-        const int kl = yc * W + x0;    // left corner key (meaningful when lin)
-        const int kr = kl + 1;         // right corner key
-        if (lin && rin) {
-            if ((kl >> shift) == (kr >> shift)) {
-                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kBoth));
-            } else {
-                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
-                emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
-            }
-        } else if (lin) {
-            emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
-        } else {
-            emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
-        }
-    }
-}
-
 // Level of plane-local segment `seg`.
 __device__ __forceinline__ int level_of_segment(const Problem& pb, int seg) {
     int l = 0;
@@ -428,8 +385,13 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* _
     __shared__ int32_t s_cnt[kMaxSegments];
     __shared__ int32_t s_wrec[kScanBlock / 64], s_wunit[kScanBlock / 64];
     __shared__ int32_t s_nmulti;
+    __shared__ unsigned long long s_total;
     const int pl = blockIdx.x, n = pb.nseg;
-    if (threadIdx.x == 0) s_nmulti = 0;
+    if (threadIdx.x == 0) {
+        s_nmulti = 0;
+        s_total = 0;
+    }
+    __syncthreads();
     const int32_t* rows = counts + static_cast<int64_t>(pl) * nchunks * n;
     // lanes per segment: 4, 2 or 1, as many as the workgroup holds; a
     // segment's lanes are adjacent (same wave, same trip count)
@@ -441,9 +403,24 @@ msda_bin_scan_kernel(const int32_t* __restrict__ counts, int nchunks, int32_t* _
         for (int c = part; c < nchunks; c += parts) sum += rows[static_cast<int64_t>(c) * n + i];
         if (parts >= 2) sum += __shfl_xor(sum, 1, 64);
         if (parts >= 4) sum += __shfl_xor(sum, 2, 64);
-        if (part == 0) s_cnt[i] = sum;
+        if (part == 0) {
+            // rows that a counting forward left are trusted only as far as
+            // they fit the plane's fixed regions (see below)
+            sum = min(max(sum, 0), plane_records);
+            s_cnt[i] = sum;
+            atomicAdd(&s_total, static_cast<unsigned long long>(sum));
+        }
     }
     __syncthreads();
+    // Counts that exceed the plane's record region cannot come from the
+    // plane's own samples (a counting forward on other locations, or rows
+    // never written): they are dropped, so that every cursor and unit stays
+    // within the plane's regions.  The backward's results are then wrong,
+    // but no access leaves the workspace.
+    if (s_total > static_cast<unsigned long long>(plane_records)) {
+        for (int i = threadIdx.x; i < n; i += kScanBlock) s_cnt[i] = 0;
+        __syncthreads();
+    }
     scan_plane<kScanBlock>(s_cnt, s_wrec, s_wunit, &s_nmulti, cursor, nunits, multi, units, accumulate, pb, pl,
                            plane_records, plane_units);
 }
@@ -895,6 +872,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         __syncthreads();
         // records, from the prologue's cell and weights in LDS, at base + a
         // slot taken from the segment's cursor
+        const int64_t plane_end = (static_cast<int64_t>(t.pl) + 1) * 4 * pb.Q * LP;
         // Samples are walked point-major: consecutive lanes take consecutive
         // queries at one (level, point), whose records mostly fall in one
         // segment and take consecutive slots there.  A sample's (at most
@@ -937,9 +915,11 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if (valid[k]) pos[k] = lbase[seg[k]] + atomicAdd(&lhist[seg[k]], 1);
+            // (positions past the plane's record region arise only from
+            // counts of other locations, see msda_bin_scan_kernel: dropped)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                if (valid[k]) recs[pos[k]] = rec[k];
+                if (valid[k] && pos[k] < plane_end) recs[pos[k]] = rec[k];
         }
         // workgroup 0 also lays the planes' units out in one dense order for
         // the accumulation: units before each plane, and their total

@@ -368,4 +368,47 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// ---- records -----------------------------------------------------------------
+// A record is one image row (y0 or y0 + 1) of one sample's bilinear cell,
+// restricted to the row's in-map corners of one segment:
+//   key   u32: query index << 8 | key of its first corner within the segment
+//   w2    float2: weight of that key's corner and of the next key's corner
+//         (0 when the row's second corner is off the map or in the next
+//         segment), each w * (1-ly or ly) * (1-lx or lx)
+constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the map
+
+// Corners of one row that a record covers.
+enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
+
+// Enumerate the records of a valid sample whose cell starts at (x0, y0) on
+// a W x H level (-1 <= x0 < W, -1 <= y0 < H): for each of the rows y0,
+// y0 + 1 that lie on the map, the in-map corners of that row.  A pair whose
+// two corners fall in different segments is split in two records.
+// emit(segment, key within segment, row 0/1, mode).
+template <typename Emit>
+__device__ __forceinline__ void for_each_record(int x0, int y0, int W, int H, int shift, int segbase,
+                                                Emit&& emit) {
+    const int mask = (1 << shift) - 1;
+    const bool lin = x0 >= 0, rin = x0 + 1 < W;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int yc = y0 + r;
+        if (yc < 0 || yc >= H) continue;
+        const int kl = yc * W + x0;    // left corner key (meaningful when lin)
+        const int kr = kl + 1;         // right corner key
+        if (lin && rin) {
+            if ((kl >> shift) == (kr >> shift)) {
+                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kBoth));
+            } else {
+                emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
+                emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
+            }
+        } else if (lin) {
+            emit(segbase + (kl >> shift), kl & mask, r, static_cast<int>(kLeftOnly));
+        } else {
+            emit(segbase + (kr >> shift), kr & mask, r, static_cast<int>(kRightOnly));
+        }
+    }
+}
+
 }  // namespace msda

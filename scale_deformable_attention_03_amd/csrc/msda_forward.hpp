@@ -106,16 +106,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value,
 }
 
 // Grid: nplanes * ceil(Q / gpb) workgroups of gpb * LPR lanes.
-// LDS: gpb * (8 * L * P + 4) words, plus 2 * gpb * L * P when REF != 0.
+// LDS: gpb * (8 * L * P + 4) words, plus 2 * gpb * L * P when REF != 0, plus
+// nseg words when CNT.
 // REF = 0: loc and attw are the sampling locations and attention weights;
 // REF = 2 or 4: they are the sampling offsets and attention logits, and ref
 // holds the reference points (see sample_location).  kmask: [bs, K] key
 // padding bytes or null (see mask_corners).
-template <int DTK, int VECB, int LPR, int L_CT, int P_CT, int REF>
+// CNT (plain form only): the workgroup also counts its samples' backward
+// records per segment (the binned backward's counting pass, done here from
+// the cells the prologue computes anyway) and adds its counts into row
+// (query tile mod nchunks) of its plane's histogram rows `counts`, which the
+// caller zeroed.
+template <int DTK, int VECB, int LPR, int L_CT, int P_CT, int REF, bool CNT>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,
                     const void* __restrict__ attw, const void* __restrict__ ref,
-                    const uint8_t* __restrict__ kmask, void* __restrict__ out, Problem pb, int gpb) {
+                    const uint8_t* __restrict__ kmask, void* __restrict__ out, Problem pb, int gpb,
+                    int32_t* __restrict__ counts, int nchunks) {
+    static_assert(!CNT || REF == 0, "counting is built for the plain form");
     constexpr int DT = value_dt(DTK), ST = sample_dt(DTK);
     constexpr int E = Elem<DT>::bytes;
     constexpr int VEC = VECB / E;
@@ -132,7 +140,10 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
     // fused prologue: the workgroup's logits and their exponentials
     float* sv = reinterpret_cast<float*>(sm + gpb * gstride);
     float* se = sv + gpb * LP;
+    int32_t* lhist = reinterpret_cast<int32_t*>(sm + gpb * gstride);   // CNT: records per segment
     if constexpr (REF != 0) load_logits<ST>(attw, t.G0, pb.M, t.gcount, LP, sv);
+    if constexpr (CNT)
+        for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) lhist[i] = 0;
     __syncthreads();
     if constexpr (REF != 0) {
         exp_logits(t.gcount, LP, sv, se);
@@ -152,6 +163,11 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         uint32_t* r = sm + g * gstride + lp * 8;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
         *reinterpret_cast<float4*>(r + 4) = make_float4(wy0 * c.hx, wy0 * c.lx, wy1 * c.hx, wy1 * c.lx);
+        if constexpr (CNT) {
+            if (c.ok)
+                for_each_record(c.x0, c.y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
+                                [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
+        }
     };
     if constexpr (kPrologueSamples<ST, REF, L_CT, P_CT> > 1) {
         // S samples of one group per lane: their locations in one 16-byte
@@ -182,6 +198,13 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         }
     }
     __syncthreads();
+    if constexpr (CNT) {
+        int32_t* row = counts + (static_cast<int64_t>(t.pl) * nchunks + (t.q0 / gpb) % nchunks) * pb.nseg;
+        for (int i = threadIdx.x; i < pb.nseg; i += blockDim.x) {
+            const int v = lhist[i];
+            if (v != 0) atomicAdd(row + i, v);
+        }
+    }
 
     const int lg = threadIdx.x / LPR, li = threadIdx.x % LPR;
     if (lg >= t.gcount || li >= pb.lpr_active) return;

@@ -69,7 +69,7 @@ template <int DT>
 struct Launch {
     static msda_status_t forward(const LaneSplit& s, const msda::Problem& pb, int ref_dims, const void* v,
                                  const void* ref, const uint8_t* kmask, const void* loc, const void* w, void* out,
-                                 hipStream_t st);
+                                 int32_t* counts, int nchunks, hipStream_t st);
     static msda_status_t gradient(const LaneSplit& s, const msda::Problem& pb, bool binned, int ref_dims,
                                   const void* v, const void* ref, const uint8_t* kmask, const void* loc,
                                   const void* w, const void* gout, float* gacc, uint3* recs, int32_t* cursor,
@@ -79,7 +79,8 @@ struct Launch {
                                     const uint8_t* kmask, float* gacc, void* gfinal, hipStream_t st);
     static msda_status_t count_scan(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
                                     int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
-                                    int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st);
+                                    int accumulate, int plane_recs, int plane_us, bool counted, hipEvent_t* ev,
+                                    hipStream_t st);
 };
 
 extern template struct Launch<kF32>;

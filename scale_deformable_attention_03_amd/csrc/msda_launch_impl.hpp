@@ -39,10 +39,10 @@ using msda_plan::tile_queries;
 
 // Reference-point form of a call: 0 (locations and weights given), 2 or 4
 // (reference points, offsets and logits given; the fused prologue).
-template <int DT, int VECB, int LPR, int REF>
+template <int DT, int VECB, int LPR, int REF, bool CNT = false>
 const void* fwd_kernel(const msda::Problem& pb) {
-    return is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4, REF>)
-                       : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0, REF>);
+    return is_l4p4(pb) ? kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 4, 4, REF, CNT>)
+                       : kfn(&msda::msda_forward_kernel<DT, VECB, LPR, 0, 0, REF, CNT>);
 }
 
 template <int DT, int VECB, int LPR, bool BINNED, int REF>
@@ -58,15 +58,22 @@ inline size_t fused_lds(int ref_dims, int gpb, int LP) { return ref_dims ? sizeo
 
 template <int DT, int VECB, int LPR>
 struct Fwd {
+    // counts != null (plain form only): the forward also counts the
+    // backward's records into the zeroed histogram rows `counts`
     static msda_status_t run(const msda::Problem& pb, int ref_dims, const void* v, const void* ref,
-                             const uint8_t* kmask, const void* loc, const void* w, void* out, hipStream_t st) {
+                             const uint8_t* kmask, const void* loc, const void* w, void* out, int32_t* counts,
+                             int nchunks, hipStream_t st) {
+        if (counts != nullptr && ref_dims != 0) return MSDA_ERROR_INVALID_VALUE;
         const int gpb = tile_queries(pb, LPR, 1024, true);
         const int LP = pb.L * pb.P;
-        const size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
-        const void* k = ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
-                        : ref_dims == 2 ? fwd_kernel<DT, VECB, LPR, 2>(pb)
-                                        : fwd_kernel<DT, VECB, LPR, 4>(pb);
-        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, kmask, out, pb, gpb);
+        size_t lds = sizeof(uint32_t) * gpb * (8 * LP + 4) + fused_lds(ref_dims, gpb, LP);
+        if (counts != nullptr) lds += sizeof(int32_t) * size_t(pb.nseg);
+        const void* k = counts != nullptr ? fwd_kernel<DT, VECB, LPR, 0, true>(pb)
+                        : ref_dims == 0   ? fwd_kernel<DT, VECB, LPR, 0>(pb)
+                        : ref_dims == 2   ? fwd_kernel<DT, VECB, LPR, 2>(pb)
+                                          : fwd_kernel<DT, VECB, LPR, 4>(pb);
+        return launch(k, plane_blocks(pb, gpb), gpb * LPR, lds, st, v, loc, w, ref, kmask, out, pb, gpb, counts,
+                      nchunks);
     }
 };
 
@@ -139,10 +146,13 @@ const void* count_scan_kernel(const msda::Problem& pb) {
 // Count records per segment and scan the counts into ranges, cursors and
 // units: one fused launch for small planes, else count (histogram rows) and
 // scan.  Events: the count stage before, the scan stage between.
+// counted: the histogram rows were filled by a counting forward (not for
+// small planes, which count and scan in one launch), so only the scan runs.
 template <int DT>
 msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
                                 int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
-                                int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
+                                int accumulate, int plane_recs, int plane_us, bool counted, hipEvent_t* ev,
+                                hipStream_t st) {
     MSDA_TRY(mark(ev, kStageCount, st));
     if (fused_count_scan(pb)) {
         const void* k = ref_dims == 0   ? count_scan_kernel<DT, 0>(pb)
@@ -153,12 +163,13 @@ msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const voi
         return mark(ev, kStageScan, st);
     }
     const int64_t chunks = count_chunks(pb);
-    const void* k = ref_dims == 0   ? count_kernel<DT, 0>(pb)
-                    : ref_dims == 2 ? count_kernel<DT, 2>(pb)
-                                    : count_kernel<DT, 4>(pb);
-    MSDA_TRY(launch(k, int64_t(pb.nplanes) * chunks, msda::kCountBlock, sizeof(int32_t) * pb.nseg, st, loc, ref,
-                    counts, pb,
-                    static_cast<int>(count_chunk(pb))));
+    if (!counted) {
+        const void* k = ref_dims == 0   ? count_kernel<DT, 0>(pb)
+                        : ref_dims == 2 ? count_kernel<DT, 2>(pb)
+                                        : count_kernel<DT, 4>(pb);
+        MSDA_TRY(launch(k, int64_t(pb.nplanes) * chunks, msda::kCountBlock, sizeof(int32_t) * pb.nseg, st, loc,
+                        ref, counts, pb, static_cast<int>(count_chunk(pb))));
+    }
     MSDA_TRY(mark(ev, kStageScan, st));
     return launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kScanBlock, 0, st,
                   static_cast<const int32_t*>(counts), static_cast<int>(chunks), cursor, nunits, multi, units,
@@ -170,8 +181,8 @@ msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const voi
 template <int DT>
 msda_status_t Launch<DT>::forward(const LaneSplit& s, const msda::Problem& pb, int ref_dims, const void* v,
                                   const void* ref, const uint8_t* kmask, const void* loc, const void* w, void* out,
-                                  hipStream_t st) {
-    return by_split<DT, Fwd>(s, pb, ref_dims, v, ref, kmask, loc, w, out, st);
+                                  int32_t* counts, int nchunks, hipStream_t st) {
+    return by_split<DT, Fwd>(s, pb, ref_dims, v, ref, kmask, loc, w, out, counts, nchunks, st);
 }
 
 template <int DT>
@@ -212,9 +223,10 @@ msda_status_t Launch<DT>::accumulate(const LaneSplit& s, const msda::Problem& pb
 template <int DT>
 msda_status_t Launch<DT>::count_scan(const msda::Problem& pb, int ref_dims, const void* ref, const void* loc,
                                      int32_t* counts, int32_t* cursor, int32_t* nunits, int32_t* multi, int4* units,
-                                     int accumulate, int plane_recs, int plane_us, hipEvent_t* ev, hipStream_t st) {
+                                     int accumulate, int plane_recs, int plane_us, bool counted, hipEvent_t* ev,
+                                     hipStream_t st) {
     return count_scan_launch<DT>(pb, ref_dims, ref, loc, counts, cursor, nunits, multi, units, accumulate,
-                                 plane_recs, plane_us, ev, st);
+                                 plane_recs, plane_us, counted, ev, st);
 }
 
 }  // namespace msda_host

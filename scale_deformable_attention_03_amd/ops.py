@@ -146,10 +146,36 @@ def forward(value, spatial_shapes, level_start_index, sampling_locations, attent
     return out
 
 
+def forward_train(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """One msda_forward_train call on the current stream: the forward, which
+    also leaves the backward's record counts in the workspace.  Returns
+    (output, workspace); pass that workspace to backward(..., counted=True)
+    with the same locations."""
+    prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
+    dev, dt, st = value.device, value.dtype, sampling_locations.dtype
+    bs, K, M, D = value.shape
+    _, Q, _, L, P, _ = sampling_locations.shape
+    _check(value, "value", dt, dev)
+    _check(sampling_locations, "sampling_locations", st, dev)
+    _check(attention_weights, "attention_weights", st, dev, (bs, Q, M, L, P))
+    if out is None:
+        out = torch.empty((bs, Q, M * D), dtype=dt, device=dev)
+    _check(out, "output", dt, dev, (bs, Q, M * D))
+    need = _lib.workspace_bytes(prob)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _lib.forward_train(prob, value.data_ptr(), sampling_locations.data_ptr(), attention_weights.data_ptr(),
+                       out.data_ptr(), workspace.data_ptr() if need > 0 else 0, need, _stream(dev))
+    return out, workspace
+
+
 def backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
-             grad_output, grads=None, workspace: torch.Tensor | None = None):
+             grad_output, grads=None, workspace: torch.Tensor | None = None, counted: bool = False):
     """One msda_backward call on the current stream; returns
-    (grad_value, grad_sampling_locations, grad_attention_weights)."""
+    (grad_value, grad_sampling_locations, grad_attention_weights).  With
+    counted=True it is msda_backward_counted on the workspace that
+    forward_train returned for the same locations."""
     prob, keep = problem_for(value, spatial_shapes, level_start_index, sampling_locations)
     dev, dt, st = value.device, value.dtype, sampling_locations.dtype
     bs, K, M, D = value.shape
@@ -167,22 +193,32 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations, atten
     _check(gw, "grad_attention_weights", st, dev, attention_weights.shape)
     need = _lib.workspace_bytes(prob)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        if counted:
+            raise ValueError("backward(counted=True) needs the workspace forward_train returned")
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if (need > 0) else 0
-    _lib.backward(prob, value.data_ptr(), sampling_locations.data_ptr(),
-                  attention_weights.data_ptr(), grad_output.data_ptr(), gv.data_ptr(),
-                  gl.data_ptr(), gw.data_ptr(), ws_ptr, need, _stream(dev))
+    call = _lib.backward_counted if counted else _lib.backward
+    call(prob, value.data_ptr(), sampling_locations.data_ptr(), attention_weights.data_ptr(),
+         grad_output.data_ptr(), gv.data_ptr(), gl.data_ptr(), gw.data_ptr(), ws_ptr, need, _stream(dev))
     return gv, gl, gw
 
 
 class MSDeformAttnFunction(torch.autograd.Function):
-    """Autograd wrapper: forward = msda_forward, backward = msda_backward."""
+    """Autograd wrapper.  When a gradient is wanted, forward =
+    msda_forward_train and backward = msda_backward_counted on the workspace
+    the forward filled (held from the forward to the backward; the saved
+    locations cannot change in between: autograd checks their version);
+    otherwise forward = msda_forward."""
 
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
         shapes = _host_int64(spatial_shapes)
         starts = _host_int64(level_start_index)
-        out = forward(value, shapes, starts, sampling_locations, attention_weights)
+        ctx.workspace = None
+        if any(ctx.needs_input_grad):
+            out, ctx.workspace = forward_train(value, shapes, starts, sampling_locations, attention_weights)
+        else:
+            out = forward(value, shapes, starts, sampling_locations, attention_weights)
         ctx.save_for_backward(value, sampling_locations, attention_weights)
         ctx.host_shapes = (shapes, starts)
         return out
@@ -191,7 +227,9 @@ class MSDeformAttnFunction(torch.autograd.Function):
     def backward(ctx, grad_output):
         value, loc, w = ctx.saved_tensors
         shapes, starts = ctx.host_shapes
-        gv, gl, gw = backward(value, shapes, starts, loc, w, grad_output.contiguous())
+        counted = ctx.workspace is not None
+        gv, gl, gw = backward(value, shapes, starts, loc, w, grad_output.contiguous(), workspace=ctx.workspace,
+                              counted=counted)
         return gv, None, None, gl, gw
 
 
