@@ -179,3 +179,31 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     bad, keep2 = prob(D=12)
     assert lib.msda_backward_noalloc(ctypes.byref(bad), *([good] * 7), None) == UNSUPPORTED
     assert lib.msda_backward_noalloc(ctypes.byref(p), None, *([good] * 6), None) == INVALID
+
+
+def test_training_pair_checks_return_before_launch():
+    """msda_forward_train checks its workspace like the backward (missing,
+    short, misaligned) and msda_backward_counted has msda_backward's checks,
+    all before anything is enqueued."""
+    lib = _lib.lib
+    good = 0x10000
+    p, keep = prob(dtype=0)
+    need = _lib.workspace_bytes(p)
+    assert need > 0
+    ft = lib.msda_forward_train
+    assert ft(ctypes.byref(p), good, good, good, good, None, need, None) == INVALID        # no workspace
+    assert ft(ctypes.byref(p), good, good, good, good, good, need - 16, None) == INVALID   # too small
+    assert ft(ctypes.byref(p), good, good, good, good, good + 2, need, None) == MISALIGNED
+    assert ft(ctypes.byref(p), None, good, good, good, good, need, None) == INVALID
+    assert ft(ctypes.byref(p), good, good, good + 4, good, good, need, None) == MISALIGNED
+    bad, keep2 = prob(D=12)
+    assert ft(ctypes.byref(bad), good, good, good, good, good, need, None) == UNSUPPORTED
+    args = [good] * 7
+    bc = lib.msda_backward_counted
+    assert bc(ctypes.byref(p), *args, None, need, None) == INVALID
+    assert bc(ctypes.byref(p), *args, good, need - 16, None) == INVALID
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert bc(ctypes.byref(p), *a, good, need, None) == INVALID, i
+    assert lib.msda_backward_counted_profile(ctypes.byref(p), *args, good, need, None, None) == INVALID  # no events
