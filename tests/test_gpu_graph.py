@@ -25,11 +25,15 @@ CASES = [
     ("decoder_bf16_f32", lambda: W.detr_decoder("bf16", sample_dtype="f32")),
     ("small_dense_f16", lambda: W.make("graph_dense", 2, [(6, 7), (3, 4)], 4, 32, 4, 400, "f16", seed=81)),
     ("fallback_f32", lambda: W.make("graph_fallback", 1, [(1, 600000)], 1, 8, 1, 64, "f32", seed=82)),
+    # more than 8192 samples per (batch, head): counted apart from the scan
+    ("counted_planes_f32", lambda: W.make("graph_counted", 1, [(40, 56), (20, 28), (10, 14), (5, 7)], 2, 32, 4, 700,
+                                          "f32", seed=83)),
 ]
 
 
+@pytest.mark.parametrize("counted", [False, True], ids=["plain", "training_pair"])
 @pytest.mark.parametrize("make", [c[1] for c in CASES], ids=[c[0] for c in CASES])
-def test_graph_replays_match_eager(make):
+def test_graph_replays_match_eager(make, counted):
     wl = make()
     print(f"[gpu] graph {wl.name}", flush=True)
     dev = torch.device("cuda")
@@ -42,8 +46,12 @@ def test_graph_replays_match_eager(make):
     grads = (torch.empty_like(v), torch.empty_like(loc), torch.empty_like(w))
 
     def step():
-        ops.forward(v, wl.spatial_shapes, wl.level_start_index, loc, w, out=out)
-        ops.backward(v, wl.spatial_shapes, wl.level_start_index, loc, w, g, grads=grads, workspace=ws)
+        if counted:      # msda_forward_train + msda_backward_counted (zero kernel, no memset node)
+            ops.forward_train(v, wl.spatial_shapes, wl.level_start_index, loc, w, out=out, workspace=ws)
+        else:
+            ops.forward(v, wl.spatial_shapes, wl.level_start_index, loc, w, out=out)
+        ops.backward(v, wl.spatial_shapes, wl.level_start_index, loc, w, g, grads=grads, workspace=ws,
+                     counted=counted)
 
     step()
     torch.cuda.synchronize()
