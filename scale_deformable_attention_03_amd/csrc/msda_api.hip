@@ -115,7 +115,7 @@ msda_status_t forward_call(const msda_problem_t* problem, int ref_dims, const vo
     if (ws != nullptr && ref_dims == 0 && forward_counts(problem, pb)) {
         const Layout lay = layout(problem, pb);
         counts = reinterpret_cast<int32_t*>(ws + lay.counts);
-        nchunks = static_cast<int>(count_chunks(pb));
+        nchunks = msda::kForwardCountRows;
         // (the rows' region is padded to 256 bytes: zeroed whole, in 16-byte words)
         MSDA_TRY(zero_bytes(counts, msda_plan::round_up(size_t(pb.nplanes) * pb.nseg * nchunks * 4), stream));
     }

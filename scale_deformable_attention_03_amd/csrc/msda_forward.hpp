@@ -115,8 +115,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_plane(const void* value,
 // CNT (plain form only): the workgroup also counts its samples' backward
 // records per segment (the binned backward's counting pass, done here from
 // the cells the prologue computes anyway) and adds its counts into row
-// (query tile mod nchunks) of its plane's histogram rows `counts`, which the
-// caller zeroed.
+// (query tile mod nchunks) of its plane's histogram rows `counts` (one row
+// per plane as launched), which the caller zeroed.
 template <int DTK, int VECB, int LPR, int L_CT, int P_CT, int REF, bool CNT>
 __global__ void __launch_bounds__(kBlock)
 msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc,

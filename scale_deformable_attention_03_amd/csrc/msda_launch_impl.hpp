@@ -172,7 +172,8 @@ msda_status_t count_scan_launch(const msda::Problem& pb, int ref_dims, const voi
     }
     MSDA_TRY(mark(ev, kStageScan, st));
     return launch(kfn(&msda::msda_bin_scan_kernel), pb.nplanes, msda::kScanBlock, 0, st,
-                  static_cast<const int32_t*>(counts), static_cast<int>(chunks), cursor, nunits, multi, units,
+                  static_cast<const int32_t*>(counts), counted ? msda::kForwardCountRows : static_cast<int>(chunks),
+                  cursor, nunits, multi, units,
                   accumulate, pb, plane_recs, plane_us);
 }
 

@@ -62,6 +62,10 @@ constexpr int kMaxBinnedExtent = 65534; // H and W of a level on the binned path
 constexpr int kCountBlock = 512;       // lanes of a counting workgroup
 constexpr int kCountChunk = 4096;      // samples one counting workgroup bins (at least)
 constexpr int kMaxCountChunks = 64;    // counting workgroups (histogram rows) per plane
+// histogram rows per plane that a counting forward adds into (its
+// workgroups add with integer atomics, so one row serves them all: the scan
+// then sums one row instead of kMaxCountChunks)
+constexpr int kForwardCountRows = 1;
 
 constexpr int kCountScanSamples = 8192;  // samples of a plane counted and scanned by one workgroup
 constexpr int kNarrowPerPlane = 8;     // workgroups per plane rounding multi-unit rows to 16 bits
