@@ -114,17 +114,25 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // VECB raw bytes of a row, held in 32-bit words.
 template <int VECB> struct Raw { uint32_t w[VECB / 4]; };
 
+// load_raw / store_raw move the data each kernel streams once (sampling
+// locations and weights, a query's grad_output row, outputs and gradients)
+// with non-temporal loads and stores, so that they do not push out of L2 the
+// value and grad_output rows that the gathers reuse (measured on the
+// large-batch bf16 encoder step: 1.233 -> 1.200 ms).  The gathers themselves
+// use buffer loads (below).
+
 template <int VECB>
 __device__ __forceinline__ Raw<VECB> load_raw(const void* p) {
     Raw<VECB> r;
     if constexpr (VECB == 16) {
-        uint4 v = *static_cast<const uint4*>(p);
-        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+        const uint4* q = static_cast<const uint4*>(p);
+        r.w[0] = __builtin_nontemporal_load(&q->x); r.w[1] = __builtin_nontemporal_load(&q->y);
+        r.w[2] = __builtin_nontemporal_load(&q->z); r.w[3] = __builtin_nontemporal_load(&q->w);
     } else if constexpr (VECB == 8) {
-        uint2 v = *static_cast<const uint2*>(p);
-        r.w[0] = v.x; r.w[1] = v.y;
+        const uint2* q = static_cast<const uint2*>(p);
+        r.w[0] = __builtin_nontemporal_load(&q->x); r.w[1] = __builtin_nontemporal_load(&q->y);
     } else {
-        r.w[0] = *static_cast<const uint32_t*>(p);
+        r.w[0] = __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
     }
     return r;
 }
@@ -132,11 +140,14 @@ __device__ __forceinline__ Raw<VECB> load_raw(const void* p) {
 template <int VECB>
 __device__ __forceinline__ void store_raw(void* p, const Raw<VECB>& r) {
     if constexpr (VECB == 16) {
-        *static_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+        uint4* q = static_cast<uint4*>(p);
+        __builtin_nontemporal_store(r.w[0], &q->x); __builtin_nontemporal_store(r.w[1], &q->y);
+        __builtin_nontemporal_store(r.w[2], &q->z); __builtin_nontemporal_store(r.w[3], &q->w);
     } else if constexpr (VECB == 8) {
-        *static_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+        uint2* q = static_cast<uint2*>(p);
+        __builtin_nontemporal_store(r.w[0], &q->x); __builtin_nontemporal_store(r.w[1], &q->y);
     } else {
-        *static_cast<uint32_t*>(p) = r.w[0];
+        __builtin_nontemporal_store(r.w[0], static_cast<uint32_t*>(p));
     }
 }
 
