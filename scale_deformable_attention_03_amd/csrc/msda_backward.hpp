@@ -28,6 +28,9 @@
 //                in-map corners of one image row of a sample's cell make a
 //                record; count records per segment (an LDS histogram per
 //                workgroup, written out as that workgroup's row of counts).
+//                In a training step the forward kernel (CNT) counts them
+//                instead, from the cells it computes anyway, adding into one
+//                zeroed row per plane; the backward then starts at the scan.
 //   2. scan      sum the rows, then an exclusive prefix over the counts gives
 //                each segment a record range and a cursor (small planes count
 //                and scan in one kernel); segments are split into units of at most
