@@ -201,18 +201,31 @@ __device__ __forceinline__ void count_samples(const void* __restrict__ loc, cons
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
+            // the cells of the S samples (kNoCell off the map or past the end)
+            uint32_t cell[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
                 const int s = s0 + u * S * NT + k;
-                if (s >= s_end) break;
-                const int lp = s % LP, l = lp / P;
-                const int4 lv = s_lv[l];
-                const int H = lv.x, W = lv.y;
+                const int4 lv = s_lv[(s % LP) / P];
                 float x, y;
-                if (!pixel_coords(lx[u * S + k], ly[u * S + k], static_cast<float>(W), static_cast<float>(H), x, y))
-                    continue;
-                const int x0 = static_cast<int>(floorf(x)), y0 = static_cast<int>(floorf(y));
-                for_each_record(x0, y0, W, H, lv.w & 0xff, lv.w >> 8,
+                cell[k] = s < s_end && pixel_coords(lx[u * S + k], ly[u * S + k], static_cast<float>(lv.y),
+                                                    static_cast<float>(lv.x), x, y)
+                              ? pack_cell(static_cast<int>(floorf(x)), static_cast<int>(floorf(y)))
+                              : kNoCell;
+            }
+            // merged cells count once (a lane pair's samples are valid together:
+            // s_begin and s_end are multiples of four)
+            bool first[S];
+#pragma unroll
+            for (int k = 0; k < S; ++k) first[k] = true;
+            if constexpr (kMergeCells<REF, L_CT, P_CT>)
+                first_of_cell<S>(cell, (s0 + u * S * NT) % P, first);
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                if (cell[k] == kNoCell || !first[k]) continue;
+                const int4 lv = s_lv[((s0 + u * S * NT + k) % LP) / P];
+                const int x0 = static_cast<int>(cell[k] & 0xffffu) - 1, y0 = static_cast<int>(cell[k] >> 16) - 1;
+                for_each_record(x0, y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
                                 [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
             }
         }
@@ -624,29 +637,34 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         __syncthreads();
     }
 
-    // prologue: sample i = g * LP + lp of the workgroup, its location xy and
-    // (REF == 0) its attention weight w_in -> LDS record and segment counts.
+    // prologue: sample i = g * LP + lp of the workgroup, its corners c (from
+    // its location) and (REF == 0) its attention weight w_in -> LDS record and
+    // segment counts (its records are counted when `count`: with cell merging,
+    // the first sample of its cell among its level's points).
     // With REF != 0 the weight kept is the softmax weight even for a sample
     // off the map (its gradient reaches the other logits of the group);
     // nothing reads it there but the softmax backward.
-    auto stage = [&](int i, int g, int lp, float2 xy, float w_in) {
+    auto corners_of = [&](int lp, float2 xy) {
         const int4 lv = s_lv[lp / P];
-        const int H = lv.x, W = lv.y;
-        Corners c = sample_corners(xy.x, xy.y, H, W, lv.z, pitch);
+        Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
         // padded corners read as zero; their records still go to the
         // accumulation, which writes padded rows as zero
-        mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, W);
+        mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
+        return c;
+    };
+    auto stage = [&](int i, int g, int lp, const Corners& c, float w_in, bool count) {
+        const int4 lv = s_lv[lp / P];
+        const int H = lv.x, W = lv.y;
         float aw;
         if constexpr (REF == 0) aw = c.ok ? w_in : 0.0f;
         else aw = se[i] / group_total(se + g * LP, LP);
         uint32_t* r = srec + g * gstride + lp * 8;
-        const uint32_t cell = c.ok ? static_cast<uint32_t>(c.x0 + 1) | (static_cast<uint32_t>(c.y0 + 1) << 16)
-                                   : kNoCell;
+        const uint32_t cell = c.ok ? pack_cell(c.x0, c.y0) : kNoCell;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
         *reinterpret_cast<uint4*>(r + 4) = make_uint4(__float_as_uint(c.lx), __float_as_uint(c.ly),
                                                       __float_as_uint(aw), cell);
         if constexpr (BINNED) {
-            if (c.ok)
+            if (c.ok && count)
                 for_each_record(c.x0, c.y0, W, H, lv.w & 0xff, lv.w >> 8,
                                 [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
         }
@@ -663,8 +681,23 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             float xy[2 * S], wv[S];
             widen<ST, 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * si * SE), xy);
             widen<ST, S * SE>(load_raw<S * SE>(static_cast<const char*>(attw) + si * SE), wv);
+            Corners c[S];
+            bool first[S];
 #pragma unroll
-            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, make_float2(xy[2 * k], xy[2 * k + 1]), wv[k]);
+            for (int k = 0; k < S; ++k) {
+                c[k] = corners_of(lp + k, make_float2(xy[2 * k], xy[2 * k + 1]));
+                first[k] = true;
+            }
+            if constexpr (BINNED && kMergeCells<REF, L_CT, P_CT>) {
+                // (the lane pair holding a level's four points is active together:
+                // t.gcount * LP and the loop stride are multiples of four)
+                uint32_t cell[S];
+#pragma unroll
+                for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
+                first_of_cell<S>(cell, lp % P, first);
+            }
+#pragma unroll
+            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], first[k]);
         }
     } else {
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
@@ -676,7 +709,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                                        static_cast<float>(lv.x), static_cast<float>(P));
             float w_in = 0.0f;
             if constexpr (REF == 0) w_in = load_scalar<ST>(attw, si);
-            stage(i, g, lp, xy, w_in);
+            stage(i, g, lp, corners_of(lp, xy), w_in, true);
         }
     }
     __syncthreads();
@@ -887,12 +920,38 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
             const uint32_t cell = __float_as_uint(fr.w);
             if (cell == kNoCell) continue;
+            // the corner weights of rows y0 (w00, w01) and y0 + 1 (w10, w11)
+            const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
+            const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
+            float w00 = wy0 * hx, w01 = wy0 * fr.x, w10 = wy1 * hx, w11 = wy1 * fr.x;
+            if constexpr (kMergeCells<REF, L_CT, P_CT>) {
+                // cell merging: a point of this level before this one in the
+                // same cell makes the records; otherwise they carry the weights
+                // of the points after it in the same cell (in point order)
+                const int p = lp % 4;
+                const uint32_t* rl = r - p * 8;          // the level's point 0
+                bool first = true;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 fq = *reinterpret_cast<const float4*>(rl + q * 8 + 4);
+                    if (q == p || __float_as_uint(fq.w) != cell) continue;
+                    if (q < p) {
+                        first = false;
+                    } else {
+                        const float qhx = 1.0f - fq.x, qhy = 1.0f - fq.y;
+                        const float qwy0 = fq.z * qhy, qwy1 = fq.z * fq.y;
+                        w00 += qwy0 * qhx;
+                        w01 += qwy0 * fq.x;
+                        w10 += qwy1 * qhx;
+                        w11 += qwy1 * fq.x;
+                    }
+                }
+                if (!first) continue;
+            }
             const int4 lv = s_lv[l];
             const int H = lv.x, W = lv.y, shift = lv.w & 0xff, segbase = lv.w >> 8;
             const int x0 = static_cast<int>(cell & 0xffffu) - 1, y0 = static_cast<int>(cell >> 16) - 1;
             const bool lin = x0 >= 0, rin = x0 + 1 < W;
-            const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
-            const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
             const uint32_t qk = static_cast<uint32_t>(t.q0 + g) << 8;
             const int kmask = (1 << shift) - 1;
             int seg[4], pos[4];
@@ -904,8 +963,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 const bool rowok = yc >= 0 && yc < H;
                 const int kl = yc * W + x0, kr = kl + 1;
                 const bool split = lin && rin && (kl >> shift) != (kr >> shift);
-                const float wy = rr ? wy1 : wy0;
-                const float cl = wy * hx, cr = wy * fr.x;
+                const float cl = rr ? w10 : w00, cr = rr ? w11 : w01;
                 const int k1 = lin ? kl : kr;
                 valid[2 * rr] = rowok;
                 seg[2 * rr] = segbase + (k1 >> shift);

@@ -391,6 +391,51 @@ constexpr uint32_t kNoCell = 0xffffffffu;  // packed cell of a sample off the ma
 // Corners of one row that a record covers.
 enum RecMode : int { kBoth = 0, kLeftOnly = 1, kRightOnly = 2 };
 
+// Packed cell (x0 + 1, y0 + 1) of an in-map sample (16-bit fields; never
+// equal to kNoCell on levels of at most 65534 pixels a side).
+__device__ __forceinline__ uint32_t pack_cell(int x0, int y0) {
+    return static_cast<uint32_t>(x0 + 1) | (static_cast<uint32_t>(y0 + 1) << 16);
+}
+
+// Cell merging.  The samples of one (batch, query, head, level) scale the
+// same grad_output row, so two of them in the same bilinear cell make
+// records with the same keys.  The first of them (lowest point index) makes
+// the records, with the corner weights of all of them summed, and the others
+// make none.  Built for the plain form at four points per level and fixed
+// L * P, where the points of a query often share a cell on the coarse levels
+// (about a fifth of the encoder's records); every count of records (count
+// kernel, counting forward, the gradient kernel's own count) and the
+// gradient kernel's records follow the same rule.
+template <int REF, int L_CT, int P_CT>
+constexpr bool kMergeCells = REF == 0 && L_CT != 0 && P_CT == 4;
+
+// first[k]: whether the lane's sample k is the first of its cell among its
+// level's four points.  The lane holds S consecutive samples of one level,
+// points p0 .. p0 + S - 1 (p0 a multiple of S), with packed cells `cell`
+// (kNoCell off the map: such a sample makes no records and its flag does not
+// matter).  S == 2: the level's other two points are in lane ^ 1, which runs
+// the same call (both lanes are active together).  S == 4: all four are here.
+template <int S>
+__device__ __forceinline__ void first_of_cell(const uint32_t (&cell)[S], int p0, bool (&first)[S]) {
+    static_assert(S == 2 || S == 4, "a lane holds two or four points of a level");
+    if constexpr (S == 4) {
+        first[0] = true;
+        first[1] = cell[1] != cell[0];
+        first[2] = cell[2] != cell[0] && cell[2] != cell[1];
+        first[3] = cell[3] != cell[0] && cell[3] != cell[1] && cell[3] != cell[2];
+    } else {
+        const uint32_t o0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cell[0]), 1, 64));
+        const uint32_t o1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cell[1]), 1, 64));
+        if (p0 == 0) {
+            first[0] = true;
+            first[1] = cell[1] != cell[0];
+        } else {                                     // points 2, 3; o0, o1 are points 0, 1
+            first[0] = cell[0] != o0 && cell[0] != o1;
+            first[1] = cell[1] != o0 && cell[1] != o1 && cell[1] != cell[0];
+        }
+    }
+}
+
 // Enumerate the records of a valid sample whose cell starts at (x0, y0) on
 // a W x H level (-1 <= x0 < W, -1 <= y0 < H): for each of the rows y0,
 // y0 + 1 that lie on the map, the in-map corners of that row.  A pair whose
