@@ -213,20 +213,21 @@ __device__ __forceinline__ void count_samples(const void* __restrict__ loc, cons
                               ? pack_cell(static_cast<int>(floorf(x)), static_cast<int>(floorf(y)))
                               : kNoCell;
             }
-            // merged cells count once (a lane pair's samples are valid together:
-            // s_begin and s_end are multiples of four)
-            bool first[S];
+            // merged records count once (a lane pair's samples are valid
+            // together: s_begin and s_end are multiples of four)
+            uint32_t rows[S];
 #pragma unroll
-            for (int k = 0; k < S; ++k) first[k] = true;
-            if constexpr (kMergeCells<REF, L_CT, P_CT>)
-                first_of_cell<S>(cell, (s0 + u * S * NT) % P, first);
+            for (int k = 0; k < S; ++k) rows[k] = 3u;
+            if constexpr (kMergeRecords<REF, L_CT, P_CT>)
+                if (pb.merge_records) record_rows<S>(cell, (s0 + u * S * NT) % P, rows);
 #pragma unroll
             for (int k = 0; k < S; ++k) {
-                if (cell[k] == kNoCell || !first[k]) continue;
+                if (cell[k] == kNoCell) continue;
                 const int4 lv = s_lv[((s0 + u * S * NT + k) % LP) / P];
                 const int x0 = static_cast<int>(cell[k] & 0xffffu) - 1, y0 = static_cast<int>(cell[k] >> 16) - 1;
-                for_each_record(x0, y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
-                                [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); });
+                for_each_record(
+                    x0, y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
+                    [&](int seg, int, int, int) { atomicAdd(&hist[seg], 1); }, rows[k]);
             }
         }
     }
@@ -639,8 +640,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
 
     // prologue: sample i = g * LP + lp of the workgroup, its corners c (from
     // its location) and (REF == 0) its attention weight w_in -> LDS record and
-    // segment counts (its records are counted when `count`: with cell merging,
-    // the first sample of its cell among its level's points).
+    // segment counts (of its records on the image rows in `rows`, bit r for
+    // row y0 + r: all, or those record merging leaves it).
     // With REF != 0 the weight kept is the softmax weight even for a sample
     // off the map (its gradient reaches the other logits of the group);
     // nothing reads it there but the softmax backward.
@@ -652,7 +653,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
         return c;
     };
-    auto stage = [&](int i, int g, int lp, const Corners& c, float w_in, bool count) {
+    auto stage = [&](int i, int g, int lp, const Corners& c, float w_in, uint32_t rows) {
         const int4 lv = s_lv[lp / P];
         const int H = lv.x, W = lv.y;
         float aw;
@@ -664,9 +665,10 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         *reinterpret_cast<uint4*>(r + 4) = make_uint4(__float_as_uint(c.lx), __float_as_uint(c.ly),
                                                       __float_as_uint(aw), cell);
         if constexpr (BINNED) {
-            if (c.ok && count)
-                for_each_record(c.x0, c.y0, W, H, lv.w & 0xff, lv.w >> 8,
-                                [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
+            if (c.ok)
+                for_each_record(
+                    c.x0, c.y0, W, H, lv.w & 0xff, lv.w >> 8,
+                    [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); }, rows);
         }
     };
     if constexpr (kPrologueSamples<ST, REF, L_CT, P_CT> > 1) {
@@ -682,22 +684,25 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             widen<ST, 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * si * SE), xy);
             widen<ST, S * SE>(load_raw<S * SE>(static_cast<const char*>(attw) + si * SE), wv);
             Corners c[S];
-            bool first[S];
+            uint32_t rows[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
                 c[k] = corners_of(lp + k, make_float2(xy[2 * k], xy[2 * k + 1]));
-                first[k] = true;
+                rows[k] = 3u;
             }
-            if constexpr (BINNED && kMergeCells<REF, L_CT, P_CT>) {
-                // (the lane pair holding a level's four points is active together:
-                // t.gcount * LP and the loop stride are multiples of four)
-                uint32_t cell[S];
+            if constexpr (BINNED && kMergeRecords<REF, L_CT, P_CT>) {
+                if (pb.merge_records) {
+                    // (the lane pair holding a level's four points is active
+                    // together: t.gcount * LP and the loop stride are multiples
+                    // of four)
+                    uint32_t cell[S];
 #pragma unroll
-                for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
-                first_of_cell<S>(cell, lp % P, first);
+                    for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
+                    record_rows<S>(cell, lp % P, rows);
+                }
             }
 #pragma unroll
-            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], first[k]);
+            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], rows[k]);
         }
     } else {
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
@@ -709,7 +714,7 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                                                        static_cast<float>(lv.x), static_cast<float>(P));
             float w_in = 0.0f;
             if constexpr (REF == 0) w_in = load_scalar<ST>(attw, si);
-            stage(i, g, lp, corners_of(lp, xy), w_in, true);
+            stage(i, g, lp, corners_of(lp, xy), w_in, 3u);
         }
     }
     __syncthreads();
@@ -924,29 +929,41 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
             const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
             float w00 = wy0 * hx, w01 = wy0 * fr.x, w10 = wy1 * hx, w11 = wy1 * fr.x;
-            if constexpr (kMergeCells<REF, L_CT, P_CT>) {
-                // cell merging: a point of this level before this one in the
-                // same cell makes the records; otherwise they carry the weights
-                // of the points after it in the same cell (in point order)
+            uint32_t rows = 3u;                          // bit r: the record of image row y0 + r
+            if (kMergeRecords<REF, L_CT, P_CT> && pb.merge_records != 0) {
+                // record merging: a row that an earlier point of this level
+                // has too (same image row, same x-pair) is that point's record;
+                // the others carry the weights of the later points' rows that
+                // they share (in point order)
                 const int p = lp % 4;
                 const uint32_t* rl = r - p * 8;          // the level's point 0
-                bool first = true;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float4 fq = *reinterpret_cast<const float4*>(rl + q * 8 + 4);
-                    if (q == p || __float_as_uint(fq.w) != cell) continue;
+                    const uint32_t cq = __float_as_uint(fq.w);
                     if (q < p) {
-                        first = false;
-                    } else {
-                        const float qhx = 1.0f - fq.x, qhy = 1.0f - fq.y;
-                        const float qwy0 = fq.z * qhy, qwy1 = fq.z * fq.y;
-                        w00 += qwy0 * qhx;
-                        w01 += qwy0 * fq.x;
-                        w10 += qwy1 * qhx;
-                        w11 += qwy1 * fq.x;
+                        rows &= ~shared_rows(cell, cq);
+                    } else if (q > p) {
+                        const uint32_t sq = shared_rows(cq, cell);   // point q's rows that this one has
+                        if (sq != 0u) {
+                            const float qhx = 1.0f - fq.x, qhy = 1.0f - fq.y;
+                            const float qwy0 = fq.z * qhy, qwy1 = fq.z * fq.y;
+                            if (sq == 3u) {                  // same cell
+                                w00 += qwy0 * qhx;
+                                w01 += qwy0 * fq.x;
+                                w10 += qwy1 * qhx;
+                                w11 += qwy1 * fq.x;
+                            } else if (sq == 1u) {           // q's row y0 is this one's row y0 + 1
+                                w10 += qwy0 * qhx;
+                                w11 += qwy0 * fq.x;
+                            } else {                         // q's row y0 + 1 is this one's row y0
+                                w00 += qwy1 * qhx;
+                                w01 += qwy1 * fq.x;
+                            }
+                        }
                     }
                 }
-                if (!first) continue;
+                if (rows == 0u) continue;
             }
             const int4 lv = s_lv[l];
             const int H = lv.x, W = lv.y, shift = lv.w & 0xff, segbase = lv.w >> 8;
@@ -965,11 +982,11 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 const bool split = lin && rin && (kl >> shift) != (kr >> shift);
                 const float cl = rr ? w10 : w00, cr = rr ? w11 : w01;
                 const int k1 = lin ? kl : kr;
-                valid[2 * rr] = rowok;
+                valid[2 * rr] = rowok && ((rows >> rr) & 1u) != 0u;
                 seg[2 * rr] = segbase + (k1 >> shift);
                 rec[2 * rr] = make_uint3(qk | static_cast<uint32_t>(k1 & kmask), __float_as_uint(lin ? cl : cr),
                                          __float_as_uint(lin && rin && !split ? cr : 0.0f));
-                valid[2 * rr + 1] = rowok && split;
+                valid[2 * rr + 1] = valid[2 * rr] && split;
                 seg[2 * rr + 1] = segbase + (kr >> shift);
                 rec[2 * rr + 1] = make_uint3(qk | static_cast<uint32_t>(kr & kmask), __float_as_uint(cr), 0u);
             }

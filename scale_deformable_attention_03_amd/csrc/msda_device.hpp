@@ -397,59 +397,78 @@ __device__ __forceinline__ uint32_t pack_cell(int x0, int y0) {
     return static_cast<uint32_t>(x0 + 1) | (static_cast<uint32_t>(y0 + 1) << 16);
 }
 
-// Cell merging.  The samples of one (batch, query, head, level) scale the
-// same grad_output row, so two of them in the same bilinear cell make
-// records with the same keys.  The first of them (lowest point index) makes
-// the records, with the corner weights of all of them summed, and the others
-// make none.  Built for the plain form at four points per level and fixed
-// L * P, where the points of a query often share a cell on the coarse levels
-// (about a fifth of the encoder's records); every count of records (count
-// kernel, counting forward, the gradient kernel's own count) and the
+// Record merging.  The samples of one (batch, query, head, level) scale the
+// same grad_output row, so records of two of them on the same image row with
+// the same x-pair have the same keys.  In point order (a point's row y0
+// before its row y0 + 1), the first such record is made, with the corner
+// weights of the later ones added in that order, and the later ones are not.
+// Built for the plain form at four points per level and fixed L * P, where
+// the points of a query often lie within a pixel of each other on the coarse
+// levels (about a quarter of the encoder's records); every count of records
+// (count kernel, counting forward, the gradient kernel's own count) and the
 // gradient kernel's records follow the same rule.
 template <int REF, int L_CT, int P_CT>
-constexpr bool kMergeCells = REF == 0 && L_CT != 0 && P_CT == 4;
+constexpr bool kMergeRecords = REF == 0 && L_CT != 0 && P_CT == 4;
 
-// first[k]: whether the lane's sample k is the first of its cell among its
-// level's four points.  The lane holds S consecutive samples of one level,
-// points p0 .. p0 + S - 1 (p0 a multiple of S), with packed cells `cell`
-// (kNoCell off the map: such a sample makes no records and its flag does not
-// matter).  S == 2: the level's other two points are in lane ^ 1, which runs
-// the same call (both lanes are active together).  S == 4: all four are here.
+// Rows of the sample with packed cell cp (bit r: image row y0 + r) that a
+// sample with packed cell cq also has (same x-pair, one or both rows in
+// common); 0 when cq is kNoCell (its low field, 0xffff, is no in-map x0 + 1).
+__device__ __forceinline__ uint32_t shared_rows(uint32_t cp, uint32_t cq) {
+    if (((cp ^ cq) & 0xffffu) != 0u) return 0u;
+    const int dy = static_cast<int>(cp >> 16) - static_cast<int>(cq >> 16);
+    return dy == 0 ? 3u : (dy == 1 ? 1u : (dy == -1 ? 2u : 0u));
+}
+
+// rows[k]: the rows (bit r: image row y0 + r) for which the lane's sample k
+// makes a record, i.e. no earlier point of its level has a record on that
+// image row with the same x-pair.  The lane holds S consecutive samples of
+// one level, points p0 .. p0 + S - 1 (p0 a multiple of S), with packed cells
+// `cell` (kNoCell off the map: such a sample makes no records and its rows
+// do not matter).  S == 2: the level's other two points are in lane ^ 1,
+// which runs the same call (both lanes are active together).  S == 4: all
+// four are here.
 template <int S>
-__device__ __forceinline__ void first_of_cell(const uint32_t (&cell)[S], int p0, bool (&first)[S]) {
+__device__ __forceinline__ void record_rows(const uint32_t (&cell)[S], int p0, uint32_t (&rows)[S]) {
     static_assert(S == 2 || S == 4, "a lane holds two or four points of a level");
+    uint32_t c[4];
     if constexpr (S == 4) {
-        first[0] = true;
-        first[1] = cell[1] != cell[0];
-        first[2] = cell[2] != cell[0] && cell[2] != cell[1];
-        first[3] = cell[3] != cell[0] && cell[3] != cell[1] && cell[3] != cell[2];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = cell[k];
+        p0 = 0;
     } else {
         const uint32_t o0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cell[0]), 1, 64));
         const uint32_t o1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(cell[1]), 1, 64));
-        if (p0 == 0) {
-            first[0] = true;
-            first[1] = cell[1] != cell[0];
-        } else {                                     // points 2, 3; o0, o1 are points 0, 1
-            first[0] = cell[0] != o0 && cell[0] != o1;
-            first[1] = cell[1] != o0 && cell[1] != o1 && cell[1] != cell[0];
-        }
+        const bool hi = p0 != 0;                     // this lane holds points 2, 3
+        c[0] = hi ? o0 : cell[0];
+        c[1] = hi ? o1 : cell[1];
+        c[2] = hi ? cell[0] : o0;
+        c[3] = hi ? cell[1] : o1;
+    }
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        uint32_t taken = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < p0 + k) taken |= shared_rows(cell[k], c[q]);
+        rows[k] = 3u & ~taken;
     }
 }
 
 // Enumerate the records of a valid sample whose cell starts at (x0, y0) on
 // a W x H level (-1 <= x0 < W, -1 <= y0 < H): for each of the rows y0,
-// y0 + 1 that lie on the map, the in-map corners of that row.  A pair whose
+// y0 + 1 that lie on the map (and are in `rows`, bit r for row y0 + r), the
+// in-map corners of that row.  A pair whose
 // two corners fall in different segments is split in two records.
 // emit(segment, key within segment, row 0/1, mode).
 template <typename Emit>
 __device__ __forceinline__ void for_each_record(int x0, int y0, int W, int H, int shift, int segbase,
-                                                Emit&& emit) {
+                                                Emit&& emit, uint32_t rows = 3u) {
     const int mask = (1 << shift) - 1;
     const bool lin = x0 >= 0, rin = x0 + 1 < W;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int yc = y0 + r;
-        if (yc < 0 || yc >= H) continue;
+        if (yc < 0 || yc >= H || ((rows >> r) & 1u) == 0u) continue;
         const int kl = yc * W + x0;    // left corner key (meaningful when lin)
         const int kr = kl + 1;         // right corner key
         if (lin && rin) {

@@ -152,15 +152,15 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
 
     // prologue: sample i = g * LP + lp of the workgroup, its corners c (from
     // its location) and (REF == 0) its attention weight w_in -> LDS record;
-    // CNT: its records are counted when `count` (cell merging: the first
-    // sample of its cell among its level's points)
+    // CNT: its records on the image rows in `rows` (bit r for row y0 + r: all,
+    // or those record merging leaves it) are counted
     auto corners_of = [&](int lp, float2 xy) {
         const int4 lv = s_lv[lp / P];
         Corners c = sample_corners(xy.x, xy.y, lv.x, lv.y, lv.z, pitch);
         mask_corners(c, kmask ? kmask + static_cast<int64_t>(t.b) * pb.K : nullptr, lv.z, lv.y);
         return c;
     };
-    auto stage = [&](int i, int g, int lp, const Corners& c, float w_in, bool count) {
+    auto stage = [&](int i, int g, int lp, const Corners& c, float w_in, uint32_t rows) {
         const int4 lv = s_lv[lp / P];
         float aw;
         if constexpr (REF == 0) aw = c.ok ? w_in : 0.0f;
@@ -170,9 +170,10 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
         *reinterpret_cast<float4*>(r + 4) = make_float4(wy0 * c.hx, wy0 * c.lx, wy1 * c.hx, wy1 * c.lx);
         if constexpr (CNT) {
-            if (c.ok && count)
-                for_each_record(c.x0, c.y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
-                                [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); });
+            if (c.ok)
+                for_each_record(
+                    c.x0, c.y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
+                    [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); }, rows);
         }
     };
     if constexpr (kPrologueSamples<ST, REF, L_CT, P_CT> > 1) {
@@ -188,22 +189,25 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
             widen<ST, 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * si * SE), xy);
             widen<ST, S * SE>(load_raw<S * SE>(static_cast<const char*>(attw) + si * SE), wv);
             Corners c[S];
-            bool first[S];
+            uint32_t rows[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
                 c[k] = corners_of(lp + k, make_float2(xy[2 * k], xy[2 * k + 1]));
-                first[k] = true;
+                rows[k] = 3u;
             }
-            if constexpr (CNT && kMergeCells<REF, L_CT, P_CT>) {
-                // (the lane pair holding a level's four points is active together:
-                // t.gcount * LP and the loop stride are multiples of four)
-                uint32_t cell[S];
+            if constexpr (CNT && kMergeRecords<REF, L_CT, P_CT>) {
+                if (pb.merge_records) {
+                    // (the lane pair holding a level's four points is active
+                    // together: t.gcount * LP and the loop stride are multiples
+                    // of four)
+                    uint32_t cell[S];
 #pragma unroll
-                for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
-                first_of_cell<S>(cell, lp % P, first);
+                    for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
+                    record_rows<S>(cell, lp % P, rows);
+                }
             }
 #pragma unroll
-            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], first[k]);
+            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], rows[k]);
         }
     } else {
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
@@ -215,7 +219,7 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
                                                        static_cast<float>(lv.x), static_cast<float>(P));
             float w_in = 0.0f;
             if constexpr (REF == 0) w_in = load_scalar<ST>(attw, si);
-            stage(i, g, lp, corners_of(lp, xy), w_in, true);
+            stage(i, g, lp, corners_of(lp, xy), w_in, 3u);
         }
     }
     __syncthreads();

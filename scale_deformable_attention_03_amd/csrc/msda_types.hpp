@@ -45,6 +45,7 @@ struct Problem {
     int32_t nseg;
     int32_t nplanes;         // bs * M
     int32_t unit_records;    // records per accumulation unit (kUnitRecords or kSparseUnitRecords)
+    int32_t merge_records;   // 1: the L4P4 kernels merge records (see kMergeRecords)
     int32_t seg_shift[kMaxLevels];
     int32_t seg_base[kMaxLevels + 1];
 };

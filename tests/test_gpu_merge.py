@@ -1,0 +1,60 @@
+"""GPU parity of the backward's record merging.
+
+The records of a query's samples on one level that share an image row and an
+x-pair become one record with summed weights, at four points per level on
+planes counted apart from the scan.  These tests use problems where most
+records merge and check the plain backward and the training pair against the
+CPU oracle:
+- tiny levels, where a query's four points often fall in one cell or in
+  vertically adjacent cells;
+- all four points of a level at one location (every row merges);
+- points one, two and three pixels below the first (rows shared between
+  neighbouring cells).
+"""
+import pytest
+import torch
+
+from scale_deformable_attention_03_amd import workloads as W
+from tests.parity import check_backward, check_forward, to_device
+
+pytestmark = pytest.mark.gpu
+
+LEVELS = [(8, 10), (4, 5), (2, 3), (1, 2)]
+
+
+def clustered(mode, dtype, sample_dtype, seed):
+    """700 queries (11,200 samples per plane: counted apart from the scan,
+    so the records merge), 2 heads of 32 channels, L4P4."""
+    wl = W.make(f"merge_{mode}", 1, LEVELS, 2, 32, 4, 700, dtype, seed=seed, loc_args=(-0.1, 1.1),
+                sample_dtype=sample_dtype)
+    loc = wl.sampling_locations.to(torch.float32)      # [bs, Q, M, L, P, 2]
+    if mode == "same":
+        loc = loc[..., :1, :].expand_as(loc).clone()
+    elif mode == "column":
+        H = torch.tensor([float(h) for h, _ in LEVELS]).view(1, 1, 1, len(LEVELS))
+        for p in range(1, 4):
+            loc[..., p, 0] = loc[..., 0, 0]
+            loc[..., p, 1] = loc[..., 0, 1] + p / H
+    wl.sampling_locations = loc.to(wl.sampling_locations.dtype)
+    return wl
+
+
+CASES = [(mode, dt, sdt) for mode in ("uniform", "same", "column")
+         for dt, sdt in (("f32", None), ("bf16", None), ("f16", "f32"))]
+
+
+@pytest.mark.parametrize("mode,dt,sdt", CASES, ids=[f"{m}_{d}{'_' + s if s else ''}" for m, d, s in CASES])
+def test_merged_records_match_oracle(mode, dt, sdt):
+    from scale_deformable_attention_03_amd import ops
+    print(f"[gpu] merged records {mode} {dt} {sdt}", flush=True)
+    wl = clustered(mode, dt, sdt, seed=1301)
+    # plain backward: the count kernel and the gradient kernel merge
+    check_backward(wl)
+    # training pair: the counting forward merges
+    t = to_device(wl)
+    out, ws = ops.forward_train(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"], t["w"])
+    grads = ops.backward(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"], t["w"], t["g"],
+                         workspace=ws, counted=True)
+    torch.cuda.synchronize()
+    check_forward(wl, out)
+    check_backward(wl, grads)
