@@ -554,7 +554,7 @@ __device__ void pre_reduce_scatter(const uint32_t* srec, int gstride, int LP, in
             const int id = ids[e], s = id >> 2, c = id & 3, g = s / LP;
             const uint32_t* r = srec + g * gstride + (s - g * LP) * 8;
             const uint32_t off = r[c];
-            const float lx = __uint_as_float(r[4]), ly = __uint_as_float(r[5]), aw = __uint_as_float(r[6]);
+            const float lx = fabsf(__uint_as_float(r[4])), ly = fabsf(__uint_as_float(r[5])), aw = __uint_as_float(r[6]);
             // the corner's weight: w * (1-ly or ly) * (1-lx or lx)
             const float wy = aw * ((c & 2) ? ly : 1.0f - ly);
             const float cw = wy * ((c & 1) ? lx : 1.0f - lx);
@@ -661,8 +661,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         else aw = se[i] / group_total(se + g * LP, LP);
         uint32_t* r = srec + g * gstride + lp * 8;
         const uint32_t cell = c.ok ? pack_cell(c.x0, c.y0) : kNoCell;
+        // record merging: a row whose record another point makes is marked
+        // by the sign bit of lx (row y0) or ly (row y0 + 1), which are never
+        // negative otherwise (readers take their magnitudes)
+        const uint32_t drop0 = c.ok && (rows & 1u) == 0u ? 0x80000000u : 0u;
+        const uint32_t drop1 = c.ok && (rows & 2u) == 0u ? 0x80000000u : 0u;
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
-        *reinterpret_cast<uint4*>(r + 4) = make_uint4(__float_as_uint(c.lx), __float_as_uint(c.ly),
+        *reinterpret_cast<uint4*>(r + 4) = make_uint4(__float_as_uint(c.lx) | drop0, __float_as_uint(c.ly) | drop1,
                                                       __float_as_uint(aw), cell);
         if constexpr (BINNED) {
             if (c.ok)
@@ -784,7 +789,8 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 for (int u = 0; u < kSB; ++u) {
                     const int lp = c0 + b0 + u;
                     const float4 fr = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);    // lx ly w cell
-                    const float4 f = make_float4(1.0f - fr.x, fr.x, 1.0f - fr.y, fr.y);      // hx lx hy ly
+                    const float flx = fabsf(fr.x), fly = fabsf(fr.y);                        // (sign: merging)
+                    const float4 f = make_float4(1.0f - flx, flx, 1.0f - fly, fly);          // hx lx hy ly
                     float d00 = 0.0f, d01 = 0.0f, d10 = 0.0f, d11 = 0.0f;
                     if constexpr (DT == kF32) {
                         float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
@@ -926,44 +932,42 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             const uint32_t cell = __float_as_uint(fr.w);
             if (cell == kNoCell) continue;
             // the corner weights of rows y0 (w00, w01) and y0 + 1 (w10, w11)
-            const float hx = 1.0f - fr.x, hy = 1.0f - fr.y;
-            const float wy0 = fr.z * hy, wy1 = fr.z * fr.y;
-            float w00 = wy0 * hx, w01 = wy0 * fr.x, w10 = wy1 * hx, w11 = wy1 * fr.x;
-            uint32_t rows = 3u;                          // bit r: the record of image row y0 + r
+            const float lx = fabsf(fr.x), ly = fabsf(fr.y);
+            const float hx = 1.0f - lx, hy = 1.0f - ly;
+            const float wy0 = fr.z * hy, wy1 = fr.z * ly;
+            float w00 = wy0 * hx, w01 = wy0 * lx, w10 = wy1 * hx, w11 = wy1 * lx;
+            // bit r: the record of image row y0 + r (the prologue marked the
+            // rows whose record an earlier point of the level makes)
+            const uint32_t rows = 3u & ~((__float_as_uint(fr.x) >> 31) | ((__float_as_uint(fr.y) >> 31) << 1));
             if (kMergeRecords<REF, L_CT, P_CT> && pb.merge_records != 0) {
-                // record merging: a row that an earlier point of this level
-                // has too (same image row, same x-pair) is that point's record;
-                // the others carry the weights of the later points' rows that
-                // they share (in point order)
+                if (rows == 0u) continue;
+                // record merging: this point's records carry the weights of
+                // the later points' rows that they share (in point order)
                 const int p = lp % 4;
                 const uint32_t* rl = r - p * 8;          // the level's point 0
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 1; q < 4; ++q) {
+                    if (q <= p) continue;
                     const float4 fq = *reinterpret_cast<const float4*>(rl + q * 8 + 4);
-                    const uint32_t cq = __float_as_uint(fq.w);
-                    if (q < p) {
-                        rows &= ~shared_rows(cell, cq);
-                    } else if (q > p) {
-                        const uint32_t sq = shared_rows(cq, cell);   // point q's rows that this one has
-                        if (sq != 0u) {
-                            const float qhx = 1.0f - fq.x, qhy = 1.0f - fq.y;
-                            const float qwy0 = fq.z * qhy, qwy1 = fq.z * fq.y;
-                            if (sq == 3u) {                  // same cell
-                                w00 += qwy0 * qhx;
-                                w01 += qwy0 * fq.x;
-                                w10 += qwy1 * qhx;
-                                w11 += qwy1 * fq.x;
-                            } else if (sq == 1u) {           // q's row y0 is this one's row y0 + 1
-                                w10 += qwy0 * qhx;
-                                w11 += qwy0 * fq.x;
-                            } else {                         // q's row y0 + 1 is this one's row y0
-                                w00 += qwy1 * qhx;
-                                w01 += qwy1 * fq.x;
-                            }
+                    const uint32_t sq = shared_rows(__float_as_uint(fq.w), cell);  // point q's rows this one has
+                    if (sq != 0u) {
+                        const float qlx = fabsf(fq.x), qly = fabsf(fq.y);
+                        const float qhx = 1.0f - qlx, qhy = 1.0f - qly;
+                        const float qwy0 = fq.z * qhy, qwy1 = fq.z * qly;
+                        if (sq == 3u) {                  // same cell
+                            w00 += qwy0 * qhx;
+                            w01 += qwy0 * qlx;
+                            w10 += qwy1 * qhx;
+                            w11 += qwy1 * qlx;
+                        } else if (sq == 1u) {           // q's row y0 is this one's row y0 + 1
+                            w10 += qwy0 * qhx;
+                            w11 += qwy0 * qlx;
+                        } else {                         // q's row y0 + 1 is this one's row y0
+                            w00 += qwy1 * qhx;
+                            w01 += qwy1 * qlx;
                         }
                     }
                 }
-                if (rows == 0u) continue;
             }
             const int4 lv = s_lv[l];
             const int H = lv.x, W = lv.y, shift = lv.w & 0xff, segbase = lv.w >> 8;
