@@ -9,7 +9,8 @@ CPU oracle:
   vertically adjacent cells;
 - all four points of a level at one location (every row merges);
 - points one, two and three pixels below the first (rows shared between
-  neighbouring cells).
+  neighbouring cells);
+and the accumulating and no-alloc entry points on merged records.
 """
 import pytest
 import torch
@@ -58,3 +59,38 @@ def test_merged_records_match_oracle(mode, dt, sdt):
     torch.cuda.synchronize()
     check_forward(wl, out)
     check_backward(wl, grads)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_merged_records_accumulate_and_noalloc(dt):
+    """Merged records through msda_backward_accumulate (every unit adds its
+    rows with float atomics: two calls on a pre-filled buffer give prefill
+    + 2 * grad_value) and through msda_backward_noalloc (the library's own
+    workspace; outputs pre-filled with NaN, so every element must be
+    written)."""
+    from scale_deformable_attention_03_amd import _lib, ops
+    from tests.parity import TOL, assert_close, f64, oracle_backward
+    print(f"[gpu] merged records, accumulating and no-alloc entry points, {dt}", flush=True)
+    wl = clustered("same", dt, None, seed=1302)
+    t = to_device(wl)
+    prob, keep = ops.problem_for(t["value"], wl.spatial_shapes, wl.level_start_index, t["loc"])
+    need = _lib.workspace_bytes(prob)
+    assert 0 < need <= _lib.noalloc_max_workspace()
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    acc = torch.full(t["value"].shape, 0.25, dtype=torch.float32, device="cuda")
+    gl, gw = torch.empty_like(t["loc"]), torch.empty_like(t["w"])
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        _lib.backward_accumulate(prob, t["value"].data_ptr(), t["loc"].data_ptr(), t["w"].data_ptr(),
+                                 t["g"].data_ptr(), acc.data_ptr(), gl.data_ptr(), gw.data_ptr(),
+                                 ws.data_ptr(), need, stream)
+    got = [torch.full_like(x, float("nan")) for x in (t["value"], t["loc"], t["w"])]
+    _lib.backward_noalloc(prob, t["value"].data_ptr(), t["loc"].data_ptr(), t["w"].data_ptr(), t["g"].data_ptr(),
+                          got[0].data_ptr(), got[1].data_ptr(), got[2].data_ptr(), stream)
+    torch.cuda.synchronize()
+    rgv, rgl, rgw = oracle_backward(wl)
+    rtol, arms, atol = TOL[("f32", "bwd")] if dt == "f32" else TOL[(dt, "bwd")]
+    assert_close("merge/accumulate/grad_value", f64(acc), 0.25 + 2 * rgv, rtol, arms, atol)
+    rtol, arms, atol = TOL[(dt, "bwd")]
+    for name, g, r in zip(("grad_value", "grad_sampling_locations", "grad_attention_weights"), got, (rgv, rgl, rgw)):
+        assert_close(f"merge/noalloc/{name}", f64(g), r, rtol, arms, atol)
