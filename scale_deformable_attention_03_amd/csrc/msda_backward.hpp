@@ -1108,7 +1108,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     int32_t* hist = reinterpret_cast<int32_t*>(skey + sorted_key_slots(UNIT));
     int32_t* cur = hist + kMaxSegKeys;
 
-    for (int i = threadIdx.x; i < nk * D; i += kAccBlock) tile[i] = 0.0f;
+    // (16-byte stores: nk * D is a multiple of 8)
+    for (int i = threadIdx.x; i < nk * D / 4; i += kAccBlock)
+        reinterpret_cast<float4*>(tile)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int i = threadIdx.x; i < kMaxSegKeys; i += kAccBlock) hist[i] = 0;
     __syncthreads();
     // counting sort by the key byte: records are read once, coalesced, and
