@@ -274,10 +274,12 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
     const int l = level_of_segment(pb, seg);
     const int k0 = (seg - pb.seg_base[l]) << pb.seg_shift[l];
     const int nk = min(1 << pb.seg_shift[l], pb.lv.H[l] * pb.lv.W[l] - k0);
-    for (int i = t; i < nk * pb.D; i += nt) {
-        const int k = i / pb.D, d = i - k * pb.D;
+    const int d4 = pb.D / 4;                          // 16-byte stores (D is a multiple of 8)
+    for (int i = t; i < nk * d4; i += nt) {
+        const int k = i / d4, c = i - k * d4;
         const int64_t key = pb.lv.start[l] + k0 + k;
-        gacc[((static_cast<int64_t>(b) * pb.K + key) * pb.M + m) * pb.D + d] = 0.0f;
+        *reinterpret_cast<float4*>(gacc + ((static_cast<int64_t>(b) * pb.K + key) * pb.M + m) * pb.D + 4 * c) =
+            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 }
 
