@@ -787,6 +787,9 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     raw[u][2] = buffer_load<VECB>(vr, o[u].z + lane_b);
                     raw[u][3] = buffer_load<VECB>(vr, o[u].w + lane_b);
                 }
+                // the batch's loads all go out before its first use (left
+                // to itself the scheduler issues them one at a time)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < kSB; ++u) {
                     const int lp = c0 + b0 + u;
@@ -829,18 +832,17 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                     const bool off = ((o[u].x & o[u].y & o[u].z & o[u].w) & kOffMap) != 0u;
                     if constexpr (kOwn > 1) {
                         // chunks start at multiples of LPR, a multiple of kOwn:
-                        // the slot (b0 + u) % kOwn is known at compile time
+                        // the slot (b0 + u) % kOwn is known at compile time.
+                        // The sums are kept as they are; the level scale, the
+                        // attention weight and the off-map test are applied
+                        // once per owned sample after the loop.
                         if (li == lp / kOwn) {
-                            const int l = lp / P;            // uniform across the wave
-                            const float vw = off ? 0.0f : sw;
-                            const float vx = off ? 0.0f : sx * (static_cast<float>(pb.lv.W[l]) * fr.z);
-                            const float vy = off ? 0.0f : sy * (static_cast<float>(pb.lv.H[l]) * fr.z);
 #pragma unroll
                             for (int k = 0; k < kOwn; ++k) {
                                 if ((b0 + u) % kOwn == k) {
-                                    keep_w[k] = vw;
-                                    keep_x[k] = vx;
-                                    keep_y[k] = vy;
+                                    keep_w[k] = sw;
+                                    keep_x[k] = sx;
+                                    keep_y[k] = sy;
                                 }
                             }
                         }
@@ -879,6 +881,20 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
             }
         }
         if constexpr (kOwn > 1) {
+            // the owned samples kOwn * li + k: gradients scaled by (W_l, H_l)
+            // times the attention weight, exactly zero for a sample off the
+            // map (cell kNoCell: all four corners off the map; the plain form
+            // has no key padding)
+#pragma unroll
+            for (int k = 0; k < kOwn; ++k) {
+                const int lp = kOwn * li + k;
+                const float4 fr = *reinterpret_cast<const float4*>(rec + lp * 8 + 4);    // lx ly w cell
+                const int4 lv = s_lv[lp / P];
+                const bool off = __float_as_uint(fr.w) == kNoCell;
+                keep_w[k] = off ? 0.0f : keep_w[k];
+                keep_x[k] = off ? 0.0f : keep_x[k] * (static_cast<float>(lv.y) * fr.z);
+                keep_y[k] = off ? 0.0f : keep_y[k] * (static_cast<float>(lv.x) * fr.z);
+            }
             constexpr int SE = Elem<ST>::bytes;
             const int64_t s0 = G * LP + kOwn * li;
             float xy[2 * kOwn];
