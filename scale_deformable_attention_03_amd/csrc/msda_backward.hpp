@@ -943,8 +943,13 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // segment and take consecutive slots there.  A sample's (at most
         // four) records are formed first, then their slots are taken
         // together and the records stored.
+        // i / gcount as a multiply-high by ceil(2^32 / gcount): exact for
+        // i * gcount < 2^32 (here i < gcount * L * P <= kMaxWgSamples); a
+        // one-query tile (whose multiplier would be 2^32) takes i itself
+        const uint32_t gmagic = t.gcount > 1 ? 0xffffffffu / static_cast<uint32_t>(t.gcount) + 1u : 0u;
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-            const int lp = i / t.gcount, g = i - lp * t.gcount, l = lp / P;
+            const int lp = t.gcount > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(i), gmagic)) : i;
+            const int g = i - lp * t.gcount, l = lp / P;
             const uint32_t* r = srec + g * gstride + lp * 8;
             const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
             const uint32_t cell = __float_as_uint(fr.w);
@@ -961,30 +966,27 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
                 if (rows == 0u) continue;
                 // record merging: this point's records carry the weights of
                 // the later points' rows that they share (in point order)
+                // (branch-free: a point that shares nothing adds zeros)
                 const int p = lp % 4;
                 const uint32_t* rl = r - p * 8;          // the level's point 0
+                float4 fq[4];
+#pragma unroll
+                for (int q = 1; q < 4; ++q) fq[q] = *reinterpret_cast<const float4*>(rl + q * 8 + 4);
 #pragma unroll
                 for (int q = 1; q < 4; ++q) {
-                    if (q <= p) continue;
-                    const float4 fq = *reinterpret_cast<const float4*>(rl + q * 8 + 4);
-                    const uint32_t sq = shared_rows(__float_as_uint(fq.w), cell);  // point q's rows this one has
-                    if (sq != 0u) {
-                        const float qlx = fabsf(fq.x), qly = fabsf(fq.y);
-                        const float qhx = 1.0f - qlx, qhy = 1.0f - qly;
-                        const float qwy0 = fq.z * qhy, qwy1 = fq.z * qly;
-                        if (sq == 3u) {                  // same cell
-                            w00 += qwy0 * qhx;
-                            w01 += qwy0 * qlx;
-                            w10 += qwy1 * qhx;
-                            w11 += qwy1 * qlx;
-                        } else if (sq == 1u) {           // q's row y0 is this one's row y0 + 1
-                            w10 += qwy0 * qhx;
-                            w11 += qwy0 * qlx;
-                        } else {                         // q's row y0 + 1 is this one's row y0
-                            w00 += qwy1 * qhx;
-                            w01 += qwy1 * qlx;
-                        }
-                    }
+                    // point q's rows this one has (later points only)
+                    const uint32_t sq = q > p ? shared_rows(__float_as_uint(fq[q].w), cell) : 0u;
+                    const float qlx = fabsf(fq[q].x), qly = fabsf(fq[q].y);
+                    const float qhx = 1.0f - qlx, qhy = 1.0f - qly;
+                    const float qwy0 = fq[q].z * qhy, qwy1 = fq[q].z * qly;
+                    // same cell: both rows; q's row y0 is this one's row
+                    // y0 + 1 (sq 1); q's row y0 + 1 is this one's row y0 (sq 2)
+                    const float a0 = sq == 3u ? qwy0 : (sq == 2u ? qwy1 : 0.0f);
+                    const float a1 = sq == 3u ? qwy1 : (sq == 1u ? qwy0 : 0.0f);
+                    w00 += a0 * qhx;
+                    w01 += a0 * qlx;
+                    w10 += a1 * qhx;
+                    w11 += a1 * qlx;
                 }
             }
             const int4 lv = s_lv[l];

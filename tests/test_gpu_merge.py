@@ -94,3 +94,14 @@ def test_merged_records_accumulate_and_noalloc(dt):
     rtol, arms, atol = TOL[(dt, "bwd")]
     for name, g, r in zip(("grad_value", "grad_sampling_locations", "grad_attention_weights"), got, (rgv, rgl, rgw)):
         assert_close(f"merge/noalloc/{name}", f64(g), r, rtol, arms, atol)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_one_query_last_tile(dt):
+    """2049 queries: the gradient kernel's last query tile (32 queries per
+    workgroup at float32, 64 at bf16) holds a single query, for which the
+    record epilogue's multiply-high division by the tile's query count is
+    replaced by the index itself."""
+    print(f"[gpu] one-query last tile, {dt}", flush=True)
+    wl = W.make("one_query_tile", 1, LEVELS, 2, 32, 4, 2049, dt, seed=1303, loc_args=(-0.1, 1.1))
+    check_backward(wl)
