@@ -275,8 +275,9 @@ __device__ void zero_segment(const Problem& pb, float* gacc, int gs, int t, int 
     const int k0 = (seg - pb.seg_base[l]) << pb.seg_shift[l];
     const int nk = min(1 << pb.seg_shift[l], pb.lv.H[l] * pb.lv.W[l] - k0);
     const int d4 = pb.D / 4;                          // 16-byte stores (D is a multiple of 8)
+    const UDiv by_d4 = udiv_by(d4);                   // (i < nk * d4 <= 2^14)
     for (int i = t; i < nk * d4; i += nt) {
-        const int k = i / d4, c = i - k * d4;
+        const int k = udiv(i, by_d4), c = i - k * d4;
         const int64_t key = pb.lv.start[l] + k0 + k;
         *reinterpret_cast<float4*>(gacc + ((static_cast<int64_t>(b) * pb.K + key) * pb.M + m) * pb.D + 4 * c) =
             make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -293,8 +294,9 @@ __device__ void narrow_segment(const Problem& pb, const float* gacc, void* out, 
     const int k0 = (seg - pb.seg_base[l]) << pb.seg_shift[l];
     const int nk = min(1 << pb.seg_shift[l], pb.lv.H[l] * pb.lv.W[l] - k0);
     const int d8 = pb.D / 8;
+    const UDiv by_d8 = udiv_by(d8);                   // (i < nk * d8 <= 2^13)
     for (int i = t; i < nk * d8; i += nt) {
-        const int k = i / d8, c = i - k * d8;
+        const int k = udiv(i, by_d8), c = i - k * d8;
         const int64_t e = ((static_cast<int64_t>(b) * pb.K + pb.lv.start[l] + k0 + k) * pb.M + m) * pb.D + 8 * c;
         const float4 a = *reinterpret_cast<const float4*>(gacc + e);
         const float4 z = *reinterpret_cast<const float4*>(gacc + e + 4);
@@ -943,12 +945,10 @@ msda_backward_kernel(const void* __restrict__ value, const void* __restrict__ lo
         // segment and take consecutive slots there.  A sample's (at most
         // four) records are formed first, then their slots are taken
         // together and the records stored.
-        // i / gcount as a multiply-high by ceil(2^32 / gcount): exact for
-        // i * gcount < 2^32 (here i < gcount * L * P <= kMaxWgSamples); a
-        // one-query tile (whose multiplier would be 2^32) takes i itself
-        const uint32_t gmagic = t.gcount > 1 ? 0xffffffffu / static_cast<uint32_t>(t.gcount) + 1u : 0u;
+        // (i < gcount * L * P <= kMaxWgSamples)
+        const UDiv by_gcount = udiv_by(t.gcount);
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
-            const int lp = t.gcount > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(i), gmagic)) : i;
+            const int lp = udiv(i, by_gcount);
             const int g = i - lp * t.gcount, l = lp / P;
             const uint32_t* r = srec + g * gstride + lp * 8;
             const float4 fr = *reinterpret_cast<const float4*>(r + 4);    // lx ly w cell
@@ -1291,21 +1291,24 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     // rows of padded keys (the module zero-fills them, so their gradient is
     // zero) are written as zeros
     const uint8_t* km = kmask ? kmask + static_cast<int64_t>(b) * pb.K + pb.lv.start[lvl] + k0 : nullptr;
+    // (divisions of i < nk * D <= 2^16 by D or less)
+    const UDiv by_d = udiv_by(D);
     if (km != nullptr) {                             // uniform: a kernel argument
         for (int i = threadIdx.x; i < nk * D; i += kAccBlock)
-            if (km[i / D] != 0) tile[i] = 0.0f;
+            if (km[udiv(i, by_d)] != 0) tile[i] = 0.0f;
         __syncthreads();
     }
     if (unit.w) {
         for (int i = threadIdx.x; i < nk * D; i += kAccBlock) {
-            const int k = i / D, d = i - k * D;
+            const int k = udiv(i, by_d), d = i - k * D;
             if (km == nullptr || km[k] == 0)
                 atomic_add_f32(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + d, tile[i]);
         }
     } else if constexpr (DT == kF32) {
         const int q4 = D / 4;
+        const UDiv by_q4 = udiv_by(q4);
         for (int i = threadIdx.x; i < nk * q4; i += kAccBlock) {
-            const int k = i / q4, c4 = i - k * q4;
+            const int k = udiv(i, by_q4), c4 = i - k * q4;
             const float4 v = *reinterpret_cast<const float4*>(tile + k * D + 4 * c4);
             float4* dst = reinterpret_cast<float4*>(gacc + (row0 + static_cast<int64_t>(k) * pb.M) * D + 4 * c4);
             __builtin_nontemporal_store(v.x, &dst->x); __builtin_nontemporal_store(v.y, &dst->y);
@@ -1313,8 +1316,9 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
         }
     } else {
         const int q8 = D / 8;
+        const UDiv by_q8 = udiv_by(q8);
         for (int i = threadIdx.x; i < nk * q8; i += kAccBlock) {
-            const int k = i / q8, c8 = i - k * q8;
+            const int k = udiv(i, by_q8), c8 = i - k * q8;
             const float* src = tile + k * D + 8 * c8;
             const Raw<16> r = narrow<DT, 16>(src);
             const int64_t e = (row0 + static_cast<int64_t>(k) * pb.M) * D + 8 * c8;

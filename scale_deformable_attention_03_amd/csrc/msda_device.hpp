@@ -342,6 +342,27 @@ __device__ __forceinline__ Cell make_cell(float x, float y, int32_t W, int32_t H
     return c;
 }
 
+// ---- division by a workgroup-uniform divisor --------------------------------------
+
+// i / d for 0 <= i and 1 <= d with i * d < 2^32, as a multiply-high by
+// ceil(2^32 / d) (d = 1 divides by taking i itself): two instructions in a
+// loop instead of an integer division sequence.
+struct UDiv {
+    uint32_t m;
+    int d;
+};
+
+__device__ __forceinline__ UDiv udiv_by(int d) {
+    UDiv u;
+    u.d = d;
+    u.m = d > 1 ? 0xffffffffu / static_cast<uint32_t>(d) + 1u : 0u;
+    return u;
+}
+
+__device__ __forceinline__ int udiv(int i, const UDiv& u) {
+    return u.d > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(i), u.m)) : i;
+}
+
 // ---- launch geometry -----------------------------------------------------------
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
