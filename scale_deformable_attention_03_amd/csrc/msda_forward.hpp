@@ -259,6 +259,11 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
             raw[u][2] = buffer_load<VECB>(vr, o.z + lane_b);
             raw[u][3] = buffer_load<VECB>(vr, o.w + lane_b);
         }
+        // a batch of several samples: its loads all go out before the first
+        // fold (measured: the large-batch bf16 forward 301 -> 293 us, the
+        // fp16 decoder's 12.2 -> 9.5 us; the one-sample batches of the generic
+        // kernel keep the compiler's own interleaving, which is faster there)
+        if constexpr (kSB > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
             if constexpr (DT == kBF16) {
