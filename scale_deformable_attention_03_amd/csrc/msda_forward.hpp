@@ -170,7 +170,7 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
         *reinterpret_cast<uint4*>(r) = make_uint4(c.o00, c.o01, c.o10, c.o11);
         *reinterpret_cast<float4*>(r + 4) = make_float4(wy0 * c.hx, wy0 * c.lx, wy1 * c.hx, wy1 * c.lx);
         if constexpr (CNT) {
-            if (c.ok)
+            if (c.ok && rows != 0u)
                 for_each_record(
                     c.x0, c.y0, lv.y, lv.x, lv.w & 0xff, lv.w >> 8,
                     [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); }, rows);
@@ -188,26 +188,33 @@ msda_forward_kernel(const void* __restrict__ value, const void* __restrict__ loc
             float xy[2 * S], wv[S];
             widen<ST, 16>(load_raw<16>(static_cast<const char*>(loc) + 2 * si * SE), xy);
             widen<ST, S * SE>(load_raw<S * SE>(static_cast<const char*>(attw) + si * SE), wv);
-            Corners c[S];
-            uint32_t rows[S];
+            // each sample's record goes to LDS as soon as its corners are
+            // known; only its packed cell stays for the counting below (so
+            // the counting forward's prologue holds S cells, not S corner sets)
+            uint32_t cell[S], rows[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
-                c[k] = corners_of(lp + k, make_float2(xy[2 * k], xy[2 * k + 1]));
+                const Corners c = corners_of(lp + k, make_float2(xy[2 * k], xy[2 * k + 1]));
+                stage(i + k, g, lp + k, c, wv[k], 0u);
+                cell[k] = c.ok ? pack_cell(c.x0, c.y0) : kNoCell;
                 rows[k] = 3u;
             }
-            if constexpr (CNT && kMergeRecords<REF, L_CT, P_CT>) {
-                if (pb.merge_records) {
+            if constexpr (CNT) {
+                if constexpr (kMergeRecords<REF, L_CT, P_CT>) {
                     // (the lane pair holding a level's four points is active
                     // together: t.gcount * LP and the loop stride are multiples
                     // of four)
-                    uint32_t cell[S];
+                    if (pb.merge_records) record_rows<S>(cell, lp % P, rows);
+                }
 #pragma unroll
-                    for (int k = 0; k < S; ++k) cell[k] = c[k].ok ? pack_cell(c[k].x0, c[k].y0) : kNoCell;
-                    record_rows<S>(cell, lp % P, rows);
+                for (int k = 0; k < S; ++k) {
+                    if (cell[k] == kNoCell) continue;
+                    const int4 lv = s_lv[(lp + k) / P];
+                    for_each_record(
+                        static_cast<int>(cell[k] & 0xffffu) - 1, static_cast<int>(cell[k] >> 16) - 1, lv.y, lv.x,
+                        lv.w & 0xff, lv.w >> 8, [&](int seg, int, int, int) { atomicAdd(&lhist[seg], 1); }, rows[k]);
                 }
             }
-#pragma unroll
-            for (int k = 0; k < S; ++k) stage(i + k, g, lp + k, c[k], wv[k], rows[k]);
         }
     } else {
         for (int i = threadIdx.x; i < t.gcount * LP; i += blockDim.x) {
