@@ -1097,16 +1097,19 @@ msda_accumulate_kernel(const void* __restrict__ gout, const uint3* __restrict__ 
     // (clamped to the grid and to [0, np): the words come from the gradient
     // kernel's workgroup 0, and the host launches this kernel only after a
     // gradient kernel with at least one workgroup)
-    const int np = pb.nplanes, total = min(nunits[3 * np], static_cast<int>(gridDim.x));
+    const int np = pb.nplanes, lane = threadIdx.x & 63;
+    // (the first 64 planes' unit prefixes load together with the total, not
+    // after it: one memory round trip fewer before the unit is known)
+    const int v0 = lane < np ? nunits[2 * np + lane] : 0x7fffffff;
+    const int total = min(nunits[3 * np], static_cast<int>(gridDim.x));
     if (static_cast<int>(blockIdx.x) >= total) return;
     // workgroups 0 .. total-1 cover the units; each XCD gets a contiguous run
     const int r = static_cast<int>(xcd_tile(blockIdx.x, total));
     // the unit's plane: the number of planes whose first unit is <= r, less
     // one, counted 64 planes per load with a ballot
-    const int lane = threadIdx.x & 63;
     int lo = -1;
     for (int c0 = 0; c0 < np; c0 += 64) {
-        const int v = c0 + lane < np ? nunits[2 * np + c0 + lane] : 0x7fffffff;
+        const int v = c0 == 0 ? v0 : (c0 + lane < np ? nunits[2 * np + c0 + lane] : 0x7fffffff);
         const int k = __popcll(__ballot(v <= r));
         lo += k;
         if (k < 64) break;
